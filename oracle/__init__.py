@@ -1,0 +1,149 @@
+"""fp64 CPU oracle for paged GQA target-verify attention (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this package.  It
+shares no code with the HIP library in ``paged_gqa_attention_va_amd`` and
+imports nothing from it.  The C source ``va_oracle.c`` states the definition it
+follows and cites the passages it comes from.
+
+``attn()`` takes the raw bit patterns of the inputs (uint16 bf16 bits, uint8
+fp8 bytes) and returns the attention output and its log-sum-exp in float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "va_oracle.c")
+_LIB = os.path.join(_HERE, "libva_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C, no GPU toolchain)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-D_DEFAULT_SOURCE", "-shared",
+                               "-fPIC", _SRC, "-o", tmp, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load_library(path: str):
+    """Open an oracle shared library at ``path`` and declare its signatures."""
+    lib = ctypes.CDLL(path)
+    _declare(lib)
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = load_library(_LIB)
+    return _lib
+
+
+def _declare(lib) -> None:
+    P = ctypes.c_void_p
+    lib.va_oracle_fp8e4m3fn_to_double.restype = ctypes.c_double
+    lib.va_oracle_fp8e4m3fn_to_double.argtypes = [ctypes.c_uint8]
+    lib.va_oracle_bf16_to_double.restype = ctypes.c_double
+    lib.va_oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.va_oracle_attn.restype = ctypes.c_int
+    lib.va_oracle_attn.argtypes = [
+        P, P, P, ctypes.c_int, P, ctypes.c_int64, P, P,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_double, ctypes.c_double, ctypes.c_double,
+        P, P, P, ctypes.c_int64, P, P, ctypes.c_int]
+
+
+def fp8_e4m3fn_to_float(code: int) -> float:
+    return _load().va_oracle_fp8e4m3fn_to_double(int(code))
+
+
+def bf16_to_float(bits: int) -> float:
+    return _load().va_oracle_bf16_to_double(int(bits))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, kv_dtype: str,
+         block_table: np.ndarray, cu_seqlens_q: np.ndarray, seqused_k: np.ndarray,
+         num_kv_heads: int, scale: float, k_descale: float = 1.0,
+         v_descale: float = 1.0, rows: Optional[Sequence[int]] = None,
+         segments: Optional[Sequence[Sequence[int]]] = None,
+         threads: Optional[int] = None, lib=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention output [n_rows, D] and natural-log LSE [n_rows], float64.
+
+    q: uint16 [total_q, Hq, D]; k, v: uint8 (fp8 e4m3fn) or uint16 (bf16)
+    [num_blocks, page, Hkv, D].  rows: flat (q_row * Hq + head) indices, default
+    all rows in order.  segments: per sequence, the ascending start keys of a
+    contiguous split of [0, seqused_k) (first start 0); the oracle then merges
+    per-segment partials by log-sum-exp instead of one pass.  lib: an
+    alternative build of the oracle (tests that plant mistakes use this).
+    """
+    if lib is None:
+        lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    if kv_dtype == "fp8":
+        k = np.ascontiguousarray(k, dtype=np.uint8)
+        v = np.ascontiguousarray(v, dtype=np.uint8)
+    elif kv_dtype == "bf16":
+        k = np.ascontiguousarray(k, dtype=np.uint16)
+        v = np.ascontiguousarray(v, dtype=np.uint16)
+    else:
+        raise ValueError(kv_dtype)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    sk = np.ascontiguousarray(seqused_k, dtype=np.int32)
+    total_q, hq, d = q.shape
+    page = k.shape[1]
+    assert k.shape[2] == num_kv_heads and k.shape[3] == d
+    if rows is None:
+        rows_arr = None
+        n = total_q * hq
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        n = int(rows_arr.shape[0])
+    seg_start = seg_ptr = None
+    if segments is not None:
+        assert len(segments) == sk.shape[0]
+        starts, ptr = [], [0]
+        for s in segments:
+            starts.extend(int(x) for x in s)
+            ptr.append(len(starts))
+        seg_start = np.asarray(starts if starts else [0], dtype=np.int32)
+        seg_ptr = np.asarray(ptr, dtype=np.int32)
+    out = np.zeros((n, d), dtype=np.float64)
+    lse = np.zeros((n,), dtype=np.float64)
+    st = lib.va_oracle_attn(
+        _ptr(q), _ptr(k), _ptr(v), 1 if kv_dtype == "fp8" else 0,
+        _ptr(bt), bt.shape[1], _ptr(cu), _ptr(sk), sk.shape[0], hq, num_kv_heads,
+        d, page, float(scale), float(k_descale), float(v_descale),
+        _ptr(seg_start), _ptr(seg_ptr), _ptr(rows_arr), n, _ptr(out), _ptr(lse),
+        default_threads() if threads is None else int(threads))
+    if st != 0:
+        raise RuntimeError(f"va_oracle_attn failed with status {st}")
+    return out, lse
+
+
+def attn_problem(p, rows=None, segments=None, threads=None, lib=None):
+    """``attn`` on a ``va_inputs.Problem``-like object (duck typed)."""
+    return attn(p.q, p.k, p.v, p.kv_dtype, p.block_table, p.cu_seqlens_q,
+                p.seqused_k, p.num_kv_heads, p.scale, p.k_descale, p.v_descale,
+                rows=rows, segments=segments, threads=threads, lib=lib)
