@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the verify-attention hot path on one MI355X.
+
+One step is one va_run: the split-KV main kernel and then the segment-reduce
+kernel, over one batch of synthetic input.  The default workload is the
+long-context batch: 16 sequences x 4 verify tokens, 32768 KV tokens each,
+16 query heads per kv head, head_dim 256, FP8 e4m3 KV in 16-token pages with a
+random block table.  It is the one the metric is quoted on: 16:1 GQA, FP8 KV,
+32K+ context.
+
+  value        effective HBM GB/s over the whole step, computed from the
+               algorithmic bytes.  Those are the unique KV pages within
+               seqused_k (K and V) plus the Q and O bytes.
+  roofline     the main kernel alone: the same algorithmic bytes over its
+               average launch time.  The time is measured with HIP events on
+               the stream it runs on, against the 8 TB/s peak.
+  cpu_baseline the fp64 oracle, timed on this host's cores on a bounded
+               sample of the same workload.
+
+Inputs are resident in HBM before timing starts.  The KV pools rotate over
+several copies, so the 256 MiB memory-side cache cannot serve a step from
+the previous one.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+
+
+def algorithmic_bytes(p, seqs=None) -> int:
+    """Unique KV pages referenced within seqused_k (K and V, each page once per
+    kv head) plus Q and O bytes, optionally restricted to some sequences."""
+    elt = 1 if p.kv_dtype == "fp8" else 2
+    idx = np.arange(p.num_seqs) if seqs is None else np.asarray(seqs)
+    pages = 0
+    rows = 0
+    for b in idx:
+        lq = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
+        if lq > 0:
+            pages += -(-int(p.seqused_k[b]) // p.page_size)
+            rows += lq
+    kv = pages * p.num_kv_heads * p.page_size * p.head_dim * elt * 2
+    qo = rows * p.num_q_heads * p.head_dim * 2 * 2
+    return int(kv + qo)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "paged_gqa_attention_va_amd", "csrc", "va.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get(workload)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(p, budget_s: float = 12.0):
+    """Time the oracle on whole sequences of p until about budget_s of work."""
+    import oracle
+    threads = oracle.default_threads()
+    G = p.num_q_heads
+    done_seqs, secs = [], 0.0
+    for b in range(p.num_seqs):
+        q0, q1 = int(p.cu_seqlens_q[b]), int(p.cu_seqlens_q[b + 1])
+        rows = np.arange(q0 * G, q1 * G, dtype=np.int64)
+        if len(rows) == 0:
+            continue
+        t0 = time.perf_counter()
+        oracle.attn_problem(p, rows=rows, threads=threads)
+        secs += time.perf_counter() - t0
+        done_seqs.append(b)
+        if secs >= budget_s:
+            break
+    nbytes = algorithmic_bytes(p, done_seqs)
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(done_seqs)} of {p.num_seqs} sequences (all their rows), "
+                      f"{nbytes} algorithmic bytes in {secs:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload id (2 = the headline)")
+    ap.add_argument("--variant", type=int, default=0, help="sweep variant of workload 4")
+    ap.add_argument("--copies", type=int, default=4, help="KV pool copies to rotate over")
+    ap.add_argument("--grid", type=int, default=0, help="force the split-KV grid (0 = plan)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage", choices=["all", "split", "merge"], default="all",
+                    help="profiling aid: time only one kernel per step")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the kernel is single-device; see DESIGN.md for how the path would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_gqa_attention_va_amd as va
+    import va_inputs
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    t0 = time.perf_counter()
+    p = va_inputs.config(args.config, args.variant)
+    log(f"bench: generated {p.name} in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(p.q.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def kv(a):
+        t = torch.from_numpy(a)
+        if p.kv_dtype == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(dev)
+
+    k0, v0 = kv(p.k), kv(p.v)
+    ks = [k0] + [k0.clone() for _ in range(args.copies - 1)]
+    vs = [v0] + [v0.clone() for _ in range(args.copies - 1)]
+    bt = torch.from_numpy(p.block_table).to(dev)
+    cu = torch.from_numpy(p.cu_seqlens_q).to(dev)
+    sk = torch.from_numpy(p.seqused_k).to(dev)
+    kd = torch.tensor([p.k_descale], dtype=torch.float32, device=dev)
+    vd = torch.tensor([p.v_descale], dtype=torch.float32, device=dev)
+    plan = va.Plan.for_problem(p, force_grid=args.grid)
+    ws = plan.workspace(dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    log(f"bench: plan grid={plan.grid} workspace={plan.workspace_bytes} B, "
+        f"{args.copies} pool copies of {2 * p.k.nbytes / 2**20:.0f} MiB")
+
+    stages = {"all": (va.VA_STAGE_SPLIT_KV, va.VA_STAGE_MERGE), "split": (va.VA_STAGE_SPLIT_KV,),
+              "merge": (va.VA_STAGE_MERGE,)}[args.stage]
+
+    def step(i, ev=None):
+        c = i % args.copies
+        for s in stages:
+            if ev is not None and s == va.VA_STAGE_SPLIT_KV:
+                ev[0].record(stream)
+            plan.run(q, ks[c], vs[c], bt, cu, sk, p.scale, kd, vd, out=out, workspace=ws,
+                     stream=stream, stage=s)
+            if ev is not None and s == va.VA_STAGE_SPLIT_KV:
+                ev[1].record(stream)
+
+    if args.stage == "merge":      # the merge reads what a split pass left in the workspace
+        plan.run(q, ks[0], vs[0], bt, cu, sk, p.scale, kd, vd, out=out, workspace=ws,
+                 stream=stream, stage=va.VA_STAGE_SPLIT_KV)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"bench: {args.warmup} warmup steps done")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    alg = algorithmic_bytes(p)
+    value = alg / (ms_step * 1e-3) / 1e9
+    log(f"bench: {args.steps} steps, {ms_step * 1e3:.2f} us/step, {value:.1f} GB/s effective")
+
+    roofline = None
+    if va.VA_STAGE_SPLIT_KV in stages:
+        main_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        achieved = alg / (main_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                    "traffic": load_traffic(p.name),
+                    "kernel": "va_split_kv_kernel", "us_per_launch": round(main_ms * 1e3, 3)}
+        log(f"bench: main kernel {main_ms * 1e3:.2f} us/launch, {achieved:.1f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(p)
+        log(f"bench: cpu baseline {cpu}")
+
+    rec = {
+        "metric": "verify-attn effective HBM GB/s (% of peak) and us/call at 16:1 GQA, FP8 KV",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "us_per_call": round(ms_step * 1e3, 3),
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": va_inputs.CONFIG_NAMES[args.config] if args.config != 4
+                   else p.name,
+                   "num_seqs": p.num_seqs, "q_len": int(p.max_seqlen_q),
+                   "kv_len_max": int(p.max_seqlen_k), "q_heads": p.num_q_heads,
+                   "kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "page": p.page_size,
+                   "kv_dtype": p.kv_dtype, "algorithmic_bytes": alg, "grid": plan.grid,
+                   "pool_copies": args.copies, "stage": args.stage},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

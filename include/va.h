@@ -1,0 +1,177 @@
+/*
+ * va.h -- C ABI of the MI355X (gfx950) paged GQA target-verify attention library.
+ *
+ * The operation.  This is attention for speculative-decoding target
+ * verification.  Each sequence has a short query block of 1..4 draft tokens
+ * (bf16).  A group of G = Hq/Hkv query heads shares one kv head.  The query
+ * attends causally over a paged KV cache of 16-token pages (FP8 e4m3fn or
+ * bf16), with per-tensor k/v descale.  This is the call the sglang PR #36330
+ * summary page shows ("Key source snippets": the aiter_backend.py shape gate
+ * and the unified_attention_3d_mtp_func call, plus the test
+ * _check_matches_aiter).
+ *
+ *   for sequence b with queries q[cu[b] .. cu[b+1]) and Lk = seqused_k[b] keys:
+ *     query token t (0-based) sees keys j = 0 .. Lk - Lq + t   (bottom-right causal)
+ *     s_j   = softmax_scale * k_descale * < q[t][h], K[j][h/G] >
+ *     out[t][h] = v_descale * sum_j softmax(s)_j * V[j][h/G]
+ *
+ * The key range is split into segments whose partial softmax results are
+ * merged by log-sum-exp.  That split is the PR #36330 page's, "Implementation
+ * breakdown" item 1: a segmented main kernel plus a reduce-segments kernel.
+ * Packing the G heads of a group over one load of each KV tile comes from the
+ * same item and from the sglang PR #34517 summary page ("Motivation").
+ *
+ * Execution model.  va_plan() runs on the host once per problem shape.  It
+ * checks the domain (the analogue of the page's shape gate and of can_handle on
+ * the PR #34517 page), chooses kernels and launch shape, and sizes the
+ * workspace.  va_run() only enqueues work on a HIP stream.  It reads every
+ * length from device memory, and never synchronises or allocates, so it may be
+ * captured in a HIP graph (the PR #30105 summary page, "Key source snippets",
+ * notes that the seq_lens + draft addition must stay inside the captured graph).
+ *
+ * Ownership.  The caller owns every device buffer: q, pools, metadata, out,
+ * workspace.  The library owns only the host-side plan object.  A plan is
+ * immutable after creation.  va_run may run concurrently on different streams
+ * if each call has its own workspace.
+ *
+ * Errors.  Functions return va_status.  Host-checkable mistakes (null
+ * pointers, unsupported shapes, a short workspace) return an error and enqueue
+ * nothing.  Device data is not validated in va_run.  Invalid device data yields
+ * an undefined result, but the kernels do not read outside their buffers:
+ *   - lengths are clamped to the block-table row;
+ *   - page ids are clamped to [0, num_blocks).
+ * Invalid device data includes q_len > seqused_k, a page id out of range, and
+ * cu_seqlens_q not ascending.
+ */
+#ifndef VA_H
+#define VA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VA_OK = 0,
+    VA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent sizes */
+    VA_ERR_UNSUPPORTED = 2,   /* outside the supported domain (see va_plan) */
+    VA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than va_plan_workspace_bytes */
+    VA_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} va_status;
+
+typedef enum {
+    VA_DT_BF16 = 1,           /* bfloat16 */
+    VA_DT_FP8_E4M3FN = 2      /* OCP fp8 e4m3fn: bias 7, max 448, NaN = 0x7F/0xFF, no inf */
+} va_dtype;
+
+/* Shape of one verify-attention call.  All fields are host values. */
+typedef struct {
+    int32_t num_seqs;            /* B >= 1 */
+    int32_t num_q_heads;         /* Hq */
+    int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0 */
+    int32_t head_dim;            /* D; must be 256 */
+    int32_t page_size;           /* must be 16 */
+    int32_t max_seqlen_q;        /* upper bound of any q_len; 1..4 */
+    int32_t max_seqlen_k;        /* upper bound of any seqused_k (may be loose) */
+    int32_t max_blocks_per_seq;  /* row stride of block_table (int32 elements) */
+    int64_t num_blocks;          /* pages in each of the k and v pools */
+    int64_t total_q;             /* rows of q / out; <= num_seqs * max_seqlen_q */
+    int32_t q_dtype;             /* va_dtype; must be VA_DT_BF16 (out is bf16 too) */
+    int32_t kv_dtype;            /* va_dtype of both pools */
+    int32_t num_cus;             /* compute units to plan for; 0 = query the current device */
+    int32_t force_grid;          /* 0 = automatic; > 0 = number of split-KV workgroups
+                                    (a testing hook: every value gives the same result
+                                    up to floating-point merge order) */
+} va_problem;
+
+typedef struct va_plan_s *va_plan_t;
+
+/*
+ * Check the problem and build a plan.
+ * Supported domain (VA_ERR_UNSUPPORTED otherwise):
+ *   - D = 256 and page 16;
+ *   - Q and out bf16; KV fp8 e4m3fn or bf16;
+ *   - G = Hq/Hkv in {4, 8, 16}; 1 <= max_seqlen_q <= 4;
+ *   - num_seqs * num_kv_heads <= 65536;
+ *   - causal only; no sliding window, softcap or sinks.
+ *   - With num_cus == 0, the current HIP device must be gfx950.
+ * The domain is the PR #36330 page's gate (gfx950, q len 2..4, G = 16, D = 256,
+ * page 16, bf16 Q, fp8 KV), widened:
+ *   - q_len 1 and G = 4/8 are the local shapes of the PR #34517 page's tests;
+ *   - bf16 KV is that page's other cache type;
+ *   - any KV length is allowed (short ones just get one segment).
+ * On success *out holds a new plan; release it with va_plan_destroy.
+ */
+va_status va_plan(const va_problem *problem, va_plan_t *out);
+
+/* Bytes of device workspace va_run needs for this plan. */
+va_status va_plan_workspace_bytes(va_plan_t plan, size_t *bytes);
+
+/* Number of split-KV workgroups the plan launches (after force_grid). */
+va_status va_plan_grid(va_plan_t plan, int32_t *grid);
+
+/*
+ * Enqueue the verify attention on `stream` (a hipStream_t; NULL = the null stream).
+ *
+ *   q            [total_q, Hq, 256] bf16, contiguous
+ *   k_pool       [num_blocks, 16, Hkv, 256] kv_dtype, contiguous
+ *   v_pool       [num_blocks, 16, Hkv, 256] kv_dtype, contiguous
+ *   block_table  [num_seqs, max_blocks_per_seq] int32; entry p = pool page of
+ *                the sequence's logical page p (only the first ceil(seqused_k/16)
+ *                entries of a row are read)
+ *   cu_seqlens_q [num_seqs + 1] int32 prefix sums of the query lengths
+ *   seqused_k    [num_seqs] int32 KV length of each sequence, verify tokens included
+ *   softmax_scale  host float (head_dim**-0.5 for the standard scale)
+ *   k_descale, v_descale  device pointers to one float each, or NULL for 1.0
+ *   out          [total_q, Hq, 256] bf16, written for every query row
+ *   workspace    device buffer of >= va_plan_workspace_bytes bytes, 256-byte
+ *                aligned; its contents need not be initialised
+ * All device pointers must be 16-byte aligned.  Returns VA_OK once both kernels
+ * are enqueued.
+ */
+va_status va_run(va_plan_t plan, const void *q, const void *k_pool, const void *v_pool,
+                 const int32_t *block_table, const int32_t *cu_seqlens_q,
+                 const int32_t *seqused_k, float softmax_scale,
+                 const float *k_descale, const float *v_descale, void *out,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The two kernels of va_run, enqueued one at a time (same arguments).
+ *   stage VA_STAGE_SPLIT_KV: the split-KV main kernel.  It writes the per-segment
+ *                            partials to the workspace, and writes rows whose
+ *                            sequence fits one segment straight to out.
+ *   stage VA_STAGE_MERGE:    the segment-reduce kernel; it reads the partials and
+ *                            writes the remaining rows of out.
+ * VA_STAGE_MERGE must follow VA_STAGE_SPLIT_KV of the same call on the same
+ * stream (with the same workspace).  va_run == SPLIT_KV then MERGE.  These exist
+ * so a caller can time or profile each kernel on its own stream.
+ */
+enum { VA_STAGE_ALL = 0, VA_STAGE_SPLIT_KV = 1, VA_STAGE_MERGE = 2 };
+va_status va_run_stage(va_plan_t plan, int32_t stage, const void *q, const void *k_pool,
+                       const void *v_pool, const int32_t *block_table,
+                       const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                       float softmax_scale, const float *k_descale,
+                       const float *v_descale, void *out, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Release a plan (NULL is ignored). */
+void va_plan_destroy(va_plan_t plan);
+
+/* Static description of a status code. */
+const char *va_status_str(va_status status);
+
+/*
+ * Decode n fp8 e4m3fn bytes to bf16 bits on the device, with the same in-register
+ * conversion the attention kernel uses on K and V.  It is a diagnostic that
+ * checks the dequant step over all 256 codes.  Both pointers are device
+ * pointers; the call enqueues one kernel on `stream`.
+ */
+va_status va_fp8_to_bf16(const uint8_t *in, uint16_t *out, int64_t n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VA_H */

@@ -1,0 +1,217 @@
+"""MI355X-native paged GQA target-verify attention.
+
+A thin Python binding over the C ABI of ``libva.so`` (include/va.h).  It only
+marshals arguments: every step of the computation runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.
+
+    plan = Plan(num_seqs=16, num_q_heads=16, num_kv_heads=1, max_seqlen_q=4,
+                max_seqlen_k=32768, max_blocks_per_seq=2048, num_blocks=32768,
+                total_q=64, kv_dtype="fp8")
+    out = plan.run(q, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k,
+                   softmax_scale=256 ** -0.5, k_descale=kd, v_descale=vd)
+
+The library is loaded from this package directory.  If it is not built, the
+first use raises ``RuntimeError``; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libva.so")
+
+VA_OK, VA_ERR_INVALID_ARG, VA_ERR_UNSUPPORTED, VA_ERR_WORKSPACE, VA_ERR_HIP = range(5)
+VA_DT_BF16, VA_DT_FP8_E4M3FN = 1, 2
+VA_STAGE_ALL, VA_STAGE_SPLIT_KV, VA_STAGE_MERGE = 0, 1, 2
+
+EXPORTED = ("va_plan", "va_plan_workspace_bytes", "va_plan_grid", "va_run", "va_run_stage",
+            "va_plan_destroy", "va_status_str", "va_fp8_to_bf16")
+
+_lib = None
+
+
+class VaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("max_seqlen_q", ctypes.c_int32),
+        ("max_seqlen_k", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64), ("total_q", ctypes.c_int64),
+        ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32), ("force_grid", ctypes.c_int32),
+    ]
+
+
+def library(path: str = LIB_PATH):
+    """Load libva.so (once) and declare the C ABI."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m paged_gqa_attention_va_amd._build` "
+                           "or __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.va_plan.restype = ctypes.c_int
+    lib.va_plan.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(P)]
+    lib.va_plan_workspace_bytes.restype = ctypes.c_int
+    lib.va_plan_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.va_plan_grid.restype = ctypes.c_int
+    lib.va_plan_grid.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
+    run_args = [P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, ctypes.c_size_t, P]
+    lib.va_run.restype = ctypes.c_int
+    lib.va_run.argtypes = run_args
+    lib.va_run_stage.restype = ctypes.c_int
+    lib.va_run_stage.argtypes = [P, ctypes.c_int32] + run_args[1:]
+    lib.va_plan_destroy.restype = None
+    lib.va_plan_destroy.argtypes = [P]
+    lib.va_status_str.restype = ctypes.c_char_p
+    lib.va_status_str.argtypes = [ctypes.c_int]
+    lib.va_fp8_to_bf16.restype = ctypes.c_int
+    lib.va_fp8_to_bf16.argtypes = [P, P, ctypes.c_int64, P]
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    try:
+        return library().va_status_str(int(status)).decode()
+    except RuntimeError:
+        return "unknown"
+
+
+def _check(status: int, where: str) -> None:
+    if status != VA_OK:
+        raise VaError(status, where)
+
+
+def _dtype_code(name: str) -> int:
+    if name in ("fp8", "fp8_e4m3fn", "float8_e4m3fn"):
+        return VA_DT_FP8_E4M3FN
+    if name in ("bf16", "bfloat16"):
+        return VA_DT_BF16
+    raise ValueError(f"unsupported dtype {name!r}")
+
+
+class Plan:
+    """A host-side plan for one problem shape (wraps va_plan / va_plan_destroy)."""
+
+    def __init__(self, num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                 max_seqlen_q: int, max_seqlen_k: int, max_blocks_per_seq: int,
+                 num_blocks: int, total_q: int, kv_dtype: str = "fp8",
+                 num_cus: int = 0, force_grid: int = 0, head_dim: int = 256,
+                 page_size: int = 16, q_dtype: str = "bf16"):
+        self._lib = library()
+        pr = _Problem(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                      max_seqlen_q, max_seqlen_k, max_blocks_per_seq, num_blocks, total_q,
+                      _dtype_code(q_dtype), _dtype_code(kv_dtype), num_cus, force_grid)
+        self.problem = pr
+        self.kv_dtype = kv_dtype
+        h = ctypes.c_void_p()
+        _check(self._lib.va_plan(ctypes.byref(pr), ctypes.byref(h)), "va_plan")
+        self._h = h
+        n = ctypes.c_size_t()
+        _check(self._lib.va_plan_workspace_bytes(h, ctypes.byref(n)), "va_plan_workspace_bytes")
+        self.workspace_bytes = int(n.value)
+        g = ctypes.c_int32()
+        _check(self._lib.va_plan_grid(h, ctypes.byref(g)), "va_plan_grid")
+        self.grid = int(g.value)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.va_plan_destroy(h)
+            self._h = None
+
+    @classmethod
+    def for_problem(cls, p, **kw) -> "Plan":
+        """Plan for a ``va_inputs.Problem``-like object (duck typed)."""
+        return cls(num_seqs=p.num_seqs, num_q_heads=p.num_q_heads, num_kv_heads=p.num_kv_heads,
+                   max_seqlen_q=max(1, p.max_seqlen_q), max_seqlen_k=p.max_seqlen_k,
+                   max_blocks_per_seq=int(p.block_table.shape[1]), num_blocks=p.num_blocks,
+                   total_q=p.total_q, kv_dtype=p.kv_dtype, **kw)
+
+    def workspace(self, device=None):
+        import torch
+        return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=device or "cuda")
+
+    def run(self, q, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k, softmax_scale: float,
+            k_descale=None, v_descale=None, out=None, workspace=None, stream=None,
+            stage: int = VA_STAGE_ALL):
+        """Enqueue the attention on ``stream`` (default: torch's current stream)."""
+        import torch
+        self._check_tensors(q, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k,
+                            k_descale, v_descale)
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.workspace(q.device)
+        if out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous():
+            raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+        if workspace.numel() * workspace.element_size() < self.workspace_bytes:
+            raise ValueError("workspace smaller than plan.workspace_bytes")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        st = self._lib.va_run_stage(
+            self._h, int(stage), ptr(q), ptr(k_pool), ptr(v_pool), ptr(block_table),
+            ptr(cu_seqlens_q), ptr(seqused_k), ctypes.c_float(softmax_scale),
+            ptr(k_descale), ptr(v_descale), ptr(out), ptr(workspace),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+            ctypes.c_void_p(sptr))
+        _check(st, "va_run")
+        return out
+
+    def _check_tensors(self, q, k_pool, v_pool, block_table, cu, seqused, kd, vd):
+        import torch
+        pr = self.problem
+        if q.dtype != torch.bfloat16 or q.dim() != 3 or tuple(q.shape) != (pr.total_q, pr.num_q_heads, pr.head_dim):
+            raise ValueError(f"q must be bf16 [{pr.total_q}, {pr.num_q_heads}, {pr.head_dim}], got {q.dtype} {tuple(q.shape)}")
+        kv_ok = (torch.uint8, torch.float8_e4m3fn) if self.kv_dtype == "fp8" else (torch.bfloat16,)
+        shape = (pr.num_blocks, pr.page_size, pr.num_kv_heads, pr.head_dim)
+        for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+            if t.dtype not in kv_ok or tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be {self.kv_dtype} {shape}, got {t.dtype} {tuple(t.shape)}")
+        if tuple(block_table.shape) != (pr.num_seqs, pr.max_blocks_per_seq) or block_table.dtype != torch.int32:
+            raise ValueError("block_table must be int32 [num_seqs, max_blocks_per_seq]")
+        if tuple(cu.shape) != (pr.num_seqs + 1,) or cu.dtype != torch.int32:
+            raise ValueError("cu_seqlens_q must be int32 [num_seqs + 1]")
+        if tuple(seqused.shape) != (pr.num_seqs,) or seqused.dtype != torch.int32:
+            raise ValueError("seqused_k must be int32 [num_seqs]")
+        for name, t in (("k_descale", kd), ("v_descale", vd)):
+            if t is not None and (t.dtype != torch.float32 or t.numel() < 1):
+                raise ValueError(f"{name} must be a float32 device tensor with one element")
+        for t in (q, k_pool, v_pool, block_table, cu, seqused, kd, vd):
+            if t is not None and (not t.is_cuda or not t.is_contiguous()):
+                raise ValueError("all tensors must be contiguous device tensors")
+
+
+def fp8_to_bf16(codes, stream=None):
+    """Device fp8 e4m3fn -> bf16 with the kernels' own in-register conversion."""
+    import torch
+    lib = library()
+    codes = codes.contiguous().view(torch.uint8)
+    out = torch.empty(codes.shape, dtype=torch.bfloat16, device=codes.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(codes.device)
+    _check(lib.va_fp8_to_bf16(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                              codes.numel(), ctypes.c_void_p(stream.cuda_stream)), "va_fp8_to_bf16")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libva.so in-tree (hipcc, gfx950)."""
+    from . import _build as _b
+    global _lib
+    _lib = None
+    return _b.build(verbose=verbose)

@@ -1,0 +1,1064 @@
+// va.hip -- paged GQA target-verify attention for MI355X (gfx950 / CDNA4).
+//
+// Two kernels and the host side of the C ABI declared in include/va.h.
+//
+//  va_split_kv_kernel   Split-KV main kernel.  Each workgroup takes a contiguous
+//                       share of the flattened page space of all (sequence, kv
+//                       head) pairs.  For each piece it loads every K/V page
+//                       once and reuses it for all G*q_len packed query rows
+//                       (GQA packing).  It dequantises FP8 in registers, runs
+//                       MFMA QK^T and PV with an online softmax, and writes
+//                       either the final rows or a partial (o, lse) per piece.
+//  va_merge_kernel      Segment reduce: log-sum-exp merge of the partials of
+//                       every (sequence, kv head) that was split over
+//                       workgroups.
+//
+// The method comes from the sglang PR #36330 summary page ("Implementation
+// breakdown", item 1: pack the G query heads and speculative tokens of a group
+// so each loaded KV tile serves all of them, split the KV range into segments
+// for CU parallelism, merge in a reduce-segments kernel).  The sglang PR #34517
+// summary page says the same in "Motivation": one KV-tile load per group of
+// query heads.  The kernels here are a CDNA4 design of their own, not the
+// Triton ones.
+//
+// Layout of the packed rows of one (sequence b, kv head g): row r = t*G + h
+// (t = speculative token, h = head within the group), padded to 16-row MFMA
+// tiles.  Each wave computes S^T = K Q^T and O^T = V^T P^T with
+// v_mfma_f32_16x16x32_bf16.  Then:
+//   - the S^T accumulator already is the P^T B-operand, so no shuffle is needed;
+//   - row statistics (max, sum) stay inside one lane column;
+//   - the K and V operands are loaded straight from HBM into registers in
+//     operand order, with 64- and 256-byte contiguous runs per key row.
+//
+// Stream-K partition: WG w of N handles flat pages [floor(w*P/N),
+// floor((w+1)*P/N)) where P is the total page count, computed on the device from
+// seqused_k / cu_seqlens_q.  Any length mix therefore balances over the CUs
+// with no host-side lengths (graph-safe).  A piece (w, bg) writes its partial to
+// workspace slot w + bg, which is unique (a later WG cannot meet an earlier
+// sequence).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "va.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 256;
+constexpr int kPage = 16;
+constexpr int kThreads = 256;            // 4 waves of 64
+constexpr int kWaves = 4;
+// Online-softmax rescale threshold (log2 units).  The running max m is only
+// moved when a new logit exceeds it by more than kTau.  Then p = 2^(x - m) <= 2^8
+// and O, l stay exact up to rounding; the final O/l does not depend on m.
+constexpr float kTau = 8.0f;
+constexpr int kKvFp8 = 0;
+constexpr int kKvBf16 = 1;
+
+struct SplitParams {
+    const uint16_t *q;
+    const uint8_t *k;
+    const uint8_t *v;
+    const int32_t *bt;
+    const int32_t *cu;
+    const int32_t *seqused;
+    const float *kdesc;
+    const float *vdesc;
+    uint16_t *out;
+    float *ws_o;          // [slots][rows_max][256]
+    float *ws_lse;        // [slots][rows_max]   log2-domain LSE of the scaled logits
+    int32_t *ws_prefix;   // [BH + 1] exclusive prefix of page counts, [BH] = total
+    int32_t *ws_meta;     // [0] = workgroups in use
+    float scale_log2;     // softmax_scale * log2(e)
+    int32_t num_seqs, hq, hkv, log2g, mbps, grid_n, min_pages, rows_max;
+    int64_t num_blocks;
+};
+
+struct MergeParams {
+    const int32_t *cu;
+    const float *vdesc;
+    const float *ws_o;
+    const float *ws_lse;
+    const int32_t *ws_prefix;
+    const int32_t *ws_meta;
+    uint16_t *out;
+    int32_t num_seqs, hq, hkv, log2g, max_q, rows_max;
+};
+
+// ------------------------------------------------------------ primitives --
+
+__device__ __forceinline__ uint32_t fp8x2_lo_to_bf16x2(uint32_t w)
+{
+    // bytes 0,1 of w (two e4m3fn values) -> two bf16 (exact: every e4m3fn
+    // value is a bf16 value).  Scale 1.0 = no scaling.
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+
+__device__ __forceinline__ uint32_t fp8x2_hi_to_bf16x2(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+
+// v_perm_b32: byte i of the result = byte sel.i of the 8-byte value {hi, lo}
+// (selector 0..3 = bytes of lo, 4..7 = bytes of hi).
+__device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    bf16x2_t v;
+    v[0] = (__bf16)a;    // round to nearest even (v_cvt_pk_bf16_f32)
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ floatx4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, const floatx4_t &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int wave_sum(int x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x += __shfl_xor(x, o);
+    return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o);
+        if (lane >= o)
+            x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ float exp2_fast(float x)
+{
+    return __builtin_amdgcn_exp2f(x);      // v_exp_f32; exp2(-inf) = 0
+}
+
+__device__ __forceinline__ int uniform(int x)
+{
+    return __builtin_amdgcn_readfirstlane(x);
+}
+
+// Pages of (sequence, kv head) bg that hold keys for at least one query row.
+// Clamped to the block-table row so a bad length cannot index past it.
+__device__ __forceinline__ int pages_of(const int32_t *cu, const int32_t *seqused, int hkv,
+                                        int mbps, int bg)
+{
+    const int b = bg / hkv;
+    const int lq = cu[b + 1] - cu[b];
+    const int lk = seqused[b];
+    if (lq <= 0 || lk <= 0)
+        return 0;
+    return min((lk + kPage - 1) / kPage, mbps);
+}
+
+// ----------------------------------------------------------- K/V loading --
+
+// Raw K/V registers of one step: two pages (32 keys) of one kv head.
+//  K (fp8): lane (n = l%16, j = l/16) holds key n of each page, bytes
+//           [16(4i+j), +16) for i = 0..3 (the 4 uint4).  k-step s = 2i+h of the
+//           QK MFMA uses dims 16(4i+j) + 8h .. +8 in lane group j.
+//  K (bf16): 8 uint4 per page, uint4 s = bytes [16(4s+j), +16) = dims 8(4s+j) .. +8.
+//  V (fp8): lane (m = l%16, j) holds, for e = 0..7, the 16 bytes of dims
+//           16m .. 16m+15 of key slot 4j + e%4 of page e/4.
+//  V (bf16): same keys, 32 bytes (2 uint4) per key.
+template <int KVT>
+struct StepRegs {
+    static constexpr int kK = KVT == kKvFp8 ? 4 : 8;   // uint4 per page of K per lane
+    static constexpr int kV = KVT == kKvFp8 ? 1 : 2;   // uint4 per key of V per lane
+    uint4 k[2][kK];
+    uint4 v[8][kV];
+};
+
+template <int KVT>
+__device__ __forceinline__ void load_k(StepRegs<KVT> &r, const uint8_t *kbase, int64_t phys_a,
+                                       int64_t phys_b, bool has_b, int hkv, int lane)
+{
+    constexpr int elt = KVT == kKvFp8 ? 1 : 2;
+    const int n = lane & 15, j = lane >> 4;
+    const int64_t row_bytes = (int64_t)kHeadDim * elt;
+    const uint8_t *ra = kbase + ((phys_a * kPage + n) * hkv) * row_bytes;
+#pragma unroll
+    for (int i = 0; i < StepRegs<KVT>::kK; ++i)
+        r.k[0][i] = *(const uint4 *)(ra + (4 * i + j) * 16);
+    if (has_b) {
+        const uint8_t *rb = kbase + ((phys_b * kPage + n) * hkv) * row_bytes;
+#pragma unroll
+        for (int i = 0; i < StepRegs<KVT>::kK; ++i)
+            r.k[1][i] = *(const uint4 *)(rb + (4 * i + j) * 16);
+    } else {
+#pragma unroll
+        for (int i = 0; i < StepRegs<KVT>::kK; ++i)
+            r.k[1][i] = make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <int KVT>
+__device__ __forceinline__ void load_v(StepRegs<KVT> &r, const uint8_t *vbase, int64_t phys_a,
+                                       int64_t phys_b, bool has_b, int hkv, int lane)
+{
+    constexpr int elt = KVT == kKvFp8 ? 1 : 2;
+    constexpr int kV = StepRegs<KVT>::kV;
+    const int m = lane & 15, j = lane >> 4;
+    const int64_t row_bytes = (int64_t)kHeadDim * elt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint8_t *ra = vbase + ((phys_a * kPage + 4 * j + e) * hkv) * row_bytes + m * 16 * kV;
+#pragma unroll
+        for (int c = 0; c < kV; ++c)
+            r.v[e][c] = *(const uint4 *)(ra + 16 * c);
+    }
+    if (has_b) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint8_t *rb = vbase + ((phys_b * kPage + 4 * j + e) * hkv) * row_bytes + m * 16 * kV;
+#pragma unroll
+            for (int c = 0; c < kV; ++c)
+                r.v[4 + e][c] = *(const uint4 *)(rb + 16 * c);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int c = 0; c < kV; ++c)
+                r.v[4 + e][c] = make_uint4(0, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ uint32_t u4get(const uint4 &u, int i)
+{
+    return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+
+// K operand (16 keys x 32 dims, bf16) of k-step s for page a.
+template <int KVT>
+__device__ __forceinline__ bf16x8_t k_operand(const StepRegs<KVT> &r, int a, int s)
+{
+    if constexpr (KVT == kKvFp8) {
+        const uint4 &u = r.k[a][s >> 1];
+        const uint32_t w0 = (s & 1) ? u.z : u.x;
+        const uint32_t w1 = (s & 1) ? u.w : u.y;
+        uint4 o;
+        o.x = fp8x2_lo_to_bf16x2(w0);
+        o.y = fp8x2_hi_to_bf16x2(w0);
+        o.z = fp8x2_lo_to_bf16x2(w1);
+        o.w = fp8x2_hi_to_bf16x2(w1);
+        return __builtin_bit_cast(bf16x8_t, o);
+    } else {
+        return __builtin_bit_cast(bf16x8_t, r.k[a][s]);
+    }
+}
+
+// ------------------------------------------------------- per-step compute --
+
+// Per-wave softmax state of its row tiles.
+template <int RTW>
+struct RowState {
+    floatx4_t o[16][RTW];   // O^T tiles: o[t][rt][e] = O[row l%16][dim 16*(4*(l/16)+e) + t]
+    float m[RTW];           // running max, log2-scaled logits
+    float l[RTW];           // this lane's partial sum of 2^(x - m)
+};
+
+// QK half of a 32-key step: S^T[a][rt] = K(page a) Q^T(rt), 16 keys x 16 rows each.
+//   qs  LDS Q operands of this wave's row tiles: [rt][s][lane] uint4
+template <int RTW, int KVT>
+__device__ __forceinline__ void qk_step(floatx4_t (&S)[2][RTW], const StepRegs<KVT> &r,
+                                        const uint4 *qs, int lane)
+{
+    // The Q operand reads are loop-invariant LDS reads; keep them here rather
+    // than letting them be hoisted out of the page loop (that would pin
+    // RTW*32 registers for the whole loop).
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+            S[a][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        bf16x8_t qop[RTW];
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+            qop[rt] = __builtin_bit_cast(bf16x8_t, qs[(rt * 8 + s) * 64 + lane]);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const bf16x8_t kop = k_operand<KVT>(r, a, s);
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+                S[a][rt] = mfma16(kop, qop[rt], S[a][rt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Softmax + PV half of a 32-key step: masked online softmax on S^T, then
+// O^T += V^T P^T.
+//   masked  this step holds keys some row may not see (the causal tail, keys
+//           at or past seqused_k, or a missing second page); uniform
+//   limit   per row tile: the last key index row (lane%16) may see
+//   key0    index of key 0 of page a; has_b: page b is part of this piece
+//   key_end first key index past the sequence (seqused_k)
+template <int RTW, int KVT>
+__device__ __forceinline__ void softmax_pv_step(RowState<RTW> &st, StepRegs<KVT> &r,
+                                                const floatx4_t (&S)[2][RTW], const int (&limit)[RTW],
+                                                int key0, bool has_b, int key_end, float c,
+                                                int lane, bool masked)
+{
+    const int j = lane >> 4;
+    // logits in log2 units, masked by select (NaN garbage in masked slots is dropped)
+    float x[RTW][8];
+    float mx[RTW];
+    bool need_any = false;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v = S[a][rt][e] * c;
+                if (masked) {
+                    const int key = key0 + 16 * a + 4 * j + e;
+                    const bool ok = (a == 0 || has_b) && key <= limit[rt];
+                    v = ok ? v : -INFINITY;
+                }
+                x[rt][4 * a + e] = v;
+            }
+        float t = x[rt][0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i)
+            t = fmaxf(t, x[rt][i]);
+        t = fmaxf(t, __shfl_xor(t, 16));
+        t = fmaxf(t, __shfl_xor(t, 32));
+        mx[rt] = t;
+        need_any |= t > st.m[rt] + kTau;
+    }
+    if (__any(need_any)) {
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            const bool need = mx[rt] > st.m[rt] + kTau;
+            const float alpha = need ? exp2_fast(st.m[rt] - mx[rt]) : 1.0f;
+            st.m[rt] = need ? mx[rt] : st.m[rt];
+            st.l[rt] *= alpha;
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                st.o[t][rt] *= alpha;
+        }
+    }
+
+    bf16x8_t pop[RTW];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        const float mref = st.m[rt] == -INFINITY ? 0.0f : st.m[rt];
+        float p[8];
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            p[i] = exp2_fast(x[rt][i] - mref);
+            sum += p[i];
+        }
+        st.l[rt] += sum;
+        uint4 w;
+        w.x = pack_bf16x2(p[0], p[1]);
+        w.y = pack_bf16x2(p[2], p[3]);
+        w.z = pack_bf16x2(p[4], p[5]);
+        w.w = pack_bf16x2(p[6], p[7]);
+        pop[rt] = __builtin_bit_cast(bf16x8_t, w);
+    }
+
+    if (masked) {
+        // keys at or past seqused_k may hold NaN bytes: zero their V rows so
+        // 0 * NaN cannot reach O.  (Page b of a short piece was never loaded.)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int key = key0 + 16 * (e >> 2) + 4 * j + (e & 3);
+            if (key >= key_end) {
+#pragma unroll
+                for (int cc = 0; cc < StepRegs<KVT>::kV; ++cc)
+                    r.v[e][cc] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+
+    // PV: V^T operand of dim tile t = dims {16m + t}, 8 keys per lane.
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t A[4][4];      // [x][kp]: tile 4q+x, key pair kp
+        if constexpr (KVT == kKvFp8) {
+#pragma unroll
+            for (int kp = 0; kp < 4; ++kp) {
+                const uint32_t X = u4get(r.v[2 * kp][0], q);
+                const uint32_t Y = u4get(r.v[2 * kp + 1][0], q);
+                const uint32_t lo = byte_perm(Y, X, 0x05010400u);   // X0 Y0 X1 Y1
+                const uint32_t hi = byte_perm(Y, X, 0x07030602u);   // X2 Y2 X3 Y3
+                A[0][kp] = fp8x2_lo_to_bf16x2(lo);
+                A[1][kp] = fp8x2_hi_to_bf16x2(lo);
+                A[2][kp] = fp8x2_lo_to_bf16x2(hi);
+                A[3][kp] = fp8x2_hi_to_bf16x2(hi);
+            }
+        } else {
+            // dims 4q..4q+3 of the lane's 16: uint4 c = q/2, dwords 2(q%2), 2(q%2)+1
+#pragma unroll
+            for (int kp = 0; kp < 4; ++kp) {
+                const int cc = q >> 1;
+                const uint32_t X0 = u4get(r.v[2 * kp][cc], 2 * (q & 1));
+                const uint32_t Y0 = u4get(r.v[2 * kp + 1][cc], 2 * (q & 1));
+                const uint32_t X1 = u4get(r.v[2 * kp][cc], 2 * (q & 1) + 1);
+                const uint32_t Y1 = u4get(r.v[2 * kp + 1][cc], 2 * (q & 1) + 1);
+                A[0][kp] = byte_perm(Y0, X0, 0x05040100u);   // X.lo Y.lo
+                A[1][kp] = byte_perm(Y0, X0, 0x07060302u);   // X.hi Y.hi
+                A[2][kp] = byte_perm(Y1, X1, 0x05040100u);
+                A[3][kp] = byte_perm(Y1, X1, 0x07060302u);
+            }
+        }
+#pragma unroll
+        for (int xx = 0; xx < 4; ++xx) {
+            const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, make_uint4(A[xx][0], A[xx][1], A[xx][2], A[xx][3]));
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+                st.o[4 * q + xx][rt] = mfma16(vop, pop[rt], st.o[4 * q + xx][rt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// -------------------------------------------------------------- locating --
+
+struct Share {
+    int n_eff;      // workgroups in use
+    int s, e;       // flat page range of this workgroup
+    int bg, base;   // first (sequence, kv head) touching s and its flat start
+};
+
+// Every wave runs this (no LDS, no barrier).  Total page count, the number of
+// workgroups in use, this workgroup's range, and where it starts.
+__device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix)
+{
+    const int bh = p.num_seqs * p.hkv;
+    int total = 0;
+    for (int c0 = 0; c0 < bh; c0 += 64) {
+        const int bg = c0 + lane;
+        const int cnt = bg < bh ? pages_of(p.cu, p.seqused, p.hkv, p.mbps, bg) : 0;
+        total += wave_sum(cnt);
+    }
+    Share sh;
+    sh.n_eff = min(p.grid_n, max(1, total / max(1, p.min_pages)));
+    sh.s = (int)(((int64_t)w * total) / sh.n_eff);
+    sh.e = (int)(((int64_t)(w + 1) * total) / sh.n_eff);
+    sh.bg = bh;
+    sh.base = total;
+    bool found = false;
+    int base = 0;
+    for (int c0 = 0; c0 < bh; c0 += 64) {
+        const int bg = c0 + lane;
+        const int cnt = bg < bh ? pages_of(p.cu, p.seqused, p.hkv, p.mbps, bg) : 0;
+        const int incl = wave_incl_scan(cnt, lane);
+        if (write_prefix && bg < bh)
+            p.ws_prefix[bg] = base + incl - cnt;
+        if (!found) {
+            const unsigned long long hit = __ballot(bg < bh && base + incl > sh.s);
+            if (hit) {
+                const int ln = __ffsll((long long)hit) - 1;
+                sh.bg = c0 + ln;
+                sh.base = base + __shfl(incl - cnt, ln);
+                found = true;
+                if (!write_prefix)
+                    break;
+            }
+        }
+        base += __shfl(incl, 63);
+    }
+    if (write_prefix && lane == 0) {
+        p.ws_prefix[bh] = total;
+        p.ws_meta[0] = sh.n_eff;
+    }
+    return sh;
+}
+
+// -------------------------------------------------------------- the kernel --
+
+// RTW: row tiles per wave; NR: row groups (waves sharing the same keys for
+// different rows); NG = 4 / NR key groups splitting each piece's page pairs.
+template <int RTW, int NR, int KVT>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void va_split_kv_kernel(SplitParams p)
+{
+    constexpr int NG = kWaves / NR;
+    constexpr int RT = RTW * NR;                       // row tiles per piece
+    constexpr int kQBytes = RT * 8 * 64 * 16;
+    constexpr int kMergeSlot = (64 * 64 + 2 * 64) * 4;   // one row tile of one wave: O^T, m, l
+    constexpr int kMergeBytes = (NG - 1) * NR * kMergeSlot;
+    constexpr int kLds = kQBytes > kMergeBytes ? kQBytes : kMergeBytes;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
+    uint4 *qs_all = reinterpret_cast<uint4 *>(lds);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const int rg = wave % NR;
+    const int kg = wave / NR;
+    const int w = blockIdx.x;
+    const int G = 1 << p.log2g;
+
+    Share sh = locate(p, w, lane, w == 0 && wave == 0);
+    sh.n_eff = uniform(sh.n_eff);
+    sh.s = uniform(sh.s);
+    sh.e = uniform(sh.e);
+    sh.bg = uniform(sh.bg);
+    sh.base = uniform(sh.base);
+    if (w >= sh.n_eff)
+        return;                                        // uniform over the workgroup
+
+    const float kd = p.kdesc ? p.kdesc[0] : 1.0f;
+    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
+    const float c = p.scale_log2 * kd;
+    constexpr int elt = KVT == kKvFp8 ? 1 : 2;
+    const uint4 *qs_wave = qs_all + rg * RTW * 8 * 64;
+
+    const int bh = p.num_seqs * p.hkv;
+    int s = sh.s, bg = sh.bg, base = sh.base;
+    while (s < sh.e && bg < bh) {
+        const int cnt = uniform(pages_of(p.cu, p.seqused, p.hkv, p.mbps, bg));
+        if (cnt == 0) {
+            ++bg;
+            continue;
+        }
+        const int b = bg / p.hkv;
+        const int g = bg - b * p.hkv;
+        const int q0 = uniform(p.cu[b]);
+        const int lq = uniform(p.cu[b + 1]) - q0;
+        const int lk = uniform(p.seqused[b]);
+        const int ctx = lk - lq;
+        const int p0 = s - base;
+        const int p1 = min(sh.e, base + cnt) - base;
+        const bool whole = (p0 == 0 && p1 == cnt);
+        const int slot = w + bg;
+
+        // ---- stage this piece's packed Q rows in LDS, in operand order
+        __syncthreads();                                // previous piece's merge reads done
+        for (int u = threadIdx.x; u < RT * 512; u += kThreads) {
+            const int rt = u >> 9, ss = (u >> 6) & 7, l = u & 63;
+            const int row = rt * 16 + (l & 15), jj = l >> 4;
+            const int dim = KVT == kKvFp8 ? (4 * (ss >> 1) + jj) * 16 + 8 * (ss & 1) : (4 * ss + jj) * 8;
+            const int t = row >> p.log2g, h = row & (G - 1);
+            uint4 val = make_uint4(0, 0, 0, 0);
+            if (t < lq)
+                val = *(const uint4 *)(p.q + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + dim);
+            qs_all[u] = val;
+        }
+        __syncthreads();
+
+        // ---- per-wave state
+        RowState<RTW> st;
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            st.m[rt] = -INFINITY;
+            st.l[rt] = 0.f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        int limit[RTW];
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            const int row = (rg * RTW + rt) * 16 + (lane & 15);
+            const int t = row >> p.log2g;
+            limit[rt] = min(ctx + t, lk - 1);
+        }
+
+        const int npairs = (p1 - p0 + 1) >> 1;
+        const bool rows_live = (rg * RTW * 16) < lq * G;
+        if (rows_live && kg < npairs) {
+            const int32_t *btrow = p.bt + (int64_t)b * p.mbps;
+            const uint8_t *kbase = p.k + (int64_t)g * kHeadDim * elt;
+            const uint8_t *vbase = p.v + (int64_t)g * kHeadDim * elt;
+            const int64_t maxpage = p.num_blocks - 1;
+            auto phys = [&](int page) -> int64_t {
+                int64_t v = btrow[page];
+                v = v < 0 ? 0 : v;
+                return v > maxpage ? maxpage : v;
+            };
+            // One register set.  K of the next step is issued as soon as this
+            // step's QK has consumed K, V of the next step as soon as PV has
+            // consumed V, so half of every step's loads overlap compute.
+            StepRegs<KVT> r;
+            int k = kg;
+            int pa = p0 + 2 * k;
+            bool hb = pa + 1 < p1;
+            int64_t ya = phys(pa), yb = hb ? phys(pa + 1) : ya;
+            load_k<KVT>(r, kbase, ya, yb, hb, p.hkv, lane);
+            load_v<KVT>(r, vbase, ya, yb, hb, p.hkv, lane);
+            while (true) {
+                floatx4_t S[2][RTW];
+                qk_step<RTW, KVT>(S, r, qs_wave, lane);
+                const int kn = k + NG;
+                const int pn = p0 + 2 * kn;
+                const bool hn = pn + 1 < p1;
+                const bool more = kn < npairs;
+                int64_t yna = 0, ynb = 0;
+                if (more) {
+                    yna = phys(pn);
+                    ynb = hn ? phys(pn + 1) : yna;
+                    load_k<KVT>(r, kbase, yna, ynb, hn, p.hkv, lane);
+                }
+                const int key0 = pa * kPage;
+                softmax_pv_step<RTW, KVT>(st, r, S, limit, key0, hb, lk, c, lane,
+                                          !hb || key0 + 31 > ctx);
+                if (!more)
+                    break;
+                load_v<KVT>(r, vbase, yna, ynb, hn, p.hkv, lane);
+                k = kn;
+                pa = pn;
+                hb = hn;
+            }
+        }
+
+        // full row sums of this wave (the 4 lane groups share a row)
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            float t = st.l[rt];
+            t += __shfl_xor(t, 16);
+            t += __shfl_xor(t, 32);
+            st.l[rt] = t;
+        }
+
+        // ---- merge the NG key groups of each row group through LDS
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            __syncthreads();
+            float *slotbuf = reinterpret_cast<float *>(lds) + (size_t)(rg * (NG - 1)) * (kMergeSlot / 4);
+            if (kg > 0) {
+                float *mine = slotbuf + (size_t)(kg - 1) * (kMergeSlot / 4);
+#pragma unroll
+                for (int t = 0; t < 16; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        mine[(t * 4 + e) * 64 + lane] = st.o[t][rt][e];
+                mine[64 * 64 + lane] = st.m[rt];
+                mine[64 * 64 + 64 + lane] = st.l[rt];
+            }
+            __syncthreads();
+            if (kg == 0) {
+                float mm = st.m[rt];
+#pragma unroll
+                for (int o = 1; o < NG; ++o)
+                    mm = fmaxf(mm, slotbuf[(size_t)(o - 1) * (kMergeSlot / 4) + 64 * 64 + lane]);
+                const float f0 = st.m[rt] == -INFINITY ? 0.f : exp2_fast(st.m[rt] - mm);
+                float L = f0 * st.l[rt];
+#pragma unroll
+                for (int t = 0; t < 16; ++t)
+                    st.o[t][rt] *= f0;
+#pragma unroll
+                for (int o = 1; o < NG; ++o) {
+                    const float *oth = slotbuf + (size_t)(o - 1) * (kMergeSlot / 4);
+                    const float mo = oth[64 * 64 + lane];
+                    const float fo = mo == -INFINITY ? 0.f : exp2_fast(mo - mm);
+                    L += fo * oth[64 * 64 + 64 + lane];
+#pragma unroll
+                    for (int t = 0; t < 16; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            st.o[t][rt][e] += fo * oth[(t * 4 + e) * 64 + lane];
+                }
+                st.m[rt] = mm;
+                st.l[rt] = L;
+            }
+        }
+
+        // ---- write: final rows for a whole sequence, else a partial
+        if (kg == 0) {
+            const int j = lane >> 4;
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt) {
+                const int row = (rg * RTW + rt) * 16 + (lane & 15);
+                const int t = row >> p.log2g;
+                const int h = row & (G - 1);
+                if (t < lq) {
+                    const float L = st.l[rt];
+                    if (whole) {
+                        const float inv = L > 0.f ? vd / L : 0.f;
+                        uint16_t *dst = p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            uint4 lo, hi;
+                            lo.x = pack_bf16x2(st.o[0][rt][e] * inv, st.o[1][rt][e] * inv);
+                            lo.y = pack_bf16x2(st.o[2][rt][e] * inv, st.o[3][rt][e] * inv);
+                            lo.z = pack_bf16x2(st.o[4][rt][e] * inv, st.o[5][rt][e] * inv);
+                            lo.w = pack_bf16x2(st.o[6][rt][e] * inv, st.o[7][rt][e] * inv);
+                            hi.x = pack_bf16x2(st.o[8][rt][e] * inv, st.o[9][rt][e] * inv);
+                            hi.y = pack_bf16x2(st.o[10][rt][e] * inv, st.o[11][rt][e] * inv);
+                            hi.z = pack_bf16x2(st.o[12][rt][e] * inv, st.o[13][rt][e] * inv);
+                            hi.w = pack_bf16x2(st.o[14][rt][e] * inv, st.o[15][rt][e] * inv);
+                            uint4 *d4 = reinterpret_cast<uint4 *>(dst + 64 * j + 16 * e);
+                            d4[0] = lo;
+                            d4[1] = hi;
+                        }
+                    } else {
+                        const float inv = L > 0.f ? 1.0f / L : 0.f;
+                        float *dst = p.ws_o + ((int64_t)slot * p.rows_max + row) * kHeadDim;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            float4 *d4 = reinterpret_cast<float4 *>(dst + 64 * j + 16 * e);
+#pragma unroll
+                            for (int qq = 0; qq < 4; ++qq)
+                                d4[qq] = make_float4(st.o[4 * qq][rt][e] * inv, st.o[4 * qq + 1][rt][e] * inv,
+                                                     st.o[4 * qq + 2][rt][e] * inv, st.o[4 * qq + 3][rt][e] * inv);
+                        }
+                        if (j == 0)
+                            p.ws_lse[(int64_t)slot * p.rows_max + row] =
+                                L > 0.f ? st.m[rt] + __log2f(L) : -INFINITY;
+                    }
+                }
+            }
+        }
+
+        s = base + p1;
+        base += cnt;
+        ++bg;
+    }
+}
+
+// Segment reduce.  One workgroup = 4 consecutive heads of one query token;
+// 64 threads per row, 4 dims each.
+__global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
+{
+    const int gq = (1 << p.log2g) >> 2;               // head quads per group
+    int idx = blockIdx.x;
+    const int hq4 = idx % gq;
+    idx /= gq;
+    const int t = idx % p.max_q;
+    const int bg = idx / p.max_q;
+    const int b = bg / p.hkv;
+    const int g = bg - b * p.hkv;
+    const int q0 = p.cu[b];
+    const int lq = p.cu[b + 1] - q0;
+    if (t >= lq)
+        return;
+    const int bh = p.num_seqs * p.hkv;
+    const int s = p.ws_prefix[bg];
+    const int e = p.ws_prefix[bg + 1];
+    const int total = p.ws_prefix[bh];
+    if (e <= s || total <= 0)
+        return;
+    const int64_t n = p.ws_meta[0];
+    const int w0 = (int)(((int64_t)(s + 1) * n - 1) / total);
+    const int w1 = (int)(((int64_t)e * n - 1) / total);
+    if (w0 == w1)
+        return;                                        // written by the main kernel
+    const int h = hq4 * 4 + (threadIdx.x >> 6);
+    const int row = (t << p.log2g) + h;
+    const int d = (threadIdx.x & 63) * 4;
+
+    float mx = -INFINITY;
+    for (int w = w0; w <= w1; ++w)
+        mx = fmaxf(mx, p.ws_lse[(int64_t)(w + bg) * p.rows_max + row]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float den = 0.f;
+    if (mx > -INFINITY) {
+        for (int w = w0; w <= w1; ++w) {
+            const int64_t sl = (int64_t)(w + bg) * p.rows_max + row;
+            const float l = p.ws_lse[sl];
+            const float f = l == -INFINITY ? 0.f : exp2_fast(l - mx);
+            const float4 o = *reinterpret_cast<const float4 *>(p.ws_o + sl * kHeadDim + d);
+            den += f;
+            acc.x += f * o.x;
+            acc.y += f * o.y;
+            acc.z += f * o.z;
+            acc.w += f * o.w;
+        }
+    }
+    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
+    const float inv = den > 0.f ? vd / den : 0.f;
+    uint2 pk;
+    pk.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+    pk.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+    const int G = 1 << p.log2g;
+    *reinterpret_cast<uint2 *>(p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + d) = pk;
+}
+
+__global__ __launch_bounds__(kThreads) void va_fp8_to_bf16_kernel(const uint8_t *in, uint16_t *out, int64_t n)
+{
+    const int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+    if (i >= n)
+        return;
+    uint32_t w = 0;
+    for (int k = 0; k < 4 && i + k < n; ++k)
+        w |= (uint32_t)in[i + k] << (8 * k);
+    const uint32_t lo = fp8x2_lo_to_bf16x2(w);
+    const uint32_t hi = fp8x2_hi_to_bf16x2(w);
+    const uint16_t r[4] = {(uint16_t)(lo & 0xFFFF), (uint16_t)(lo >> 16), (uint16_t)(hi & 0xFFFF),
+                           (uint16_t)(hi >> 16)};
+    for (int k = 0; k < 4 && i + k < n; ++k)
+        out[i + k] = r[k];
+}
+
+// ------------------------------------------------------------------ host --
+
+typedef void (*split_fn)(SplitParams);
+
+template <int RTW, int NR, int KVT>
+void launch_split(SplitParams p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((va_split_kv_kernel<RTW, NR, KVT>), dim3(grid), dim3(kThreads), 0, s, p);
+}
+
+typedef void (*launch_fn)(SplitParams, int, hipStream_t);
+
+struct Variant {
+    int rtw, nr;
+    launch_fn fp8, bf16;
+};
+
+// Row tiles needed -> (row tiles per wave, row groups).  Three or four row
+// tiles use two row groups of two, so a wave's O^T accumulators stay at 128
+// registers (three row tiles per wave do not fit the register file without
+// spilling).
+const Variant kVariants[5] = {
+    {1, 1, nullptr, nullptr},
+    {1, 1, launch_split<1, 1, kKvFp8>, launch_split<1, 1, kKvBf16>},
+    {2, 1, launch_split<2, 1, kKvFp8>, launch_split<2, 1, kKvBf16>},
+    {2, 2, launch_split<2, 2, kKvFp8>, launch_split<2, 2, kKvBf16>},
+    {2, 2, launch_split<2, 2, kKvFp8>, launch_split<2, 2, kKvBf16>},
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+struct va_plan_s {
+    va_problem prob;
+    int log2g;
+    int rt;             // row tiles the packed rows need (selects the kernel variant)
+    int grid;           // split-KV workgroups
+    int min_pages;
+    int rows_max;
+    int64_t slots;
+    size_t off_prefix, off_lse, off_o, ws_bytes;
+};
+
+extern "C" {
+
+const char *va_status_str(va_status s)
+{
+    switch (s) {
+    case VA_OK: return "ok";
+    case VA_ERR_INVALID_ARG: return "invalid argument";
+    case VA_ERR_UNSUPPORTED: return "unsupported problem (outside the supported domain)";
+    case VA_ERR_WORKSPACE: return "workspace missing or too small";
+    case VA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+va_status va_plan(const va_problem *pr, va_plan_t *out)
+{
+    if (!pr || !out)
+        return VA_ERR_INVALID_ARG;
+    *out = nullptr;
+    const va_problem &p = *pr;
+    if (p.num_seqs < 1 || p.num_q_heads < 1 || p.num_kv_heads < 1 || p.head_dim < 1 ||
+        p.page_size < 1 || p.max_seqlen_q < 1 || p.max_seqlen_k < 0 || p.max_blocks_per_seq < 1 ||
+        p.num_blocks < 1 || p.total_q < 0 || p.num_cus < 0 || p.force_grid < 0)
+        return VA_ERR_INVALID_ARG;
+    if (p.total_q > (int64_t)p.num_seqs * p.max_seqlen_q)
+        return VA_ERR_INVALID_ARG;
+    if (p.q_dtype != VA_DT_BF16 && p.q_dtype != VA_DT_FP8_E4M3FN)
+        return VA_ERR_INVALID_ARG;
+    if (p.kv_dtype != VA_DT_BF16 && p.kv_dtype != VA_DT_FP8_E4M3FN)
+        return VA_ERR_INVALID_ARG;
+    if (p.q_dtype != VA_DT_BF16)
+        return VA_ERR_UNSUPPORTED;
+    if (p.head_dim != kHeadDim || p.page_size != kPage)
+        return VA_ERR_UNSUPPORTED;
+    if (p.num_q_heads % p.num_kv_heads != 0)
+        return VA_ERR_UNSUPPORTED;
+    const int G = p.num_q_heads / p.num_kv_heads;
+    if (G != 4 && G != 8 && G != 16)
+        return VA_ERR_UNSUPPORTED;
+    if (p.max_seqlen_q > 4)
+        return VA_ERR_UNSUPPORTED;
+    const int64_t bh = (int64_t)p.num_seqs * p.num_kv_heads;
+    if (bh > 65536 || bh * (int64_t)p.max_blocks_per_seq > INT32_MAX)
+        return VA_ERR_UNSUPPORTED;
+    if ((int64_t)p.max_seqlen_k > (int64_t)p.max_blocks_per_seq * kPage)
+        return VA_ERR_INVALID_ARG;
+
+    int cus = p.num_cus;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess)
+            return VA_ERR_HIP;
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return VA_ERR_HIP;
+        if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+            return VA_ERR_UNSUPPORTED;
+        cus = prop.multiProcessorCount;
+        if (cus < 1)
+            return VA_ERR_HIP;
+    }
+
+    va_plan_s *pl = new (std::nothrow) va_plan_s;
+    if (!pl)
+        return VA_ERR_INVALID_ARG;
+    pl->prob = p;
+    pl->log2g = G == 4 ? 2 : G == 8 ? 3 : 4;
+    const int rows = G * p.max_seqlen_q;
+    pl->rt = (rows + 15) / 16;
+    pl->rows_max = 16 * kVariants[pl->rt].rtw * kVariants[pl->rt].nr;
+    pl->grid = p.force_grid > 0 ? p.force_grid : cus;
+    pl->min_pages = 8;
+    pl->slots = (int64_t)pl->grid + bh;
+    size_t off = 256;                                   // meta
+    pl->off_prefix = off;
+    off = align_up(off + (size_t)(bh + 1) * 4, 256);
+    pl->off_lse = off;
+    off = align_up(off + (size_t)pl->slots * pl->rows_max * 4, 256);
+    pl->off_o = off;
+    off = align_up(off + (size_t)pl->slots * pl->rows_max * kHeadDim * 4, 256);
+    pl->ws_bytes = off;
+    *out = pl;
+    return VA_OK;
+}
+
+va_status va_plan_workspace_bytes(va_plan_t plan, size_t *bytes)
+{
+    if (!plan || !bytes)
+        return VA_ERR_INVALID_ARG;
+    *bytes = plan->ws_bytes;
+    return VA_OK;
+}
+
+va_status va_plan_grid(va_plan_t plan, int32_t *grid)
+{
+    if (!plan || !grid)
+        return VA_ERR_INVALID_ARG;
+    *grid = plan->grid;
+    return VA_OK;
+}
+
+void va_plan_destroy(va_plan_t plan)
+{
+    delete plan;
+}
+
+va_status va_run_stage(va_plan_t plan, int32_t stage, const void *q, const void *k_pool,
+                       const void *v_pool, const int32_t *block_table,
+                       const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                       float softmax_scale, const float *k_descale, const float *v_descale,
+                       void *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!plan)
+        return VA_ERR_INVALID_ARG;
+    if (stage != VA_STAGE_ALL && stage != VA_STAGE_SPLIT_KV && stage != VA_STAGE_MERGE)
+        return VA_ERR_INVALID_ARG;
+    if (!q || !k_pool || !v_pool || !block_table || !cu_seqlens_q || !seqused_k || !out)
+        return VA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < plan->ws_bytes)
+        return VA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+        return VA_ERR_INVALID_ARG;
+    const uintptr_t align16 = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pool) |
+                              reinterpret_cast<uintptr_t>(v_pool) | reinterpret_cast<uintptr_t>(out);
+    if (align16 & 15)
+        return VA_ERR_INVALID_ARG;
+    const va_problem &pr = plan->prob;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+
+    if (stage == VA_STAGE_ALL || stage == VA_STAGE_SPLIT_KV) {
+        SplitParams sp;
+        sp.q = static_cast<const uint16_t *>(q);
+        sp.k = static_cast<const uint8_t *>(k_pool);
+        sp.v = static_cast<const uint8_t *>(v_pool);
+        sp.bt = block_table;
+        sp.cu = cu_seqlens_q;
+        sp.seqused = seqused_k;
+        sp.kdesc = k_descale;
+        sp.vdesc = v_descale;
+        sp.out = static_cast<uint16_t *>(out);
+        sp.ws_o = reinterpret_cast<float *>(ws + plan->off_o);
+        sp.ws_lse = reinterpret_cast<float *>(ws + plan->off_lse);
+        sp.ws_prefix = reinterpret_cast<int32_t *>(ws + plan->off_prefix);
+        sp.ws_meta = reinterpret_cast<int32_t *>(ws);
+        sp.scale_log2 = softmax_scale * 1.4426950408889634f;
+        sp.num_seqs = pr.num_seqs;
+        sp.hq = pr.num_q_heads;
+        sp.hkv = pr.num_kv_heads;
+        sp.log2g = plan->log2g;
+        sp.mbps = pr.max_blocks_per_seq;
+        sp.grid_n = plan->grid;
+        sp.min_pages = plan->min_pages;
+        sp.rows_max = plan->rows_max;
+        sp.num_blocks = pr.num_blocks;
+        const Variant &v = kVariants[plan->rt];
+        launch_fn fn = pr.kv_dtype == VA_DT_FP8_E4M3FN ? v.fp8 : v.bf16;
+        fn(sp, plan->grid, s);
+        if (hipGetLastError() != hipSuccess)
+            return VA_ERR_HIP;
+    }
+    if (stage == VA_STAGE_ALL || stage == VA_STAGE_MERGE) {
+        MergeParams mp;
+        mp.cu = cu_seqlens_q;
+        mp.vdesc = v_descale;
+        mp.ws_o = reinterpret_cast<const float *>(ws + plan->off_o);
+        mp.ws_lse = reinterpret_cast<const float *>(ws + plan->off_lse);
+        mp.ws_prefix = reinterpret_cast<const int32_t *>(ws + plan->off_prefix);
+        mp.ws_meta = reinterpret_cast<const int32_t *>(ws);
+        mp.out = static_cast<uint16_t *>(out);
+        mp.num_seqs = pr.num_seqs;
+        mp.hq = pr.num_q_heads;
+        mp.hkv = pr.num_kv_heads;
+        mp.log2g = plan->log2g;
+        mp.max_q = pr.max_seqlen_q;
+        mp.rows_max = plan->rows_max;
+        const int64_t blocks = (int64_t)pr.num_seqs * pr.num_kv_heads * pr.max_seqlen_q *
+                               ((pr.num_q_heads / pr.num_kv_heads) / 4);
+        if (blocks > 0) {
+            hipLaunchKernelGGL(va_merge_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, mp);
+            if (hipGetLastError() != hipSuccess)
+                return VA_ERR_HIP;
+        }
+    }
+    return VA_OK;
+}
+
+va_status va_run(va_plan_t plan, const void *q, const void *k_pool, const void *v_pool,
+                 const int32_t *block_table, const int32_t *cu_seqlens_q,
+                 const int32_t *seqused_k, float softmax_scale, const float *k_descale,
+                 const float *v_descale, void *out, void *workspace, size_t workspace_bytes,
+                 void *stream)
+{
+    return va_run_stage(plan, VA_STAGE_ALL, q, k_pool, v_pool, block_table, cu_seqlens_q,
+                        seqused_k, softmax_scale, k_descale, v_descale, out, workspace,
+                        workspace_bytes, stream);
+}
+
+va_status va_fp8_to_bf16(const uint8_t *in, uint16_t *out, int64_t n, void *stream)
+{
+    if (n < 0 || (n > 0 && (!in || !out)))
+        return VA_ERR_INVALID_ARG;
+    if (n == 0)
+        return VA_OK;
+    const int64_t threads = (n + 3) / 4;
+    const int64_t blocks = (threads + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(va_fp8_to_bf16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), in, out, n);
+    return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+}
+
+}  // extern "C"

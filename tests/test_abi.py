@@ -1,0 +1,113 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/va.h declares, and va_plan / va_run reject bad arguments with the
+documented status codes (no kernel is launched in any of these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_gqa_attention_va_amd as va
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "va.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(va_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("va_plan", "va_plan_workspace_bytes", "va_run", "va_plan_destroy", "va_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    lib = va.library()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) == set(va.EXPORTED)
+
+
+def base_problem(**kw):
+    d = dict(num_seqs=16, num_q_heads=16, num_kv_heads=1, max_seqlen_q=4, max_seqlen_k=32768,
+             max_blocks_per_seq=2048, num_blocks=32768, total_q=64, kv_dtype="fp8", num_cus=256)
+    d.update(kw)
+    return d
+
+
+def test_plan_accepts_the_workloads():
+    for kw in (dict(), dict(num_q_heads=32, num_kv_heads=2), dict(num_q_heads=4, max_seqlen_q=1, total_q=16),
+               dict(num_q_heads=8, kv_dtype="bf16", max_seqlen_q=3, total_q=48)):
+        p = va.Plan(**base_problem(**kw))
+        assert p.workspace_bytes > 0 and p.grid == 256
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=12), va.VA_ERR_UNSUPPORTED),          # G = 12
+    (dict(num_q_heads=2, num_kv_heads=1), va.VA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=16, num_kv_heads=3), va.VA_ERR_UNSUPPORTED),
+    (dict(head_dim=128), va.VA_ERR_UNSUPPORTED),
+    (dict(page_size=32), va.VA_ERR_UNSUPPORTED),
+    (dict(max_seqlen_q=5, total_q=64), va.VA_ERR_UNSUPPORTED),
+    (dict(q_dtype="fp8"), va.VA_ERR_UNSUPPORTED),
+    (dict(num_seqs=0), va.VA_ERR_INVALID_ARG),
+    (dict(total_q=65), va.VA_ERR_INVALID_ARG),
+    (dict(max_seqlen_q=0), va.VA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), va.VA_ERR_INVALID_ARG),
+    (dict(max_seqlen_k=32769), va.VA_ERR_INVALID_ARG),
+    (dict(num_cus=-1), va.VA_ERR_INVALID_ARG),
+])
+def test_plan_rejects(kw, status):
+    with pytest.raises(va.VaError) as e:
+        va.Plan(**base_problem(**kw))
+    assert e.value.status == status
+
+
+def test_plan_rejects_bad_dtype_enum_and_null():
+    lib = va.library()
+    pr = va._Problem(1, 16, 1, 256, 16, 4, 100, 7, 7, 4, 1, 9, 256, 0)   # kv_dtype 9
+    h = ctypes.c_void_p()
+    assert lib.va_plan(ctypes.byref(pr), ctypes.byref(h)) == va.VA_ERR_INVALID_ARG
+    assert lib.va_plan(None, ctypes.byref(h)) == va.VA_ERR_INVALID_ARG
+    pr.kv_dtype = 2
+    assert lib.va_plan(ctypes.byref(pr), None) == va.VA_ERR_INVALID_ARG
+
+
+def test_force_grid_sets_grid_and_workspace_grows_with_it():
+    a = va.Plan(**base_problem(force_grid=7))
+    b = va.Plan(**base_problem(force_grid=700))
+    assert a.grid == 7 and b.grid == 700 and b.workspace_bytes > a.workspace_bytes
+
+
+def _run_args(plan, ws_bytes, **over):
+    fake = ctypes.c_void_p(0x10000)          # never dereferenced: argument checks fail first
+    args = dict(q=fake, k=fake, v=fake, bt=fake, cu=fake, sk=fake, out=fake, ws=fake)
+    args.update(over)
+    return (plan._h, args["q"], args["k"], args["v"], args["bt"], args["cu"], args["sk"],
+            ctypes.c_float(0.0625), None, None, args["out"], args["ws"],
+            ctypes.c_size_t(ws_bytes), None)
+
+
+def test_run_rejects_null_pointers_and_short_workspace():
+    lib = va.library()
+    plan = va.Plan(**base_problem())
+    n = plan.workspace_bytes
+    assert lib.va_run(*_run_args(plan, n, q=None)) == va.VA_ERR_INVALID_ARG
+    assert lib.va_run(*_run_args(plan, n, out=None)) == va.VA_ERR_INVALID_ARG
+    assert lib.va_run(*_run_args(plan, n, bt=None)) == va.VA_ERR_INVALID_ARG
+    assert lib.va_run(*_run_args(plan, n - 1)) == va.VA_ERR_WORKSPACE
+    assert lib.va_run(*_run_args(plan, n, ws=None)) == va.VA_ERR_WORKSPACE
+    assert lib.va_run(*_run_args(plan, n, ws=ctypes.c_void_p(0x10010))) == va.VA_ERR_INVALID_ARG
+    assert lib.va_run(*_run_args(plan, n, q=ctypes.c_void_p(0x10002))) == va.VA_ERR_INVALID_ARG
+    assert lib.va_run(None, *_run_args(plan, n)[1:]) == va.VA_ERR_INVALID_ARG
+    assert lib.va_run_stage(plan._h, 7, *_run_args(plan, n)[1:]) == va.VA_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in range(5):
+        assert va.status_str(s) and va.status_str(s) != "unknown status"
+    assert va.status_str(99) == "unknown status"

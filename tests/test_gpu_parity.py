@@ -1,0 +1,168 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: every element within |gpu - ref| <= 1e-2 + 1e-2*|ref|.  This is the
+tolerance of the page test's assert_close (sglang PR #36330 summary page,
+"Key source snippets").  In addition the relative RMS error must stay <= 5e-3.
+Small problems are compared on every output row.  The full-size workloads are
+compared on seeded samples of rows that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_gqa_attention_va_amd as va
+import va_inputs
+from gpu_util import as_f64, check_problem, compare, note, run, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def test_fp8_dequant_all_codes_matches_oracle_decoder():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).cuda()
+    got = va.fp8_to_bf16(codes).float().cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    ref = np.array([oracle.fp8_e4m3fn_to_float(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_tiny_configs_all_rows(cfg):
+    p = va_inputs.config(cfg)
+    check_problem(p)
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_tiny_configs_unpoisoned(cfg):
+    # exactly the page test's construction (identity table, no poison)
+    p = va_inputs.config(cfg, poison=False)
+    check_problem(p)
+
+
+RAGGED = [
+    # q_lens, kv_lens, Hq, Hkv, dtype, kd, vd
+    ([1, 2, 3, 4, 4], [1, 17, 100, 1000, 4099], 16, 1, "fp8", 1.0, 1.0),
+    ([4, 3], [33, 2050], 32, 2, "fp8", 1.5, 0.75),
+    ([2, 0, 4], [47, 31, 4], 8, 1, "fp8", 1.0, 1.0),
+    ([3, 1, 2, 4], [48, 15, 64, 515], 4, 1, "fp8", 0.5, 2.0),
+    ([4, 2], [1024, 769], 16, 1, "bf16", 1.0, 1.0),
+    ([1, 3, 2], [5000, 129, 3], 8, 2, "bf16", 1.25, 0.5),
+    ([4, 4, 4, 4], [4, 5, 16, 17], 16, 4, "fp8", 1.0, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[f"r{i}" for i in range(len(RAGGED))])
+def test_ragged_shapes_all_rows(case):
+    ql, kl, hq, hkv, dt, kd, vd = case
+    p = va_inputs.custom(ql, kl, hq, hkv, dt, seed=sum(kl) + hq, k_descale=kd, v_descale=vd,
+                         name=f"ragged{hq}/{hkv}{dt}")
+    check_problem(p)
+
+
+@pytest.mark.parametrize("grid", [1, 2, 7, 64, 1000])
+def test_forced_grid_sizes_agree(grid):
+    p = va_inputs.custom([4, 2, 3, 1], [3000, 769, 100, 40], 16, 1, "fp8", seed=42,
+                         name=f"grid{grid}")
+    check_problem(p, force_grid=grid)
+
+
+def test_forced_grid_sizes_agree_with_each_other():
+    p = va_inputs.custom([4, 2, 3], [4000, 1500, 33], 16, 2, "fp8", seed=43)
+    dev = to_device(p)
+    outs = [as_f64(run(p, dev=dev, force_grid=g)) for g in (1, 3, 16, 256)]
+    for o in outs[1:]:
+        compare(o, outs[0], "grid vs grid1")
+
+
+def test_run_to_run_bitwise_deterministic():
+    p = va_inputs.custom([4, 3, 2], [9000, 3000, 700], 16, 1, "fp8", seed=44)
+    dev = to_device(p)
+    plan = va.Plan.for_problem(p)
+    a = run(p, dev=dev, plan=plan).clone()
+    b = run(p, dev=dev, plan=plan).clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_first_verify_token_with_one_key_is_exact():
+    # Lk == Lq: query token 0 sees key 0 only, so out = bf16(v_descale * V[key 0])
+    p = va_inputs.custom([4, 3], [4, 3], 16, 1, "fp8", seed=45, v_descale=1.5)
+    out = run(p).float().cpu().numpy().reshape(p.total_q, p.num_q_heads, -1)
+    V = torch.from_numpy(p.v).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for b in range(p.num_seqs):
+        q0 = p.cu_seqlens_q[b]
+        v0 = V[p.block_table[b, 0], 0, 0] * p.v_descale
+        expect = torch.from_numpy(v0).to(torch.bfloat16).float().numpy()
+        for h in range(p.num_q_heads):
+            assert np.array_equal(out[q0, h], expect)
+
+
+def test_zero_query_gives_mean_of_visible_values():
+    p = va_inputs.custom([4, 2], [3000, 77], 16, 1, "fp8", seed=46)
+    p.q[:] = 0
+    check_problem(p)
+
+
+def test_segment_markers_expose_a_dropped_or_doubled_piece():
+    # Uniform logits (Q = 0) and V zero except a marker 256.0 in dimension
+    # (page index mod 256) of every key.  Each output dimension is then
+    # 256 * (visible keys in pages of that residue) / (visible keys): a piece
+    # of the split that went missing or was counted twice moves whole
+    # dimensions by far more than the tolerance.
+    p = va_inputs.custom([4, 3], [40000, 20000], 16, 1, "fp8", seed=47, poison=False)
+    p.q[:] = 0
+    p.v[:] = 0
+    for b in range(p.num_seqs):
+        for lp in range(-(-int(p.seqused_k[b]) // 16)):
+            p.v[p.block_table[b, lp], :, 0, lp % 256] = 0x78      # e4m3fn 256.0
+    check_problem(p)
+    check_problem(p, force_grid=37)
+
+
+def test_q_len_zero_rows_untouched_and_others_correct():
+    p = va_inputs.custom([0, 4, 0, 2], [100, 3000, 50, 20], 8, 1, "fp8", seed=48)
+    check_problem(p)
+
+
+def test_graph_capture_replay_matches_eager():
+    p = va_inputs.custom([4, 2, 3], [5000, 800, 64], 16, 1, "fp8", seed=49)
+    dev = to_device(p)
+    plan = va.Plan.for_problem(p)
+    ws = plan.workspace()
+    eager = run(p, dev=dev, plan=plan, workspace=ws).clone()
+    out = torch.empty_like(dev["q"])
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        plan.run(dev["q"], dev["k"], dev["v"], dev["bt"], dev["cu"], dev["sk"], p.scale,
+                 dev["kd"], dev["vd"], out=out, workspace=ws)
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+
+
+# ------------------------------------------------------- full-size workloads
+
+def _sampled(p, n_rows, seed=0, **kw):
+    rows = va_inputs.sample_rows(p, n_rows, seed=seed)
+    note(f"  {p.name}: {len(rows)} sampled rows")
+    return check_problem(p, rows=rows, **kw)
+
+
+def test_config2_long_context_sampled():
+    _sampled(va_inputs.config(2), 48)
+
+
+def test_config3_high_concurrency_sampled():
+    _sampled(va_inputs.config(3), 48)
+
+
+@pytest.mark.parametrize("variant", range(len(va_inputs.SWEEP_VARIANTS)),
+                         ids=[f"g{g}-{d}" for g, d in va_inputs.SWEEP_VARIANTS])
+def test_config4_shape_sweep_sampled(variant):
+    _sampled(va_inputs.config(4, variant), 24)
