@@ -382,12 +382,12 @@ __device__ __forceinline__ void softmax_pv_step(RowState<RTW> &st, StepRegs<KVT>
     }
 
     if (masked) {
-        // keys at or past seqused_k may hold NaN bytes: zero their V rows so
-        // 0 * NaN cannot reach O.  (Page b of a short piece was never loaded.)
+        // keys at or past seqused_k may hold NaN bytes, and page b of a short
+        // piece holds no key of it: zero their V rows so 0 * NaN cannot reach O.
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int key = key0 + 16 * (e >> 2) + 4 * j + (e & 3);
-            if (key >= key_end) {
+            if (key >= key_end || (e >= 4 && !has_b)) {
 #pragma unroll
                 for (int cc = 0; cc < StepRegs<KVT>::kV; ++cc)
                     r.v[e][cc] = make_uint4(0, 0, 0, 0);
@@ -732,6 +732,384 @@ void va_split_kv_kernel(SplitParams p)
     }
 }
 
+// ------------------------------------------------- FP8 kernel, LDS ring --
+
+// Direct global -> LDS copy of 16 bytes per lane: global address sbase + voff
+// (per lane), LDS address lds_addr + 16 * lane.  Issued as inline asm so the
+// compiler does not insert a conservative wait for it before every LDS read;
+// the ring below waits on vmcnt itself.  No other vector-memory instruction
+// is issued inside the page loop, so the counts are exact.
+// M0 is written inside the statement and listed as clobbered; nothing else in
+// these kernels reads M0 (clang warns that it is a reserved register).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// One ring stage = one step (two pages) of one kv head, 16 KiB:
+//   [K page a | K page b | V page a | V page b], 4 KiB each, 16 key rows of
+//   256 bytes.  The 16-byte chunk c of key row n sits at slot c ^ n of the row
+//   (XOR swizzle), so the operand reads below touch 16 distinct slots per 16 lanes.
+constexpr int kStageBytes = 16384;
+constexpr int kDmaPerStep = 16;          // 4 pages x 4 KiB / 1 KiB per instruction
+
+// Lane offsets of the 4 copy instructions of one page: instruction i, lane l
+// writes LDS bytes [1024 i + 16 l, +16) = key row n = 4i + l/16, slot l%16, so it
+// fetches chunk (l%16) ^ n of that key row.  16 lanes read one 256-byte row.
+__device__ __forceinline__ void dma_lane_offsets(uint32_t (&off)[4], int hkv, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int n = 4 * i + (lane >> 4);
+        off[i] = (uint32_t)(n * hkv * kHeadDim + (((lane & 15) ^ n) * 16));
+    }
+}
+
+// Copy one step (pages a and b of the kv head) into a ring stage.  Always 16
+// instructions: a missing page b re-reads page a (masked out later), so the
+// vmcnt bookkeeping is the same for every step.
+__device__ __forceinline__ void dma_step(uint32_t stage, const uint8_t *kb, const uint8_t *vb,
+                                         int64_t ya, int64_t yb, int64_t page_bytes,
+                                         const uint32_t (&off)[4])
+{
+    const uint8_t *ka = kb + ya * page_bytes;
+    const uint8_t *kbb = kb + yb * page_bytes;
+    const uint8_t *va = vb + ya * page_bytes;
+    const uint8_t *vbb = vb + yb * page_bytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        dma16(ka, off[i], stage + 1024 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        dma16(kbb, off[i], stage + 4096 + 1024 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        dma16(va, off[i], stage + 8192 + 1024 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        dma16(vbb, off[i], stage + 12288 + 1024 * i);
+}
+
+// QK half of a step with K read from a ring stage (same math as qk_step).
+template <int RT>
+__device__ __forceinline__ void qk_lds(floatx4_t (&S)[2][RT], const unsigned char *stage,
+                                       const uint4 *qs, int lane)
+{
+    const int n = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            S[a][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    uint4 kr[2];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        if ((s & 1) == 0) {
+            const int chunk = 4 * (s >> 1) + j;
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+                kr[a] = *reinterpret_cast<const uint4 *>(stage + 4096 * a + 256 * n + 16 * (chunk ^ n));
+        }
+        bf16x8_t qop[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            qop[rt] = __builtin_bit_cast(bf16x8_t, qs[(rt * 8 + s) * 64 + lane]);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const uint32_t w0 = (s & 1) ? kr[a].z : kr[a].x;
+            const uint32_t w1 = (s & 1) ? kr[a].w : kr[a].y;
+            uint4 o;
+            o.x = fp8x2_lo_to_bf16x2(w0);
+            o.y = fp8x2_hi_to_bf16x2(w0);
+            o.z = fp8x2_lo_to_bf16x2(w1);
+            o.w = fp8x2_hi_to_bf16x2(w1);
+            const bf16x8_t kop = __builtin_bit_cast(bf16x8_t, o);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                S[a][rt] = mfma16(kop, qop[rt], S[a][rt]);
+        }
+        if (s & 1)
+            __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// V rows of a step from a ring stage into the register order softmax_pv_step
+// expects: v[e] = dims 16m .. 16m+15 of key slot 4j + e%4 of page e/4.
+__device__ __forceinline__ void v_from_lds(StepRegs<kKvFp8> &r, const unsigned char *stage, int lane)
+{
+    const int m = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int n = 4 * j + (e & 3);
+        r.v[e][0] = *reinterpret_cast<const uint4 *>(stage + 8192 + 4096 * (e >> 2) + 256 * n + 16 * (m ^ n));
+    }
+}
+
+// Merge the softmax states of the NG key groups of each row group through
+// LDS.  The key-group-0 wave of each row group then writes its rows: final
+// rows when the piece is the whole sequence, else the piece's partial.
+template <int RTW, int NR>
+__device__ __forceinline__ void merge_and_write(RowState<RTW> &st, unsigned char *lds, const SplitParams &p,
+                                                int kg, int rg, int lane, int lq, int q0, int g,
+                                                int slot, bool whole, float vd)
+{
+    constexpr int NG = kWaves / NR;
+    constexpr int kMergeFloats = 64 * 64 + 2 * 64;        // one row tile of one wave: O^T, m, l
+    const int G = 1 << p.log2g;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        float t = st.l[rt];
+        t += __shfl_xor(t, 16);
+        t += __shfl_xor(t, 32);
+        st.l[rt] = t;
+    }
+    float *buf = reinterpret_cast<float *>(lds) + (size_t)rg * (NG - 1) * kMergeFloats;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        __syncthreads();
+        if (kg > 0) {
+            float *mine = buf + (size_t)(kg - 1) * kMergeFloats;
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    mine[(t * 4 + e) * 64 + lane] = st.o[t][rt][e];
+            mine[64 * 64 + lane] = st.m[rt];
+            mine[64 * 64 + 64 + lane] = st.l[rt];
+        }
+        __syncthreads();
+        if (kg == 0) {
+            float mm = st.m[rt];
+#pragma unroll
+            for (int o = 1; o < NG; ++o)
+                mm = fmaxf(mm, buf[(size_t)(o - 1) * kMergeFloats + 64 * 64 + lane]);
+            const float f0 = st.m[rt] == -INFINITY ? 0.f : exp2_fast(st.m[rt] - mm);
+            float L = f0 * st.l[rt];
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                st.o[t][rt] *= f0;
+#pragma unroll
+            for (int o = 1; o < NG; ++o) {
+                const float *oth = buf + (size_t)(o - 1) * kMergeFloats;
+                const float mo = oth[64 * 64 + lane];
+                const float fo = mo == -INFINITY ? 0.f : exp2_fast(mo - mm);
+                L += fo * oth[64 * 64 + 64 + lane];
+#pragma unroll
+                for (int t = 0; t < 16; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        st.o[t][rt][e] += fo * oth[(t * 4 + e) * 64 + lane];
+            }
+            st.m[rt] = mm;
+            st.l[rt] = L;
+        }
+    }
+    if (kg != 0)
+        return;
+    const int j = lane >> 4;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        const int row = (rg * RTW + rt) * 16 + (lane & 15);
+        const int t = row >> p.log2g;
+        const int h = row & (G - 1);
+        if (t >= lq)
+            continue;
+        const float L = st.l[rt];
+        if (whole) {
+            const float inv = L > 0.f ? vd / L : 0.f;
+            uint16_t *dst = p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint4 lo, hi;
+                lo.x = pack_bf16x2(st.o[0][rt][e] * inv, st.o[1][rt][e] * inv);
+                lo.y = pack_bf16x2(st.o[2][rt][e] * inv, st.o[3][rt][e] * inv);
+                lo.z = pack_bf16x2(st.o[4][rt][e] * inv, st.o[5][rt][e] * inv);
+                lo.w = pack_bf16x2(st.o[6][rt][e] * inv, st.o[7][rt][e] * inv);
+                hi.x = pack_bf16x2(st.o[8][rt][e] * inv, st.o[9][rt][e] * inv);
+                hi.y = pack_bf16x2(st.o[10][rt][e] * inv, st.o[11][rt][e] * inv);
+                hi.z = pack_bf16x2(st.o[12][rt][e] * inv, st.o[13][rt][e] * inv);
+                hi.w = pack_bf16x2(st.o[14][rt][e] * inv, st.o[15][rt][e] * inv);
+                uint4 *d4 = reinterpret_cast<uint4 *>(dst + 64 * j + 16 * e);
+                d4[0] = lo;
+                d4[1] = hi;
+            }
+        } else {
+            const float inv = L > 0.f ? 1.0f / L : 0.f;
+            float *dst = p.ws_o + ((int64_t)slot * p.rows_max + row) * kHeadDim;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float4 *d4 = reinterpret_cast<float4 *>(dst + 64 * j + 16 * e);
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq)
+                    d4[qq] = make_float4(st.o[4 * qq][rt][e] * inv, st.o[4 * qq + 1][rt][e] * inv,
+                                         st.o[4 * qq + 2][rt][e] * inv, st.o[4 * qq + 3][rt][e] * inv);
+            }
+            if (j == 0)
+                p.ws_lse[(int64_t)slot * p.rows_max + row] = L > 0.f ? st.m[rt] + __log2f(L) : -INFINITY;
+        }
+    }
+}
+
+// FP8 split-KV kernel.  The 4 waves form NG = 4/NR key groups x NR row
+// groups: a wave holds RTW row tiles (row group rg) and takes every NG-th step
+// (page pair) of the piece (key group kg).  Each wave copies its steps straight
+// from HBM into its own 2-stage LDS ring, one step ahead of the compute, so
+// 16-32 KiB per wave stay in flight.  With NR = 2 the two waves of a key
+// group fetch the same pages (the second fetch is served by L2).
+template <int RTW, int NR>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void va_split_kv_fp8_kernel(SplitParams p)
+{
+    constexpr int NG = kWaves / NR;
+    constexpr int RT = RTW * NR;                             // row tiles per piece
+    constexpr int kQBytes = 4 * 8 * 64 * 16;                 // Q operands, up to 4 row tiles
+    constexpr int kRingBytes = 2 * kStageBytes;              // per wave
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kQBytes + kWaves * kRingBytes];
+    uint4 *qs = reinterpret_cast<uint4 *>(lds);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const int rg = wave % NR;
+    const int kg = wave / NR;
+    const int w = blockIdx.x;
+    const int G = 1 << p.log2g;
+
+    Share sh = locate(p, w, lane, w == 0 && wave == 0);
+    sh.n_eff = uniform(sh.n_eff);
+    sh.s = uniform(sh.s);
+    sh.e = uniform(sh.e);
+    sh.bg = uniform(sh.bg);
+    sh.base = uniform(sh.base);
+    if (w >= sh.n_eff)
+        return;                                        // uniform over the workgroup
+
+    const float kd = p.kdesc ? p.kdesc[0] : 1.0f;
+    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
+    const float c = p.scale_log2 * kd;
+    unsigned char *ring = lds + kQBytes + wave * kRingBytes;
+    const uint32_t ring_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(ring));
+    const uint4 *qs_wave = qs + rg * RTW * 8 * 64;
+    uint32_t off[4];
+    dma_lane_offsets(off, p.hkv, lane);
+    const int64_t page_bytes = (int64_t)kPage * p.hkv * kHeadDim;
+
+    const int bh = p.num_seqs * p.hkv;
+    int s = sh.s, bg = sh.bg, base = sh.base;
+    while (s < sh.e && bg < bh) {
+        const int cnt = uniform(pages_of(p.cu, p.seqused, p.hkv, p.mbps, bg));
+        if (cnt == 0) {
+            ++bg;
+            continue;
+        }
+        const int b = uniform(bg / p.hkv);
+        const int g = bg - b * p.hkv;
+        const int q0 = uniform(p.cu[b]);
+        const int lq = uniform(p.cu[b + 1]) - q0;
+        const int lk = uniform(p.seqused[b]);
+        const int ctx = lk - lq;
+        const int p0 = s - base;
+        const int p1 = min(sh.e, base + cnt) - base;
+        const bool whole = (p0 == 0 && p1 == cnt);
+        const int slot = w + bg;
+
+        // ---- packed Q rows of this piece in LDS, in operand order
+        __syncthreads();                                // previous piece's merge reads done
+        for (int u = threadIdx.x; u < RT * 512; u += kThreads) {
+            const int rt = u >> 9, ss = (u >> 6) & 7, l = u & 63;
+            const int row = rt * 16 + (l & 15), jj = l >> 4;
+            const int dim = (4 * (ss >> 1) + jj) * 16 + 8 * (ss & 1);
+            const int t = row >> p.log2g, h = row & (G - 1);
+            uint4 val = make_uint4(0, 0, 0, 0);
+            if (t < lq)
+                val = *(const uint4 *)(p.q + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + dim);
+            qs[u] = val;
+        }
+        __syncthreads();
+
+        RowState<RTW> st;
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            st.m[rt] = -INFINITY;
+            st.l[rt] = 0.f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        int limit[RTW];
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            const int t = ((rg * RTW + rt) * 16 + (lane & 15)) >> p.log2g;
+            limit[rt] = min(ctx + t, lk - 1);
+        }
+
+        const int npairs = (p1 - p0 + 1) >> 1;
+        const bool rows_live = (rg * RTW * 16) < lq * G;
+        if (rows_live && kg < npairs) {
+            const int32_t *btrow = p.bt + (int64_t)b * p.mbps;
+            const uint8_t *kb = p.k + (int64_t)g * kHeadDim;
+            const uint8_t *vb = p.v + (int64_t)g * kHeadDim;
+            const int64_t maxpage = p.num_blocks - 1;
+            auto phys = [&](int page) -> int64_t {
+                int64_t v = uniform(btrow[page]);
+                v = v < 0 ? 0 : v;
+                return v > maxpage ? maxpage : v;
+            };
+            auto issue = [&](int k, int stage) {
+                const int pa = p0 + 2 * k;
+                const int64_t ya = phys(pa);
+                const int64_t yb = pa + 1 < p1 ? phys(pa + 1) : ya;
+                dma_step(ring_addr + stage * kStageBytes, kb, vb, ya, yb, page_bytes, off);
+            };
+            issue(kg, 0);
+            if (kg + NG < npairs)
+                issue(kg + NG, 1);
+            int t = 0;
+            for (int k = kg; k < npairs; k += NG, ++t) {
+                if (k + NG < npairs)                           // next step already in flight
+                    wait_vmcnt<kDmaPerStep>();
+                else
+                    wait_vmcnt<0>();
+                const unsigned char *stage = ring + (t & 1) * kStageBytes;
+                floatx4_t S[2][RTW];
+                qk_lds<RTW>(S, stage, qs_wave, lane);
+                StepRegs<kKvFp8> r;
+                v_from_lds(r, stage, lane);
+                const int pa = p0 + 2 * k;
+                const bool hb = pa + 1 < p1;
+                const int key0 = pa * kPage;
+                softmax_pv_step<RTW, kKvFp8>(st, r, S, limit, key0, hb, lk, c, lane,
+                                             !hb || key0 + 31 > ctx);
+                if (k + 2 * NG < npairs) {
+                    wait_lgkmcnt0();                           // this stage's reads are done
+                    issue(k + 2 * NG, t & 1);
+                }
+            }
+        }
+
+        merge_and_write<RTW, NR>(st, lds, p, kg, rg, lane, lq, q0, g, slot, whole, vd);
+
+        s = base + p1;
+        base += cnt;
+        ++bg;
+    }
+}
+
 // Segment reduce.  One workgroup = 4 consecutive heads of one query token;
 // 64 threads per row, 4 dims each.
 __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
@@ -818,21 +1196,26 @@ void launch_split(SplitParams p, int grid, hipStream_t s)
 
 typedef void (*launch_fn)(SplitParams, int, hipStream_t);
 
+template <int RTW, int NR>
+void launch_fp8(SplitParams p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((va_split_kv_fp8_kernel<RTW, NR>), dim3(grid), dim3(kThreads), 0, s, p);
+}
+
 struct Variant {
-    int rtw, nr;
+    int rtw, nr;        // bf16 kernel: row tiles per wave, row groups
     launch_fn fp8, bf16;
 };
 
-// Row tiles needed -> (row tiles per wave, row groups).  Three or four row
-// tiles use two row groups of two, so a wave's O^T accumulators stay at 128
-// registers (three row tiles per wave do not fit the register file without
-// spilling).
+// Row tiles needed -> kernels.  Three or four row tiles use two row groups of
+// two, so a wave's O^T accumulators stay at 128 registers (three or four row
+// tiles in one wave do not fit the register file without spilling).
 const Variant kVariants[5] = {
     {1, 1, nullptr, nullptr},
-    {1, 1, launch_split<1, 1, kKvFp8>, launch_split<1, 1, kKvBf16>},
-    {2, 1, launch_split<2, 1, kKvFp8>, launch_split<2, 1, kKvBf16>},
-    {2, 2, launch_split<2, 2, kKvFp8>, launch_split<2, 2, kKvBf16>},
-    {2, 2, launch_split<2, 2, kKvFp8>, launch_split<2, 2, kKvBf16>},
+    {1, 1, launch_fp8<1, 1>, launch_split<1, 1, kKvBf16>},
+    {2, 1, launch_fp8<2, 1>, launch_split<2, 1, kKvBf16>},
+    {2, 2, launch_fp8<2, 2>, launch_split<2, 2, kKvBf16>},
+    {2, 2, launch_fp8<2, 2>, launch_split<2, 2, kKvBf16>},
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
