@@ -155,6 +155,15 @@ __device__ __forceinline__ int uniform(int x)
     return __builtin_amdgcn_readfirstlane(x);
 }
 
+// Load of a read-only int32 at a wave-uniform address through the constant
+// address space, so it becomes a scalar load (it then waits on lgkmcnt, never
+// on the vmcnt that tracks the LDS ring's copies).
+__device__ __forceinline__ int load_uniform(const int32_t *base, int64_t idx)
+{
+    typedef const __attribute__((address_space(4))) int32_t cint32;
+    return ((cint32 *)base)[idx];
+}
+
 // Pages of (sequence, kv head) bg that hold keys for at least one query row.
 // Clamped to the block-table row so a bad length cannot index past it.
 __device__ __forceinline__ int pages_of(const int32_t *cu, const int32_t *seqused, int hkv,
@@ -307,23 +316,24 @@ __device__ __forceinline__ void qk_step(floatx4_t (&S)[2][RTW], const StepRegs<K
     }
 }
 
-// Softmax + PV half of a 32-key step: masked online softmax on S^T, then
-// O^T += V^T P^T.
+// Softmax part of a 32-key step: masked online softmax on S^T; returns the P^T
+// B-operands (bf16) of this wave's row tiles.
 //   masked  this step holds keys some row may not see (the causal tail, keys
 //           at or past seqused_k, or a missing second page); uniform
 //   limit   per row tile: the last key index row (lane%16) may see
 //   key0    index of key 0 of page a; has_b: page b is part of this piece
-//   key_end first key index past the sequence (seqused_k)
-template <int RTW, int KVT>
-__device__ __forceinline__ void softmax_pv_step(RowState<RTW> &st, StepRegs<KVT> &r,
-                                                const floatx4_t (&S)[2][RTW], const int (&limit)[RTW],
-                                                int key0, bool has_b, int key_end, float c,
-                                                int lane, bool masked)
+template <int RTW>
+__device__ __forceinline__ void softmax_step(RowState<RTW> &st, bf16x8_t (&pop)[RTW],
+                                             const floatx4_t (&S)[2][RTW], const int (&limit)[RTW],
+                                             int key0, bool has_b, float c, int lane, bool masked)
 {
     const int j = lane >> 4;
-    // logits in log2 units, masked by select (NaN garbage in masked slots is dropped)
+    // Logits in log2 units, masked by select (NaN garbage in masked slots is
+    // dropped).  The running max m of a row only moves when a logit exceeds it
+    // by more than kTau, so in the common case each lane only compares its own
+    // logits with m + kTau and one wave-wide vote decides; the cross-lane row
+    // max and the rescale of O and l run only when the vote says so.
     float x[RTW][8];
-    float mx[RTW];
     bool need_any = false;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
@@ -339,29 +349,29 @@ __device__ __forceinline__ void softmax_pv_step(RowState<RTW> &st, StepRegs<KVT>
                 }
                 x[rt][4 * a + e] = v;
             }
-        float t = x[rt][0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i)
-            t = fmaxf(t, x[rt][i]);
-        t = fmaxf(t, __shfl_xor(t, 16));
-        t = fmaxf(t, __shfl_xor(t, 32));
-        mx[rt] = t;
-        need_any |= t > st.m[rt] + kTau;
+        const float lmax = fmaxf(fmaxf(fmaxf(x[rt][0], x[rt][1]), fmaxf(x[rt][2], x[rt][3])),
+                                 fmaxf(fmaxf(x[rt][4], x[rt][5]), fmaxf(x[rt][6], x[rt][7])));
+        need_any |= lmax > st.m[rt] + kTau;
     }
     if (__any(need_any)) {
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt) {
-            const bool need = mx[rt] > st.m[rt] + kTau;
-            const float alpha = need ? exp2_fast(st.m[rt] - mx[rt]) : 1.0f;
-            st.m[rt] = need ? mx[rt] : st.m[rt];
+            float t = x[rt][0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i)
+                t = fmaxf(t, x[rt][i]);
+            t = fmaxf(t, __shfl_xor(t, 16));
+            t = fmaxf(t, __shfl_xor(t, 32));            // row max of this step
+            const bool need = t > st.m[rt] + kTau;
+            const float alpha = need ? exp2_fast(st.m[rt] - t) : 1.0f;
+            st.m[rt] = need ? t : st.m[rt];
             st.l[rt] *= alpha;
 #pragma unroll
-            for (int t = 0; t < 16; ++t)
-                st.o[t][rt] *= alpha;
+            for (int tt = 0; tt < 16; ++tt)
+                st.o[tt][rt] *= alpha;
         }
     }
 
-    bf16x8_t pop[RTW];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
         const float mref = st.m[rt] == -INFINITY ? 0.0f : st.m[rt];
@@ -380,22 +390,38 @@ __device__ __forceinline__ void softmax_pv_step(RowState<RTW> &st, StepRegs<KVT>
         w.w = pack_bf16x2(p[6], p[7]);
         pop[rt] = __builtin_bit_cast(bf16x8_t, w);
     }
+}
 
-    if (masked) {
-        // keys at or past seqused_k may hold NaN bytes, and page b of a short
-        // piece holds no key of it: zero their V rows so 0 * NaN cannot reach O.
+// Keys of a step whose V rows must be zeroed before PV: at or past seqused_k
+// (they may hold NaN bytes), or in page b when page b is not part of the
+// piece.  Bit e = key (page e/4, slot 4j + e%4) of this lane.
+__device__ __forceinline__ uint32_t v_zero_mask(int key0, bool has_b, int key_end, int lane)
+{
+    const int j = lane >> 4;
+    uint32_t z = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int key = key0 + 16 * (e >> 2) + 4 * j + (e & 3);
-            if (key >= key_end || (e >= 4 && !has_b)) {
+    for (int e = 0; e < 8; ++e) {
+        const int key = key0 + 16 * (e >> 2) + 4 * j + (e & 3);
+        if (key >= key_end || (e >= 4 && !has_b))
+            z |= 1u << e;
+    }
+    return z;
+}
+
+// PV from V rows in registers (v[e] = dims 16m .. 16m+15 of key slot 4j + e%4
+// of page e/4): O^T += V^T P^T.  V^T operand of dim tile t = dims {16m + t}.
+template <int RTW, int KVT>
+__device__ __forceinline__ void pv_regs(RowState<RTW> &st, StepRegs<KVT> &r, const bf16x8_t (&pop)[RTW],
+                                        uint32_t zmask)
+{
+    if (zmask) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (zmask & (1u << e))
 #pragma unroll
                 for (int cc = 0; cc < StepRegs<KVT>::kV; ++cc)
                     r.v[e][cc] = make_uint4(0, 0, 0, 0);
-            }
-        }
     }
-
-    // PV: V^T operand of dim tile t = dims {16m + t}, 8 keys per lane.
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         uint32_t A[4][4];      // [x][kp]: tile 4q+x, key pair kp
@@ -434,6 +460,51 @@ __device__ __forceinline__ void softmax_pv_step(RowState<RTW> &st, StepRegs<KVT>
                 st.o[4 * q + xx][rt] = mfma16(vop, pop[rt], st.o[4 * q + xx][rt]);
         }
         __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// PV with FP8 V rows read from a ring stage, 8 bytes (dims 8h .. 8h+7 of the
+// lane's 16) of each of the 8 keys at a time, so only 16 registers of raw V
+// are live.  Same operand order as pv_regs.
+template <int RTW>
+__device__ __forceinline__ void pv_lds(RowState<RTW> &st, const unsigned char *stage,
+                                       const bf16x8_t (&pop)[RTW], uint32_t zmask, int lane)
+{
+    const int m = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint2 vv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int n = 4 * j + (e & 3);
+            vv[e] = *reinterpret_cast<const uint2 *>(stage + 8192 + 4096 * (e >> 2) + 256 * n +
+                                                     16 * (m ^ n) + 8 * h);
+            if (zmask & (1u << e))
+                vv[e] = make_uint2(0, 0);
+        }
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            const int q = 2 * h + qq;
+            uint32_t A[4][4];
+#pragma unroll
+            for (int kp = 0; kp < 4; ++kp) {
+                const uint32_t X = qq ? vv[2 * kp].y : vv[2 * kp].x;
+                const uint32_t Y = qq ? vv[2 * kp + 1].y : vv[2 * kp + 1].x;
+                const uint32_t lo = byte_perm(Y, X, 0x05010400u);   // X0 Y0 X1 Y1
+                const uint32_t hi = byte_perm(Y, X, 0x07030602u);   // X2 Y2 X3 Y3
+                A[0][kp] = fp8x2_lo_to_bf16x2(lo);
+                A[1][kp] = fp8x2_hi_to_bf16x2(lo);
+                A[2][kp] = fp8x2_lo_to_bf16x2(hi);
+                A[3][kp] = fp8x2_hi_to_bf16x2(hi);
+            }
+#pragma unroll
+            for (int xx = 0; xx < 4; ++xx) {
+                const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, make_uint4(A[xx][0], A[xx][1], A[xx][2], A[xx][3]));
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt)
+                    st.o[4 * q + xx][rt] = mfma16(vop, pop[rt], st.o[4 * q + xx][rt]);
+            }
+        }
     }
 }
 
@@ -616,8 +687,10 @@ void va_split_kv_kernel(SplitParams p)
                     load_k<KVT>(r, kbase, yna, ynb, hn, p.hkv, lane);
                 }
                 const int key0 = pa * kPage;
-                softmax_pv_step<RTW, KVT>(st, r, S, limit, key0, hb, lk, c, lane,
-                                          !hb || key0 + 31 > ctx);
+                const bool masked = !hb || key0 + 31 > ctx;
+                bf16x8_t pop[RTW];
+                softmax_step<RTW>(st, pop, S, limit, key0, hb, c, lane, masked);
+                pv_regs<RTW, KVT>(st, r, pop, masked ? v_zero_mask(key0, hb, lk, lane) : 0u);
                 if (!more)
                     break;
                 load_v<KVT>(r, vbase, yna, ynb, hn, p.hkv, lane);
@@ -806,6 +879,22 @@ __device__ __forceinline__ void dma_step(uint32_t stage, const uint8_t *kb, cons
         dma16(vbb, off[i], stage + 12288 + 1024 * i);
 }
 
+// Half of a step copy: the K pages (part 0) or the V pages (part 1), 8
+// instructions.  Two waves that share a ring stage issue one part each.
+__device__ __forceinline__ void dma_step_part(uint32_t stage, const uint8_t *pool, int part, int64_t ya,
+                                              int64_t yb, int64_t page_bytes, const uint32_t (&off)[4])
+{
+    const uint8_t *a = pool + ya * page_bytes;
+    const uint8_t *b = pool + yb * page_bytes;
+    const uint32_t base = stage + 8192 * part;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        dma16(a, off[i], base + 1024 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        dma16(b, off[i], base + 4096 + 1024 * i);
+}
+
 // QK half of a step with K read from a ring stage (same math as qk_step).
 template <int RT>
 __device__ __forceinline__ void qk_lds(floatx4_t (&S)[2][RT], const unsigned char *stage,
@@ -844,33 +933,21 @@ __device__ __forceinline__ void qk_lds(floatx4_t (&S)[2][RT], const unsigned cha
             for (int rt = 0; rt < RT; ++rt)
                 S[a][rt] = mfma16(kop, qop[rt], S[a][rt]);
         }
-        if (s & 1)
-            __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// V rows of a step from a ring stage into the register order softmax_pv_step
-// expects: v[e] = dims 16m .. 16m+15 of key slot 4j + e%4 of page e/4.
-__device__ __forceinline__ void v_from_lds(StepRegs<kKvFp8> &r, const unsigned char *stage, int lane)
-{
-    const int m = lane & 15, j = lane >> 4;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int n = 4 * j + (e & 3);
-        r.v[e][0] = *reinterpret_cast<const uint4 *>(stage + 8192 + 4096 * (e >> 2) + 256 * n + 16 * (m ^ n));
     }
 }
 
 // Merge the softmax states of the NG key groups of each row group through
-// LDS.  The key-group-0 wave of each row group then writes its rows: final
-// rows when the piece is the whole sequence, else the piece's partial.
-template <int RTW, int NR>
+// LDS, as a binary tree (key group kg absorbs kg + d for d = 1, 2, ...), one
+// row tile at a time with a barrier between rounds, so a wave holds at most
+// one incoming row tile (64 floats per lane) at a time.  The key-group-0 wave
+// of each row group then writes its rows: final rows when the piece is the
+// whole sequence, else the piece's partial.
+template <int RTW, int NR, int NG>
 __device__ __forceinline__ void merge_and_write(RowState<RTW> &st, unsigned char *lds, const SplitParams &p,
                                                 int kg, int rg, int lane, int lq, int q0, int g,
                                                 int slot, bool whole, float vd)
 {
-    constexpr int NG = kWaves / NR;
-    constexpr int kMergeFloats = 64 * 64 + 2 * 64;        // one row tile of one wave: O^T, m, l
+    constexpr int kSlotFloats = 64 * 64 + 2 * 64;         // one row tile of one wave: O^T, m, l
     const int G = 1 << p.log2g;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
@@ -879,45 +956,39 @@ __device__ __forceinline__ void merge_and_write(RowState<RTW> &st, unsigned char
         t += __shfl_xor(t, 32);
         st.l[rt] = t;
     }
-    float *buf = reinterpret_cast<float *>(lds) + (size_t)rg * (NG - 1) * kMergeFloats;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-        __syncthreads();
-        if (kg > 0) {
-            float *mine = buf + (size_t)(kg - 1) * kMergeFloats;
 #pragma unroll
-            for (int t = 0; t < 16; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    mine[(t * 4 + e) * 64 + lane] = st.o[t][rt][e];
-            mine[64 * 64 + lane] = st.m[rt];
-            mine[64 * 64 + 64 + lane] = st.l[rt];
-        }
-        __syncthreads();
-        if (kg == 0) {
-            float mm = st.m[rt];
-#pragma unroll
-            for (int o = 1; o < NG; ++o)
-                mm = fmaxf(mm, buf[(size_t)(o - 1) * kMergeFloats + 64 * 64 + lane]);
-            const float f0 = st.m[rt] == -INFINITY ? 0.f : exp2_fast(st.m[rt] - mm);
-            float L = f0 * st.l[rt];
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-                st.o[t][rt] *= f0;
-#pragma unroll
-            for (int o = 1; o < NG; ++o) {
-                const float *oth = buf + (size_t)(o - 1) * kMergeFloats;
-                const float mo = oth[64 * 64 + lane];
-                const float fo = mo == -INFINITY ? 0.f : exp2_fast(mo - mm);
-                L += fo * oth[64 * 64 + 64 + lane];
+        for (int d = 1; d < NG; d <<= 1) {
+            float *buf = reinterpret_cast<float *>(lds) + (size_t)(rg * (NG / 2) + kg / (2 * d)) * kSlotFloats;
+            __syncthreads();
+            if (kg % (2 * d) == d) {
+                float4 *o4 = reinterpret_cast<float4 *>(buf);
 #pragma unroll
                 for (int t = 0; t < 16; ++t)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        st.o[t][rt][e] += fo * oth[(t * 4 + e) * 64 + lane];
+                    o4[t * 64 + lane] = make_float4(st.o[t][rt][0], st.o[t][rt][1], st.o[t][rt][2], st.o[t][rt][3]);
+                buf[64 * 64 + lane] = st.m[rt];
+                buf[64 * 64 + 64 + lane] = st.l[rt];
             }
-            st.m[rt] = mm;
-            st.l[rt] = L;
+            __syncthreads();
+            if (kg % (2 * d) == 0 && kg + d < NG) {
+                const float4 *o4 = reinterpret_cast<const float4 *>(buf);
+                const float mo = buf[64 * 64 + lane];
+                const float lo = buf[64 * 64 + 64 + lane];
+                const float mm = fmaxf(st.m[rt], mo);
+                const float fa = st.m[rt] == -INFINITY ? 0.f : exp2_fast(st.m[rt] - mm);
+                const float fb = mo == -INFINITY ? 0.f : exp2_fast(mo - mm);
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const float4 v = o4[t * 64 + lane];
+                    st.o[t][rt][0] = fa * st.o[t][rt][0] + fb * v.x;
+                    st.o[t][rt][1] = fa * st.o[t][rt][1] + fb * v.y;
+                    st.o[t][rt][2] = fa * st.o[t][rt][2] + fb * v.z;
+                    st.o[t][rt][3] = fa * st.o[t][rt][3] + fb * v.w;
+                }
+                st.l[rt] = fa * st.l[rt] + fb * lo;
+                st.m[rt] = mm;
+            }
         }
     }
     if (kg != 0)
@@ -1012,16 +1083,16 @@ void va_split_kv_fp8_kernel(SplitParams p)
     const int bh = p.num_seqs * p.hkv;
     int s = sh.s, bg = sh.bg, base = sh.base;
     while (s < sh.e && bg < bh) {
-        const int cnt = uniform(pages_of(p.cu, p.seqused, p.hkv, p.mbps, bg));
+        const int b = uniform(bg / p.hkv);
+        const int g = bg - b * p.hkv;
+        const int q0 = load_uniform(p.cu, b);
+        const int lq = load_uniform(p.cu, b + 1) - q0;
+        const int lk = load_uniform(p.seqused, b);
+        const int cnt = (lq <= 0 || lk <= 0) ? 0 : min((lk + kPage - 1) / kPage, p.mbps);
         if (cnt == 0) {
             ++bg;
             continue;
         }
-        const int b = uniform(bg / p.hkv);
-        const int g = bg - b * p.hkv;
-        const int q0 = uniform(p.cu[b]);
-        const int lq = uniform(p.cu[b + 1]) - q0;
-        const int lk = uniform(p.seqused[b]);
         const int ctx = lk - lq;
         const int p0 = s - base;
         const int p1 = min(sh.e, base + cnt) - base;
@@ -1065,8 +1136,13 @@ void va_split_kv_fp8_kernel(SplitParams p)
             const uint8_t *kb = p.k + (int64_t)g * kHeadDim;
             const uint8_t *vb = p.v + (int64_t)g * kHeadDim;
             const int64_t maxpage = p.num_blocks - 1;
+            // Block-table entries are read with scalar loads (uniform address,
+            // read-only memory, so the constant address space): a vector load
+            // here would need a vmcnt wait that also drains the ring's copies.
+            typedef const __attribute__((address_space(4))) int32_t cint32;
+            cint32 *btc = (cint32 *)btrow;
             auto phys = [&](int page) -> int64_t {
-                int64_t v = uniform(btrow[page]);
+                int64_t v = btc[uniform(page)];
                 v = v < 0 ? 0 : v;
                 return v > maxpage ? maxpage : v;
             };
@@ -1088,13 +1164,13 @@ void va_split_kv_fp8_kernel(SplitParams p)
                 const unsigned char *stage = ring + (t & 1) * kStageBytes;
                 floatx4_t S[2][RTW];
                 qk_lds<RTW>(S, stage, qs_wave, lane);
-                StepRegs<kKvFp8> r;
-                v_from_lds(r, stage, lane);
                 const int pa = p0 + 2 * k;
                 const bool hb = pa + 1 < p1;
                 const int key0 = pa * kPage;
-                softmax_pv_step<RTW, kKvFp8>(st, r, S, limit, key0, hb, lk, c, lane,
-                                             !hb || key0 + 31 > ctx);
+                const bool masked = !hb || key0 + 31 > ctx;
+                bf16x8_t pop[RTW];
+                softmax_step<RTW>(st, pop, S, limit, key0, hb, c, lane, masked);
+                pv_lds<RTW>(st, stage, pop, masked ? v_zero_mask(key0, hb, lk, lane) : 0u, lane);
                 if (k + 2 * NG < npairs) {
                     wait_lgkmcnt0();                           // this stage's reads are done
                     issue(k + 2 * NG, t & 1);
@@ -1102,7 +1178,150 @@ void va_split_kv_fp8_kernel(SplitParams p)
             }
         }
 
-        merge_and_write<RTW, NR>(st, lds, p, kg, rg, lane, lq, q0, g, slot, whole, vd);
+        merge_and_write<RTW, NR, NG>(st, lds, p, kg, rg, lane, lq, q0, g, slot, whole, vd);
+
+        s = base + p1;
+        base += cnt;
+        ++bg;
+    }
+}
+
+// FP8 split-KV kernel, 8 waves (two per SIMD, so one wave's MFMA work runs
+// while the other's vector work issues).  The waves form 4 key groups x 2 row
+// groups: a wave holds RTW row tiles (row group rg) and computes every 4th
+// step (page pair) of the piece (key group kg).  The two waves of a key group
+// share a 2-stage LDS ring: for each step one copies the K pages and the other
+// the V pages, straight from HBM, one step ahead of the compute.  One
+// workgroup barrier per step makes a stage visible to both waves and frees the
+// stage the next copy overwrites.
+template <int RTW>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void va_split_kv_fp8_w8_kernel(SplitParams p)
+{
+    constexpr int NR = 2;
+    constexpr int NG = 4;
+    constexpr int RT = RTW * NR;                             // row tiles per piece
+    constexpr int kQBytes = 4 * 8 * 64 * 16;                 // Q operands, up to 4 row tiles
+    constexpr int kRingBytes = 2 * kStageBytes;              // per key group
+    constexpr int kThreadsW8 = 512;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kQBytes + NG * kRingBytes];
+    uint4 *qs = reinterpret_cast<uint4 *>(lds);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const int rg = wave & 1;
+    const int kg = wave >> 1;
+    const int w = blockIdx.x;
+    const int G = 1 << p.log2g;
+
+    Share sh = locate(p, w, lane, w == 0 && wave == 0);
+    sh.n_eff = uniform(sh.n_eff);
+    sh.s = uniform(sh.s);
+    sh.e = uniform(sh.e);
+    sh.bg = uniform(sh.bg);
+    sh.base = uniform(sh.base);
+    if (w >= sh.n_eff)
+        return;                                        // uniform over the workgroup
+
+    const float kd = p.kdesc ? p.kdesc[0] : 1.0f;
+    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
+    const float c = p.scale_log2 * kd;
+    unsigned char *ring = lds + kQBytes + kg * kRingBytes;
+    const uint32_t ring_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(ring));
+    const uint4 *qs_wave = qs + rg * RTW * 8 * 64;
+    uint32_t off[4];
+    dma_lane_offsets(off, p.hkv, lane);
+    const int64_t page_bytes = (int64_t)kPage * p.hkv * kHeadDim;
+
+    const int bh = p.num_seqs * p.hkv;
+    int s = sh.s, bg = sh.bg, base = sh.base;
+    while (s < sh.e && bg < bh) {
+        const int b = uniform(bg / p.hkv);
+        const int g = bg - b * p.hkv;
+        const int q0 = load_uniform(p.cu, b);
+        const int lq = load_uniform(p.cu, b + 1) - q0;
+        const int lk = load_uniform(p.seqused, b);
+        const int cnt = (lq <= 0 || lk <= 0) ? 0 : min((lk + kPage - 1) / kPage, p.mbps);
+        if (cnt == 0) {
+            ++bg;
+            continue;
+        }
+        const int ctx = lk - lq;
+        const int p0 = s - base;
+        const int p1 = min(sh.e, base + cnt) - base;
+        const bool whole = (p0 == 0 && p1 == cnt);
+        const int slot = w + bg;
+
+        // ---- packed Q rows of this piece in LDS, in operand order
+        __syncthreads();                                // previous piece's merge reads done
+        for (int u = threadIdx.x; u < RT * 512; u += kThreadsW8) {
+            const int rt = u >> 9, ss = (u >> 6) & 7, l = u & 63;
+            const int row = rt * 16 + (l & 15), jj = l >> 4;
+            const int dim = (4 * (ss >> 1) + jj) * 16 + 8 * (ss & 1);
+            const int t = row >> p.log2g, h = row & (G - 1);
+            uint4 val = make_uint4(0, 0, 0, 0);
+            if (t < lq)
+                val = *(const uint4 *)(p.q + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + dim);
+            qs[u] = val;
+        }
+
+        RowState<RTW> st;
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            st.m[rt] = -INFINITY;
+            st.l[rt] = 0.f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        int limit[RTW];
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            const int t = ((rg * RTW + rt) * 16 + (lane & 15)) >> p.log2g;
+            limit[rt] = min(ctx + t, lk - 1);
+        }
+
+        const int npairs = (p1 - p0 + 1) >> 1;
+        const int nsteps = (npairs + NG - 1) / NG;             // uniform over the workgroup
+        const bool rows_live = (rg * RTW * 16) < lq * G;
+        const int32_t *btrow = p.bt + (int64_t)b * p.mbps;
+        const uint8_t *pool = (rg == 0 ? p.k : p.v) + (int64_t)g * kHeadDim;
+        const int64_t maxpage = p.num_blocks - 1;
+        auto phys = [&](int page) -> int64_t {
+            int64_t v = load_uniform(btrow, uniform(page));
+            v = v < 0 ? 0 : v;
+            return v > maxpage ? maxpage : v;
+        };
+        auto issue = [&](int k, int stage) {                   // this wave's half of step k
+            const int pa = p0 + 2 * k;
+            const int64_t ya = phys(pa);
+            const int64_t yb = pa + 1 < p1 ? phys(pa + 1) : ya;
+            dma_step_part(ring_addr + stage * kStageBytes, pool, rg, ya, yb, page_bytes, off);
+        };
+        if (kg < npairs)
+            issue(kg, 0);
+        for (int t = 0; t < nsteps; ++t) {
+            const int k = kg + t * NG;
+            wait_vmcnt<0>();                                   // own copies of step t landed
+            __syncthreads();                                   // partner's too; stage t+1 is free
+            if (k + NG < npairs)
+                issue(k + NG, (t + 1) & 1);
+            if (k < npairs && rows_live) {
+                const unsigned char *stage = ring + (t & 1) * kStageBytes;
+                floatx4_t S[2][RTW];
+                qk_lds<RTW>(S, stage, qs_wave, lane);
+                const int pa = p0 + 2 * k;
+                const bool hb = pa + 1 < p1;
+                const int key0 = pa * kPage;
+                const bool masked = !hb || key0 + 31 > ctx;
+                bf16x8_t pop[RTW];
+                softmax_step<RTW>(st, pop, S, limit, key0, hb, c, lane, masked);
+                pv_lds<RTW>(st, stage, pop, masked ? v_zero_mask(key0, hb, lk, lane) : 0u, lane);
+            }
+        }
+        wait_vmcnt<0>();
+
+        merge_and_write<RTW, NR, NG>(st, lds, p, kg, rg, lane, lq, q0, g, slot, whole, vd);
 
         s = base + p1;
         base += cnt;
@@ -1111,9 +1330,11 @@ void va_split_kv_fp8_kernel(SplitParams p)
 }
 
 // Segment reduce.  One workgroup = 4 consecutive heads of one query token;
-// 64 threads per row, 4 dims each.
+// 64 threads per row, 4 dims each.  The partials of a row are read in chunks of
+// 8 slots with all loads of a chunk issued before any is used.
 __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
 {
+    constexpr int kChunk = 8;
     const int gq = (1 << p.log2g) >> 2;               // head quads per group
     int idx = blockIdx.x;
     const int hq4 = idx % gq;
@@ -1122,17 +1343,17 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
     const int bg = idx / p.max_q;
     const int b = bg / p.hkv;
     const int g = bg - b * p.hkv;
-    const int q0 = p.cu[b];
-    const int lq = p.cu[b + 1] - q0;
+    const int q0 = load_uniform(p.cu, b);
+    const int lq = load_uniform(p.cu, b + 1) - q0;
     if (t >= lq)
         return;
     const int bh = p.num_seqs * p.hkv;
-    const int s = p.ws_prefix[bg];
-    const int e = p.ws_prefix[bg + 1];
-    const int total = p.ws_prefix[bh];
+    const int s = load_uniform(p.ws_prefix, bg);
+    const int e = load_uniform(p.ws_prefix, bg + 1);
+    const int total = load_uniform(p.ws_prefix, bh);
     if (e <= s || total <= 0)
         return;
-    const int64_t n = p.ws_meta[0];
+    const int64_t n = load_uniform(p.ws_meta, 0);
     const int w0 = (int)(((int64_t)(s + 1) * n - 1) / total);
     const int w1 = (int)(((int64_t)e * n - 1) / total);
     if (w0 == w1)
@@ -1140,23 +1361,44 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
     const int h = hq4 * 4 + (threadIdx.x >> 6);
     const int row = (t << p.log2g) + h;
     const int d = (threadIdx.x & 63) * 4;
+    const float *lse = p.ws_lse + (int64_t)(w0 + bg) * p.rows_max + row;
+    const float *o = p.ws_o + ((int64_t)(w0 + bg) * p.rows_max + row) * kHeadDim + d;
+    const int64_t lstride = p.rows_max;
+    const int64_t ostride = (int64_t)p.rows_max * kHeadDim;
+    const int ns = w1 - w0 + 1;
 
     float mx = -INFINITY;
-    for (int w = w0; w <= w1; ++w)
-        mx = fmaxf(mx, p.ws_lse[(int64_t)(w + bg) * p.rows_max + row]);
+    for (int c0 = 0; c0 < ns; c0 += kChunk) {
+        float l[kChunk];
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i)
+            l[i] = c0 + i < ns ? lse[(c0 + i) * lstride] : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i)
+            mx = fmaxf(mx, l[i]);
+    }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float den = 0.f;
     if (mx > -INFINITY) {
-        for (int w = w0; w <= w1; ++w) {
-            const int64_t sl = (int64_t)(w + bg) * p.rows_max + row;
-            const float l = p.ws_lse[sl];
-            const float f = l == -INFINITY ? 0.f : exp2_fast(l - mx);
-            const float4 o = *reinterpret_cast<const float4 *>(p.ws_o + sl * kHeadDim + d);
-            den += f;
-            acc.x += f * o.x;
-            acc.y += f * o.y;
-            acc.z += f * o.z;
-            acc.w += f * o.w;
+        for (int c0 = 0; c0 < ns; c0 += kChunk) {
+            float l[kChunk];
+            float4 v[kChunk];
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                const bool in = c0 + i < ns;
+                l[i] = in ? lse[(c0 + i) * lstride] : -INFINITY;
+                v[i] = in ? *reinterpret_cast<const float4 *>(o + (c0 + i) * ostride)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                const float f = l[i] == -INFINITY ? 0.f : exp2_fast(l[i] - mx);
+                den += f;
+                acc.x += f * v[i].x;
+                acc.y += f * v[i].y;
+                acc.z += f * v[i].z;
+                acc.w += f * v[i].w;
+            }
         }
     }
     const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
@@ -1202,6 +1444,12 @@ void launch_fp8(SplitParams p, int grid, hipStream_t s)
     hipLaunchKernelGGL((va_split_kv_fp8_kernel<RTW, NR>), dim3(grid), dim3(kThreads), 0, s, p);
 }
 
+template <int RTW>
+void launch_fp8_w8(SplitParams p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((va_split_kv_fp8_w8_kernel<RTW>), dim3(grid), dim3(512), 0, s, p);
+}
+
 struct Variant {
     int rtw, nr;        // bf16 kernel: row tiles per wave, row groups
     launch_fn fp8, bf16;
@@ -1212,10 +1460,10 @@ struct Variant {
 // tiles in one wave do not fit the register file without spilling).
 const Variant kVariants[5] = {
     {1, 1, nullptr, nullptr},
-    {1, 1, launch_fp8<1, 1>, launch_split<1, 1, kKvBf16>},
-    {2, 1, launch_fp8<2, 1>, launch_split<2, 1, kKvBf16>},
-    {2, 2, launch_fp8<2, 2>, launch_split<2, 2, kKvBf16>},
-    {2, 2, launch_fp8<2, 2>, launch_split<2, 2, kKvBf16>},
+    {1, 1, launch_fp8_w8<1>, launch_split<1, 1, kKvBf16>},
+    {2, 1, launch_fp8_w8<1>, launch_split<2, 1, kKvBf16>},
+    {2, 2, launch_fp8_w8<2>, launch_split<2, 2, kKvBf16>},
+    {2, 2, launch_fp8_w8<2>, launch_split<2, 2, kKvBf16>},
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1302,7 +1550,8 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     pl->log2g = G == 4 ? 2 : G == 8 ? 3 : 4;
     const int rows = G * p.max_seqlen_q;
     pl->rt = (rows + 15) / 16;
-    pl->rows_max = 16 * kVariants[pl->rt].rtw * kVariants[pl->rt].nr;
+    pl->rows_max = p.kv_dtype == VA_DT_FP8_E4M3FN ? 16 * 2 * (pl->rt <= 2 ? 1 : 2)
+                                                 : 16 * kVariants[pl->rt].rtw * kVariants[pl->rt].nr;
     pl->grid = p.force_grid > 0 ? p.force_grid : cus;
     pl->min_pages = 8;
     pl->slots = (int64_t)pl->grid + bh;
