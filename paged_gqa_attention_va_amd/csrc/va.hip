@@ -50,6 +50,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef int intx8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kHeadDim = 256;
 constexpr int kPage = 16;
@@ -124,6 +125,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 __device__ __forceinline__ floatx4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, const floatx4_t &c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x128 MFMA with fp8 e4m3 A and B (format code 0 for both), unit
+// block scales (E8M0 127 = 2^0).  Lane l holds 32 k-values of row/column l%16.
+__device__ __forceinline__ floatx4_t mfma16_f8(const intx8_t &a, const intx8_t &b, const floatx4_t &c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 __device__ __forceinline__ int wave_sum(int x)
@@ -316,16 +324,19 @@ __device__ __forceinline__ void qk_step(floatx4_t (&S)[2][RTW], const StepRegs<K
     }
 }
 
-// Softmax part of a 32-key step: masked online softmax on S^T; returns the P^T
+// Softmax part of a 32-key step: online softmax on S^T; returns the P^T
 // B-operands (bf16) of this wave's row tiles.
 //   masked  this step holds keys some row may not see (the causal tail, keys
 //           at or past seqused_k, or a missing second page); uniform
 //   limit   per row tile: the last key index row (lane%16) may see
 //   key0    index of key 0 of page a; has_b: page b is part of this piece
+//   c       per row tile: logit multiplier (softmax_scale * k_descale * log2 e,
+//           times the row's Q scale where Q was rescaled)
 template <int RTW>
 __device__ __forceinline__ void softmax_step(RowState<RTW> &st, bf16x8_t (&pop)[RTW],
                                              const floatx4_t (&S)[2][RTW], const int (&limit)[RTW],
-                                             int key0, bool has_b, float c, int lane, bool masked)
+                                             int key0, bool has_b, const float (&c)[RTW], int lane,
+                                             bool masked)
 {
     const int j = lane >> 4;
     // Logits in log2 units, masked by select (NaN garbage in masked slots is
@@ -341,7 +352,7 @@ __device__ __forceinline__ void softmax_step(RowState<RTW> &st, bf16x8_t (&pop)[
         for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float v = S[a][rt][e] * c;
+                float v = S[a][rt][e] * c[rt];
                 if (masked) {
                     const int key = key0 + 16 * a + 4 * j + e;
                     const bool ok = (a == 0 || has_b) && key <= limit[rt];
@@ -468,7 +479,7 @@ __device__ __forceinline__ void pv_regs(RowState<RTW> &st, StepRegs<KVT> &r, con
 // are live.  Same operand order as pv_regs.
 template <int RTW>
 __device__ __forceinline__ void pv_lds(RowState<RTW> &st, const unsigned char *stage,
-                                       const bf16x8_t (&pop)[RTW], uint32_t zmask, int lane)
+                                       const bf16x8_t (&pop)[RTW], bool masked, uint32_t zmask, int lane)
 {
     const int m = lane & 15, j = lane >> 4;
 #pragma unroll
@@ -479,8 +490,12 @@ __device__ __forceinline__ void pv_lds(RowState<RTW> &st, const unsigned char *s
             const int n = 4 * j + (e & 3);
             vv[e] = *reinterpret_cast<const uint2 *>(stage + 8192 + 4096 * (e >> 2) + 256 * n +
                                                      16 * (m ^ n) + 8 * h);
-            if (zmask & (1u << e))
-                vv[e] = make_uint2(0, 0);
+        }
+        if (masked) {                                  // wave-uniform
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (zmask & (1u << e))
+                    vv[e] = make_uint2(0, 0);
         }
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
@@ -521,6 +536,33 @@ struct Share {
 __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix)
 {
     const int bh = p.num_seqs * p.hkv;
+    if (bh <= 64) {                                    // one pass: one count per lane
+        const int cnt = lane < bh ? pages_of(p.cu, p.seqused, p.hkv, p.mbps, lane) : 0;
+        const int incl = wave_incl_scan(cnt, lane);
+        const int total = __shfl(incl, 63);
+        Share sh;
+        sh.n_eff = min(p.grid_n, max(1, total / max(1, p.min_pages)));
+        sh.s = (int)(((int64_t)w * total) / sh.n_eff);
+        sh.e = (int)(((int64_t)(w + 1) * total) / sh.n_eff);
+        const unsigned long long hit = __ballot(lane < bh && incl > sh.s);
+        if (hit) {
+            const int ln = __ffsll((long long)hit) - 1;
+            sh.bg = ln;
+            sh.base = __shfl(incl - cnt, ln);
+        } else {
+            sh.bg = bh;
+            sh.base = total;
+        }
+        if (write_prefix) {
+            if (lane < bh)
+                p.ws_prefix[lane] = incl - cnt;
+            if (lane == 0) {
+                p.ws_prefix[bh] = total;
+                p.ws_meta[0] = sh.n_eff;
+            }
+        }
+        return sh;
+    }
     int total = 0;
     for (int c0 = 0; c0 < bh; c0 += 64) {
         const int bg = c0 + lane;
@@ -689,7 +731,13 @@ void va_split_kv_kernel(SplitParams p)
                 const int key0 = pa * kPage;
                 const bool masked = !hb || key0 + 31 > ctx;
                 bf16x8_t pop[RTW];
-                softmax_step<RTW>(st, pop, S, limit, key0, hb, c, lane, masked);
+                {
+                    float cr[RTW];
+#pragma unroll
+                    for (int rt = 0; rt < RTW; ++rt)
+                        cr[rt] = c;
+                    softmax_step<RTW>(st, pop, S, limit, key0, hb, cr, lane, masked);
+                }
                 pv_regs<RTW, KVT>(st, r, pop, masked ? v_zero_mask(key0, hb, lk, lane) : 0u);
                 if (!more)
                     break;
@@ -1169,8 +1217,14 @@ void va_split_kv_fp8_kernel(SplitParams p)
                 const int key0 = pa * kPage;
                 const bool masked = !hb || key0 + 31 > ctx;
                 bf16x8_t pop[RTW];
-                softmax_step<RTW>(st, pop, S, limit, key0, hb, c, lane, masked);
-                pv_lds<RTW>(st, stage, pop, masked ? v_zero_mask(key0, hb, lk, lane) : 0u, lane);
+                {
+                    float cr[RTW];
+#pragma unroll
+                    for (int rt = 0; rt < RTW; ++rt)
+                        cr[rt] = c;
+                    softmax_step<RTW>(st, pop, S, limit, key0, hb, cr, lane, masked);
+                }
+                pv_lds<RTW>(st, stage, pop, masked, masked ? v_zero_mask(key0, hb, lk, lane) : 0u, lane);
                 if (k + 2 * NG < npairs) {
                     wait_lgkmcnt0();                           // this stage's reads are done
                     issue(k + 2 * NG, t & 1);
@@ -1183,6 +1237,148 @@ void va_split_kv_fp8_kernel(SplitParams p)
         s = base + p1;
         base += cnt;
         ++bg;
+    }
+}
+
+// ------------------------------------------- QK on fp8 (Q split hi + lo) --
+//
+// For the FP8 cache the QK^T contraction runs on v_mfma_f32_16x16x128_f8f6f4
+// with K used as stored.  Each packed Q row r (bf16) is scaled by 2^k_r so its
+// largest magnitude lies in [128, 256), then split into
+//   hi = e4m3(q 2^k_r),  lo = e4m3(q 2^k_r - hi)   (round to nearest even).
+// For every element of magnitude >= 2^-2 after scaling (all but those below
+// 1/512 of the row maximum) hi + lo equals the scaled bf16 value exactly: the
+// bits of a bf16 value below the top four fit one more e4m3 value.  Smaller
+// elements are kept to 2^-10 absolute, i.e. 2^-17 of the row scale.  So
+// S = K.hi + K.lo carries the same information as the bf16 product, and the
+// logit multiplier of row r absorbs 2^-k_r.
+//
+// LDS layout of the Q operands: [rt][kc][part][lane] x 32 bytes, where kc
+// selects dims [128 kc, 128 kc + 128), part 0 = hi, 1 = lo, and lane l holds
+// row 16 rt + l%16, dims 128 kc + 32 (l/16) .. +32.
+constexpr int kQf8Bytes = 4 * 2 * 2 * 64 * 32;              // up to 4 row tiles: 32 KiB
+
+// Each wave stages the rows of its own row group in the order its lanes
+// consume them: lane l takes row 16 (rg RTW + rt) + l%16 and dims
+// 128 kc + 32 (l/16) .. +32 for kc = 0, 1.  The four lanes that share a row
+// hold all 256 dims, so two lane exchanges give every lane its row's maximum
+// and exponent k_r, which the lane keeps (the row's logit multiplier is
+// c 2^-k_r).  Only key group 0 writes the operands to LDS; the other key
+// groups of the row group compute the same exponents.
+template <int RTW>
+__device__ __forceinline__ void stage_q_fp8(unsigned char *qlds, float (&crow)[RTW], float c,
+                                            const SplitParams &p, int q0, int lq, int g, int rg,
+                                            bool writer, int lane)
+{
+    const int G = 1 << p.log2g;
+    const int j = lane >> 4;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        const int r = (rg * RTW + rt) * 16 + (lane & 15);  // packed row
+        const int t = r >> p.log2g, h = r & (G - 1);
+        uint32_t raw[2][16];                               // bf16 pairs of dims 128 kc + 32 j ..
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            uint4 q4[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
+                           make_uint4(0, 0, 0, 0)};
+            if (t < lq) {
+                const uint4 *src = (const uint4 *)(p.q + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim +
+                                                   128 * kc + 32 * j);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    q4[i] = src[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                raw[kc][4 * i] = q4[i].x;
+                raw[kc][4 * i + 1] = q4[i].y;
+                raw[kc][4 * i + 2] = q4[i].z;
+                raw[kc][4 * i + 3] = q4[i].w;
+            }
+        }
+        auto lo_f = [](uint32_t w) { return __builtin_bit_cast(float, w << 16); };
+        auto hi_f = [](uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); };
+        float amax = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                amax = fmaxf(amax, fmaxf(fabsf(lo_f(raw[kc][i])), fabsf(hi_f(raw[kc][i]))));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));         // row max (4 lanes)
+        int k = 0;
+        if (amax > 0.f) {
+            int e;
+            frexpf(amax, &e);                              // amax in [2^(e-1), 2^e)
+            k = min(8 - e, 127);
+        }
+        crow[rt] = ldexpf(c, -k);
+        if (!writer)
+            continue;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            uint32_t hi[8], lo[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float s0 = ldexpf(lo_f(raw[kc][2 * i]), k), s1 = ldexpf(hi_f(raw[kc][2 * i]), k);
+                const float s2 = ldexpf(lo_f(raw[kc][2 * i + 1]), k), s3 = ldexpf(hi_f(raw[kc][2 * i + 1]), k);
+                int hw = __builtin_amdgcn_cvt_pk_fp8_f32(s0, s1, 0, false);
+                hw = __builtin_amdgcn_cvt_pk_fp8_f32(s2, s3, hw, true);
+                const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+                const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+                int lw = __builtin_amdgcn_cvt_pk_fp8_f32(s0 - h01[0], s1 - h01[1], 0, false);
+                lw = __builtin_amdgcn_cvt_pk_fp8_f32(s2 - h23[0], s3 - h23[1], lw, true);
+                hi[i] = (uint32_t)hw;
+                lo[i] = (uint32_t)lw;
+            }
+            uint4 *dh = reinterpret_cast<uint4 *>(qlds + ((size_t)(((rg * RTW + rt) * 2 + kc) * 2) * 64 + lane) * 32);
+            uint4 *dl = reinterpret_cast<uint4 *>(qlds + ((size_t)(((rg * RTW + rt) * 2 + kc) * 2 + 1) * 64 + lane) * 32);
+            dh[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            dh[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+            dl[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            dl[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+        }
+    }
+}
+
+// QK^T of a step (two pages) on fp8: S^T[a][rt] (16 keys x 16 rows) from the
+// ring stage's K rows and the staged hi/lo Q operands.  K operand: lane (n =
+// l%16, j = l/16) holds dims 128 kc + 32 j .. +32 of key n, i.e. 16-byte chunks
+// 8 kc + 2 j and 8 kc + 2 j + 1 (stored at slots chunk ^ n).
+template <int RTW>
+__device__ __forceinline__ void qk_lds_f8(floatx4_t (&S)[2][RTW], const unsigned char *stage,
+                                          const unsigned char *qw, int lane)
+{
+    const int n = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+            S[a][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        intx8_t kop[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const int c0 = 8 * kc + 2 * j;
+            const uint4 lo4 = *reinterpret_cast<const uint4 *>(stage + 4096 * a + 256 * n + 16 * (c0 ^ n));
+            const uint4 hi4 = *reinterpret_cast<const uint4 *>(stage + 4096 * a + 256 * n + 16 * ((c0 + 1) ^ n));
+            kop[a] = intx8_t{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
+                             (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+        }
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {
+                const uint4 *qp = reinterpret_cast<const uint4 *>(
+                    qw + ((size_t)((rt * 2 + kc) * 2 + part) * 64 + lane) * 32);
+                const uint4 b0 = qp[0], b1 = qp[1];
+                const intx8_t qop = intx8_t{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                                            (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+                    S[a][rt] = mfma16_f8(kop[a], qop, S[a][rt]);
+            }
     }
 }
 
@@ -1201,11 +1397,9 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
     constexpr int NR = 2;
     constexpr int NG = 4;
     constexpr int RT = RTW * NR;                             // row tiles per piece
-    constexpr int kQBytes = 4 * 8 * 64 * 16;                 // Q operands, up to 4 row tiles
+    constexpr int kQBytes = kQf8Bytes;                      // fp8 hi/lo Q operands, 4 row tiles
     constexpr int kRingBytes = 2 * kStageBytes;              // per key group
-    constexpr int kThreadsW8 = 512;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kQBytes + NG * kRingBytes];
-    uint4 *qs = reinterpret_cast<uint4 *>(lds);
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
@@ -1228,7 +1422,7 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
     const float c = p.scale_log2 * kd;
     unsigned char *ring = lds + kQBytes + kg * kRingBytes;
     const uint32_t ring_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(ring));
-    const uint4 *qs_wave = qs + rg * RTW * 8 * 64;
+    const unsigned char *qw = lds + (size_t)rg * RTW * 2 * 2 * 64 * 32;
     uint32_t off[4];
     dma_lane_offsets(off, p.hkv, lane);
     const int64_t page_bytes = (int64_t)kPage * p.hkv * kHeadDim;
@@ -1252,35 +1446,6 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
         const bool whole = (p0 == 0 && p1 == cnt);
         const int slot = w + bg;
 
-        // ---- packed Q rows of this piece in LDS, in operand order
-        __syncthreads();                                // previous piece's merge reads done
-        for (int u = threadIdx.x; u < RT * 512; u += kThreadsW8) {
-            const int rt = u >> 9, ss = (u >> 6) & 7, l = u & 63;
-            const int row = rt * 16 + (l & 15), jj = l >> 4;
-            const int dim = (4 * (ss >> 1) + jj) * 16 + 8 * (ss & 1);
-            const int t = row >> p.log2g, h = row & (G - 1);
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (t < lq)
-                val = *(const uint4 *)(p.q + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + dim);
-            qs[u] = val;
-        }
-
-        RowState<RTW> st;
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt) {
-            st.m[rt] = -INFINITY;
-            st.l[rt] = 0.f;
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-                st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        int limit[RTW];
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt) {
-            const int t = ((rg * RTW + rt) * 16 + (lane & 15)) >> p.log2g;
-            limit[rt] = min(ctx + t, lk - 1);
-        }
-
         const int npairs = (p1 - p0 + 1) >> 1;
         const int nsteps = (npairs + NG - 1) / NG;             // uniform over the workgroup
         const bool rows_live = (rg * RTW * 16) < lq * G;
@@ -1298,25 +1463,50 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
             const int64_t yb = pa + 1 < p1 ? phys(pa + 1) : ya;
             dma_step_part(ring_addr + stage * kStageBytes, pool, rg, ya, yb, page_bytes, off);
         };
+
+        __syncthreads();                                // previous piece's merge reads done
         if (kg < npairs)
-            issue(kg, 0);
+            issue(kg, 0);                              // first copy overlaps the Q staging
+
+        // ---- packed Q rows of this piece in LDS (fp8 hi/lo operands), row multipliers
+        float crow[RTW];                                       // logit multiplier of this lane's row
+        stage_q_fp8<RTW>(lds, crow, c, p, q0, lq, g, rg, kg == 0, lane);
+
+        RowState<RTW> st;
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            st.m[rt] = -INFINITY;
+            st.l[rt] = 0.f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        int limit[RTW];
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            const int t = ((rg * RTW + rt) * 16 + (lane & 15)) >> p.log2g;
+            limit[rt] = min(ctx + t, lk - 1);
+        }
+
+
         for (int t = 0; t < nsteps; ++t) {
             const int k = kg + t * NG;
             wait_vmcnt<0>();                                   // own copies of step t landed
             __syncthreads();                                   // partner's too; stage t+1 is free
+
             if (k + NG < npairs)
                 issue(k + NG, (t + 1) & 1);
             if (k < npairs && rows_live) {
                 const unsigned char *stage = ring + (t & 1) * kStageBytes;
                 floatx4_t S[2][RTW];
-                qk_lds<RTW>(S, stage, qs_wave, lane);
+                qk_lds_f8<RTW>(S, stage, qw, lane);
                 const int pa = p0 + 2 * k;
                 const bool hb = pa + 1 < p1;
                 const int key0 = pa * kPage;
                 const bool masked = !hb || key0 + 31 > ctx;
                 bf16x8_t pop[RTW];
-                softmax_step<RTW>(st, pop, S, limit, key0, hb, c, lane, masked);
-                pv_lds<RTW>(st, stage, pop, masked ? v_zero_mask(key0, hb, lk, lane) : 0u, lane);
+                softmax_step<RTW>(st, pop, S, limit, key0, hb, crow, lane, masked);
+                pv_lds<RTW>(st, stage, pop, masked, masked ? v_zero_mask(key0, hb, lk, lane) : 0u, lane);
             }
         }
         wait_vmcnt<0>();
