@@ -35,6 +35,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+MAIN_KERNEL = {"fp8": "va_split_kv_fp8_w8_kernel", "bf16": "va_split_kv_kernel"}
+# Arithmetic of the path: FP8 KV runs QK^T on fp8 MFMA (Q as an exact hi/lo fp8
+# pair) and PV on bf16 MFMA; bf16 KV runs both on bf16 MFMA; fp32 accumulation.
+COMPUTE_DTYPE = {"fp8": "fp8/bf16", "bf16": "bf16"}
 
 
 def algorithmic_bytes(p, seqs=None) -> int:
@@ -213,7 +217,7 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                     "traffic": load_traffic(p.name),
-                    "kernel": "va_split_kv_kernel", "us_per_launch": round(main_ms * 1e3, 3)}
+                    "kernel": MAIN_KERNEL[p.kv_dtype], "us_per_launch": round(main_ms * 1e3, 3)}
         log(f"bench: main kernel {main_ms * 1e3:.2f} us/launch, {achieved:.1f} GB/s")
 
     cpu = None
@@ -234,7 +238,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": COMPUTE_DTYPE[p.kv_dtype],
         "data": "synthetic",
         "config": {"workload": va_inputs.CONFIG_NAMES[args.config] if args.config != 4
                    else p.name,
