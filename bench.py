@@ -148,6 +148,7 @@ def main():
 
     t0 = time.perf_counter()
     p = va_inputs.config(args.config, args.variant)
+    workload = va_inputs.CONFIG_NAMES[args.config] if args.config != 4 else p.name
     log(f"bench: generated {p.name} in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
     q = torch.from_numpy(p.q.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -216,7 +217,7 @@ def main():
         achieved = alg / (main_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                    "traffic": load_traffic(p.name),
+                    "traffic": load_traffic(workload),
                     "kernel": MAIN_KERNEL[p.kv_dtype], "us_per_launch": round(main_ms * 1e3, 3)}
         log(f"bench: main kernel {main_ms * 1e3:.2f} us/launch, {achieved:.1f} GB/s")
 
@@ -240,8 +241,7 @@ def main():
         "vs_baseline": None,
         "dtype": COMPUTE_DTYPE[p.kv_dtype],
         "data": "synthetic",
-        "config": {"workload": va_inputs.CONFIG_NAMES[args.config] if args.config != 4
-                   else p.name,
+        "config": {"workload": workload,
                    "num_seqs": p.num_seqs, "q_len": int(p.max_seqlen_q),
                    "kv_len_max": int(p.max_seqlen_k), "q_heads": p.num_q_heads,
                    "kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "page": p.page_size,
