@@ -73,10 +73,13 @@ struct SplitParams {
     const float *kdesc;
     const float *vdesc;
     uint16_t *out;
-    float *ws_o;          // [slots][rows_max][256]
+    void *ws_o;           // [slots][rows_max][256]: fp16 (FP8 cache) or fp32 (bf16 cache)
+    int32_t ws_o_bytes;   // size of the ws_o region
     float *ws_lse;        // [slots][rows_max]   log2-domain LSE of the scaled logits
     int32_t *ws_prefix;   // [BH + 1] exclusive prefix of page counts, [BH] = total
     int32_t *ws_meta;     // [0] = workgroups in use
+    int32_t *ws_count;    // [slots] pieces of a group finished, at the group's first slot; zero between calls
+    int32_t *ws_count2;   // [BH] groups of a (sequence, kv head) finished; zero between calls
     float scale_log2;     // softmax_scale * log2(e)
     int32_t num_seqs, hq, hkv, log2g, mbps, grid_n, min_pages, rows_max;
     int64_t num_blocks;
@@ -85,7 +88,7 @@ struct SplitParams {
 struct MergeParams {
     const int32_t *cu;
     const float *vdesc;
-    const float *ws_o;
+    const void *ws_o;     // fp16 or fp32 partials, see SplitParams
     const float *ws_lse;
     const int32_t *ws_prefix;
     const int32_t *ws_meta;
@@ -529,6 +532,7 @@ struct Share {
     int n_eff;      // workgroups in use
     int s, e;       // flat page range of this workgroup
     int bg, base;   // first (sequence, kv head) touching s and its flat start
+    int total;      // pages over all (sequence, kv head) pairs
 };
 
 // Every wave runs this (no LDS, no barrier).  Total page count, the number of
@@ -542,6 +546,7 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
         const int total = __shfl(incl, 63);
         Share sh;
         sh.n_eff = min(p.grid_n, max(1, total / max(1, p.min_pages)));
+        sh.total = total;
         sh.s = (int)(((int64_t)w * total) / sh.n_eff);
         sh.e = (int)(((int64_t)(w + 1) * total) / sh.n_eff);
         const unsigned long long hit = __ballot(lane < bh && incl > sh.s);
@@ -571,6 +576,7 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
     }
     Share sh;
     sh.n_eff = min(p.grid_n, max(1, total / max(1, p.min_pages)));
+    sh.total = total;
     sh.s = (int)(((int64_t)w * total) / sh.n_eff);
     sh.e = (int)(((int64_t)(w + 1) * total) / sh.n_eff);
     sh.bg = bh;
@@ -830,7 +836,7 @@ void va_split_kv_kernel(SplitParams p)
                         }
                     } else {
                         const float inv = L > 0.f ? 1.0f / L : 0.f;
-                        float *dst = p.ws_o + ((int64_t)slot * p.rows_max + row) * kHeadDim;
+                        float *dst = static_cast<float *>(p.ws_o) + ((int64_t)slot * p.rows_max + row) * kHeadDim;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             float4 *d4 = reinterpret_cast<float4 *>(dst + 64 * j + 16 * e);
@@ -878,17 +884,12 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-__device__ __forceinline__ void wait_lgkmcnt0()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
-
 // One ring stage = one step (two pages) of one kv head, 16 KiB:
 //   [K page a | K page b | V page a | V page b], 4 KiB each, 16 key rows of
 //   256 bytes.  The 16-byte chunk c of key row n sits at slot c ^ n of the row
 //   (XOR swizzle), so the operand reads below touch 16 distinct slots per 16 lanes.
 constexpr int kStageBytes = 16384;
-constexpr int kDmaPerStep = 16;          // 4 pages x 4 KiB / 1 KiB per instruction
+constexpr int kDmaPerPart = 8;           // copy instructions per wave and step (two 4 KiB pages)
 
 // Lane offsets of the 4 copy instructions of one page: instruction i, lane l
 // writes LDS bytes [1024 i + 16 l, +16) = key row n = 4i + l/16, slot l%16, so it
@@ -900,31 +901,6 @@ __device__ __forceinline__ void dma_lane_offsets(uint32_t (&off)[4], int hkv, in
         const int n = 4 * i + (lane >> 4);
         off[i] = (uint32_t)(n * hkv * kHeadDim + (((lane & 15) ^ n) * 16));
     }
-}
-
-// Copy one step (pages a and b of the kv head) into a ring stage.  Always 16
-// instructions: a missing page b re-reads page a (masked out later), so the
-// vmcnt bookkeeping is the same for every step.
-__device__ __forceinline__ void dma_step(uint32_t stage, const uint8_t *kb, const uint8_t *vb,
-                                         int64_t ya, int64_t yb, int64_t page_bytes,
-                                         const uint32_t (&off)[4])
-{
-    const uint8_t *ka = kb + ya * page_bytes;
-    const uint8_t *kbb = kb + yb * page_bytes;
-    const uint8_t *va = vb + ya * page_bytes;
-    const uint8_t *vbb = vb + yb * page_bytes;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        dma16(ka, off[i], stage + 1024 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        dma16(kbb, off[i], stage + 4096 + 1024 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        dma16(va, off[i], stage + 8192 + 1024 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        dma16(vbb, off[i], stage + 12288 + 1024 * i);
 }
 
 // Half of a step copy: the K pages (part 0) or the V pages (part 1), 8
@@ -941,303 +917,6 @@ __device__ __forceinline__ void dma_step_part(uint32_t stage, const uint8_t *poo
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         dma16(b, off[i], base + 4096 + 1024 * i);
-}
-
-// QK half of a step with K read from a ring stage (same math as qk_step).
-template <int RT>
-__device__ __forceinline__ void qk_lds(floatx4_t (&S)[2][RT], const unsigned char *stage,
-                                       const uint4 *qs, int lane)
-{
-    const int n = lane & 15, j = lane >> 4;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-            S[a][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    uint4 kr[2];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        if ((s & 1) == 0) {
-            const int chunk = 4 * (s >> 1) + j;
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-                kr[a] = *reinterpret_cast<const uint4 *>(stage + 4096 * a + 256 * n + 16 * (chunk ^ n));
-        }
-        bf16x8_t qop[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-            qop[rt] = __builtin_bit_cast(bf16x8_t, qs[(rt * 8 + s) * 64 + lane]);
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            const uint32_t w0 = (s & 1) ? kr[a].z : kr[a].x;
-            const uint32_t w1 = (s & 1) ? kr[a].w : kr[a].y;
-            uint4 o;
-            o.x = fp8x2_lo_to_bf16x2(w0);
-            o.y = fp8x2_hi_to_bf16x2(w0);
-            o.z = fp8x2_lo_to_bf16x2(w1);
-            o.w = fp8x2_hi_to_bf16x2(w1);
-            const bf16x8_t kop = __builtin_bit_cast(bf16x8_t, o);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                S[a][rt] = mfma16(kop, qop[rt], S[a][rt]);
-        }
-    }
-}
-
-// Merge the softmax states of the NG key groups of each row group through
-// LDS, as a binary tree (key group kg absorbs kg + d for d = 1, 2, ...), one
-// row tile at a time with a barrier between rounds, so a wave holds at most
-// one incoming row tile (64 floats per lane) at a time.  The key-group-0 wave
-// of each row group then writes its rows: final rows when the piece is the
-// whole sequence, else the piece's partial.
-template <int RTW, int NR, int NG>
-__device__ __forceinline__ void merge_and_write(RowState<RTW> &st, unsigned char *lds, const SplitParams &p,
-                                                int kg, int rg, int lane, int lq, int q0, int g,
-                                                int slot, bool whole, float vd)
-{
-    constexpr int kSlotFloats = 64 * 64 + 2 * 64;         // one row tile of one wave: O^T, m, l
-    const int G = 1 << p.log2g;
-#pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-        float t = st.l[rt];
-        t += __shfl_xor(t, 16);
-        t += __shfl_xor(t, 32);
-        st.l[rt] = t;
-    }
-#pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-#pragma unroll
-        for (int d = 1; d < NG; d <<= 1) {
-            float *buf = reinterpret_cast<float *>(lds) + (size_t)(rg * (NG / 2) + kg / (2 * d)) * kSlotFloats;
-            __syncthreads();
-            if (kg % (2 * d) == d) {
-                float4 *o4 = reinterpret_cast<float4 *>(buf);
-#pragma unroll
-                for (int t = 0; t < 16; ++t)
-                    o4[t * 64 + lane] = make_float4(st.o[t][rt][0], st.o[t][rt][1], st.o[t][rt][2], st.o[t][rt][3]);
-                buf[64 * 64 + lane] = st.m[rt];
-                buf[64 * 64 + 64 + lane] = st.l[rt];
-            }
-            __syncthreads();
-            if (kg % (2 * d) == 0 && kg + d < NG) {
-                const float4 *o4 = reinterpret_cast<const float4 *>(buf);
-                const float mo = buf[64 * 64 + lane];
-                const float lo = buf[64 * 64 + 64 + lane];
-                const float mm = fmaxf(st.m[rt], mo);
-                const float fa = st.m[rt] == -INFINITY ? 0.f : exp2_fast(st.m[rt] - mm);
-                const float fb = mo == -INFINITY ? 0.f : exp2_fast(mo - mm);
-#pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    const float4 v = o4[t * 64 + lane];
-                    st.o[t][rt][0] = fa * st.o[t][rt][0] + fb * v.x;
-                    st.o[t][rt][1] = fa * st.o[t][rt][1] + fb * v.y;
-                    st.o[t][rt][2] = fa * st.o[t][rt][2] + fb * v.z;
-                    st.o[t][rt][3] = fa * st.o[t][rt][3] + fb * v.w;
-                }
-                st.l[rt] = fa * st.l[rt] + fb * lo;
-                st.m[rt] = mm;
-            }
-        }
-    }
-    if (kg != 0)
-        return;
-    const int j = lane >> 4;
-#pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-        const int row = (rg * RTW + rt) * 16 + (lane & 15);
-        const int t = row >> p.log2g;
-        const int h = row & (G - 1);
-        if (t >= lq)
-            continue;
-        const float L = st.l[rt];
-        if (whole) {
-            const float inv = L > 0.f ? vd / L : 0.f;
-            uint16_t *dst = p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint4 lo, hi;
-                lo.x = pack_bf16x2(st.o[0][rt][e] * inv, st.o[1][rt][e] * inv);
-                lo.y = pack_bf16x2(st.o[2][rt][e] * inv, st.o[3][rt][e] * inv);
-                lo.z = pack_bf16x2(st.o[4][rt][e] * inv, st.o[5][rt][e] * inv);
-                lo.w = pack_bf16x2(st.o[6][rt][e] * inv, st.o[7][rt][e] * inv);
-                hi.x = pack_bf16x2(st.o[8][rt][e] * inv, st.o[9][rt][e] * inv);
-                hi.y = pack_bf16x2(st.o[10][rt][e] * inv, st.o[11][rt][e] * inv);
-                hi.z = pack_bf16x2(st.o[12][rt][e] * inv, st.o[13][rt][e] * inv);
-                hi.w = pack_bf16x2(st.o[14][rt][e] * inv, st.o[15][rt][e] * inv);
-                uint4 *d4 = reinterpret_cast<uint4 *>(dst + 64 * j + 16 * e);
-                d4[0] = lo;
-                d4[1] = hi;
-            }
-        } else {
-            const float inv = L > 0.f ? 1.0f / L : 0.f;
-            float *dst = p.ws_o + ((int64_t)slot * p.rows_max + row) * kHeadDim;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float4 *d4 = reinterpret_cast<float4 *>(dst + 64 * j + 16 * e);
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq)
-                    d4[qq] = make_float4(st.o[4 * qq][rt][e] * inv, st.o[4 * qq + 1][rt][e] * inv,
-                                         st.o[4 * qq + 2][rt][e] * inv, st.o[4 * qq + 3][rt][e] * inv);
-            }
-            if (j == 0)
-                p.ws_lse[(int64_t)slot * p.rows_max + row] = L > 0.f ? st.m[rt] + __log2f(L) : -INFINITY;
-        }
-    }
-}
-
-// FP8 split-KV kernel.  The 4 waves form NG = 4/NR key groups x NR row
-// groups: a wave holds RTW row tiles (row group rg) and takes every NG-th step
-// (page pair) of the piece (key group kg).  Each wave copies its steps straight
-// from HBM into its own 2-stage LDS ring, one step ahead of the compute, so
-// 16-32 KiB per wave stay in flight.  With NR = 2 the two waves of a key
-// group fetch the same pages (the second fetch is served by L2).
-template <int RTW, int NR>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
-void va_split_kv_fp8_kernel(SplitParams p)
-{
-    constexpr int NG = kWaves / NR;
-    constexpr int RT = RTW * NR;                             // row tiles per piece
-    constexpr int kQBytes = 4 * 8 * 64 * 16;                 // Q operands, up to 4 row tiles
-    constexpr int kRingBytes = 2 * kStageBytes;              // per wave
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[kQBytes + kWaves * kRingBytes];
-    uint4 *qs = reinterpret_cast<uint4 *>(lds);
-
-    const int lane = threadIdx.x & 63;
-    const int wave = uniform(threadIdx.x >> 6);
-    const int rg = wave % NR;
-    const int kg = wave / NR;
-    const int w = blockIdx.x;
-    const int G = 1 << p.log2g;
-
-    Share sh = locate(p, w, lane, w == 0 && wave == 0);
-    sh.n_eff = uniform(sh.n_eff);
-    sh.s = uniform(sh.s);
-    sh.e = uniform(sh.e);
-    sh.bg = uniform(sh.bg);
-    sh.base = uniform(sh.base);
-    if (w >= sh.n_eff)
-        return;                                        // uniform over the workgroup
-
-    const float kd = p.kdesc ? p.kdesc[0] : 1.0f;
-    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
-    const float c = p.scale_log2 * kd;
-    unsigned char *ring = lds + kQBytes + wave * kRingBytes;
-    const uint32_t ring_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(ring));
-    const uint4 *qs_wave = qs + rg * RTW * 8 * 64;
-    uint32_t off[4];
-    dma_lane_offsets(off, p.hkv, lane);
-    const int64_t page_bytes = (int64_t)kPage * p.hkv * kHeadDim;
-
-    const int bh = p.num_seqs * p.hkv;
-    int s = sh.s, bg = sh.bg, base = sh.base;
-    while (s < sh.e && bg < bh) {
-        const int b = uniform(bg / p.hkv);
-        const int g = bg - b * p.hkv;
-        const int q0 = load_uniform(p.cu, b);
-        const int lq = load_uniform(p.cu, b + 1) - q0;
-        const int lk = load_uniform(p.seqused, b);
-        const int cnt = (lq <= 0 || lk <= 0) ? 0 : min((lk + kPage - 1) / kPage, p.mbps);
-        if (cnt == 0) {
-            ++bg;
-            continue;
-        }
-        const int ctx = lk - lq;
-        const int p0 = s - base;
-        const int p1 = min(sh.e, base + cnt) - base;
-        const bool whole = (p0 == 0 && p1 == cnt);
-        const int slot = w + bg;
-
-        // ---- packed Q rows of this piece in LDS, in operand order
-        __syncthreads();                                // previous piece's merge reads done
-        for (int u = threadIdx.x; u < RT * 512; u += kThreads) {
-            const int rt = u >> 9, ss = (u >> 6) & 7, l = u & 63;
-            const int row = rt * 16 + (l & 15), jj = l >> 4;
-            const int dim = (4 * (ss >> 1) + jj) * 16 + 8 * (ss & 1);
-            const int t = row >> p.log2g, h = row & (G - 1);
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (t < lq)
-                val = *(const uint4 *)(p.q + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + dim);
-            qs[u] = val;
-        }
-        __syncthreads();
-
-        RowState<RTW> st;
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt) {
-            st.m[rt] = -INFINITY;
-            st.l[rt] = 0.f;
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-                st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        int limit[RTW];
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt) {
-            const int t = ((rg * RTW + rt) * 16 + (lane & 15)) >> p.log2g;
-            limit[rt] = min(ctx + t, lk - 1);
-        }
-
-        const int npairs = (p1 - p0 + 1) >> 1;
-        const bool rows_live = (rg * RTW * 16) < lq * G;
-        if (rows_live && kg < npairs) {
-            const int32_t *btrow = p.bt + (int64_t)b * p.mbps;
-            const uint8_t *kb = p.k + (int64_t)g * kHeadDim;
-            const uint8_t *vb = p.v + (int64_t)g * kHeadDim;
-            const int64_t maxpage = p.num_blocks - 1;
-            // Block-table entries are read with scalar loads (uniform address,
-            // read-only memory, so the constant address space): a vector load
-            // here would need a vmcnt wait that also drains the ring's copies.
-            typedef const __attribute__((address_space(4))) int32_t cint32;
-            cint32 *btc = (cint32 *)btrow;
-            auto phys = [&](int page) -> int64_t {
-                int64_t v = btc[uniform(page)];
-                v = v < 0 ? 0 : v;
-                return v > maxpage ? maxpage : v;
-            };
-            auto issue = [&](int k, int stage) {
-                const int pa = p0 + 2 * k;
-                const int64_t ya = phys(pa);
-                const int64_t yb = pa + 1 < p1 ? phys(pa + 1) : ya;
-                dma_step(ring_addr + stage * kStageBytes, kb, vb, ya, yb, page_bytes, off);
-            };
-            issue(kg, 0);
-            if (kg + NG < npairs)
-                issue(kg + NG, 1);
-            int t = 0;
-            for (int k = kg; k < npairs; k += NG, ++t) {
-                if (k + NG < npairs)                           // next step already in flight
-                    wait_vmcnt<kDmaPerStep>();
-                else
-                    wait_vmcnt<0>();
-                const unsigned char *stage = ring + (t & 1) * kStageBytes;
-                floatx4_t S[2][RTW];
-                qk_lds<RTW>(S, stage, qs_wave, lane);
-                const int pa = p0 + 2 * k;
-                const bool hb = pa + 1 < p1;
-                const int key0 = pa * kPage;
-                const bool masked = !hb || key0 + 31 > ctx;
-                bf16x8_t pop[RTW];
-                {
-                    float cr[RTW];
-#pragma unroll
-                    for (int rt = 0; rt < RTW; ++rt)
-                        cr[rt] = c;
-                    softmax_step<RTW>(st, pop, S, limit, key0, hb, cr, lane, masked);
-                }
-                pv_lds<RTW>(st, stage, pop, masked, masked ? v_zero_mask(key0, hb, lk, lane) : 0u, lane);
-                if (k + 2 * NG < npairs) {
-                    wait_lgkmcnt0();                           // this stage's reads are done
-                    issue(k + 2 * NG, t & 1);
-                }
-            }
-        }
-
-        merge_and_write<RTW, NR, NG>(st, lds, p, kg, rg, lane, lq, q0, g, slot, whole, vd);
-
-        s = base + p1;
-        base += cnt;
-        ++bg;
-    }
 }
 
 // ------------------------------------------- QK on fp8 (Q split hi + lo) --
@@ -1258,52 +937,82 @@ void va_split_kv_fp8_kernel(SplitParams p)
 // row 16 rt + l%16, dims 128 kc + 32 (l/16) .. +32.
 constexpr int kQf8Bytes = 4 * 2 * 2 * 64 * 32;              // up to 4 row tiles: 32 KiB
 
-// Each wave stages the rows of its own row group in the order its lanes
-// consume them: lane l takes row 16 (rg RTW + rt) + l%16 and dims
-// 128 kc + 32 (l/16) .. +32 for kc = 0, 1.  The four lanes that share a row
-// hold all 256 dims, so two lane exchanges give every lane its row's maximum
-// and exponent k_r, which the lane keeps (the row's logit multiplier is
-// c 2^-k_r).  Only key group 0 writes the operands to LDS; the other key
-// groups of the row group compute the same exponents.
+// The piece's packed Q rows arrive in the Q area as bf16, 512 B per row
+// r = t G + h, by direct copies; the 16-byte chunk c of row r sits at slot
+// c ^ (r & 15) so that the 16 rows read by one lane group hit 16 different
+// banks.  Each wave reads the rows of its own row
+// group in the order its lanes consume them: lane l takes row 16 (rg RTW + rt)
+// + l%16 and dims 128 kc + 32 (l/16) .. +32 for kc = 0, 1.  The four lanes
+// that share a row hold all 256 dims, so two lane exchanges give every lane
+// its row's maximum and exponent k_r, which the lane keeps (the row's logit
+// multiplier is c 2^-k_r).  After a barrier (every wave holds its rows) the
+// four key groups of the row group overwrite the area with the fp8 operands,
+// one (row tile, dim half) block each.
+template <int RTW>
+__device__ __forceinline__ void convert_q_block(unsigned char *qlds, const uint32_t (&raw)[16], int k, int blk,
+                                                int lane)
+{
+    auto lo_f = [](uint32_t w) { return __builtin_bit_cast(float, w << 16); };
+    auto hi_f = [](uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); };
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float s0 = ldexpf(lo_f(raw[2 * i]), k), s1 = ldexpf(hi_f(raw[2 * i]), k);
+        const float s2 = ldexpf(lo_f(raw[2 * i + 1]), k), s3 = ldexpf(hi_f(raw[2 * i + 1]), k);
+        int hw = __builtin_amdgcn_cvt_pk_fp8_f32(s0, s1, 0, false);
+        hw = __builtin_amdgcn_cvt_pk_fp8_f32(s2, s3, hw, true);
+        const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+        const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+        int lw = __builtin_amdgcn_cvt_pk_fp8_f32(s0 - h01[0], s1 - h01[1], 0, false);
+        lw = __builtin_amdgcn_cvt_pk_fp8_f32(s2 - h23[0], s3 - h23[1], lw, true);
+        hi[i] = (uint32_t)hw;
+        lo[i] = (uint32_t)lw;
+    }
+    // block blk = rt * 2 + kc of the whole tile set; parts 0 (hi) and 1 (lo)
+    uint4 *dh = reinterpret_cast<uint4 *>(qlds + ((size_t)(blk * 2) * 64 + lane) * 32);
+    uint4 *dl = reinterpret_cast<uint4 *>(qlds + ((size_t)(blk * 2 + 1) * 64 + lane) * 32);
+    dh[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    dh[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+    dl[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    dl[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+}
+
 template <int RTW>
 __device__ __forceinline__ void stage_q_fp8(unsigned char *qlds, float (&crow)[RTW], float c,
-                                            const SplitParams &p, int q0, int lq, int g, int rg,
-                                            bool writer, int lane)
+                                            const SplitParams &p, int lq, int rg, int kg, int lane)
 {
-    const int G = 1 << p.log2g;
     const int j = lane >> 4;
+    uint32_t raw[RTW][2][16];                              // bf16 pairs of dims 128 kc + 32 j ..
+    int kx[RTW];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-        const int r = (rg * RTW + rt) * 16 + (lane & 15);  // packed row
-        const int t = r >> p.log2g, h = r & (G - 1);
-        uint32_t raw[2][16];                               // bf16 pairs of dims 128 kc + 32 j ..
+        const int n = lane & 15;
+        const int r = (rg * RTW + rt) * 16 + n;             // packed row
+        const bool live = (r >> p.log2g) < lq;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-            uint4 q4[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
-                           make_uint4(0, 0, 0, 0)};
-            if (t < lq) {
-                const uint4 *src = (const uint4 *)(p.q + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim +
-                                                   128 * kc + 32 * j);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    q4[i] = src[i];
-            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                raw[kc][4 * i] = q4[i].x;
-                raw[kc][4 * i + 1] = q4[i].y;
-                raw[kc][4 * i + 2] = q4[i].z;
-                raw[kc][4 * i + 3] = q4[i].w;
+                const int chunk = 16 * kc + 4 * j + i;      // dims 8 chunk .. +8
+                const uint4 q4 = live ? *reinterpret_cast<const uint4 *>(qlds + (size_t)r * 512 + ((chunk ^ n) * 16))
+                                      : make_uint4(0, 0, 0, 0);
+                raw[rt][kc][4 * i] = q4.x;
+                raw[rt][kc][4 * i + 1] = q4.y;
+                raw[rt][kc][4 * i + 2] = q4.z;
+                raw[rt][kc][4 * i + 3] = q4.w;
             }
         }
-        auto lo_f = [](uint32_t w) { return __builtin_bit_cast(float, w << 16); };
-        auto hi_f = [](uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); };
+    }
+    auto lo_f = [](uint32_t w) { return __builtin_bit_cast(float, w << 16); };
+    auto hi_f = [](uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); };
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
         float amax = 0.f;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                amax = fmaxf(amax, fmaxf(fabsf(lo_f(raw[kc][i])), fabsf(hi_f(raw[kc][i]))));
+                amax = fmaxf(amax, fmaxf(fabsf(lo_f(raw[rt][kc][i])), fabsf(hi_f(raw[rt][kc][i]))));
         amax = fmaxf(amax, __shfl_xor(amax, 16));
         amax = fmaxf(amax, __shfl_xor(amax, 32));         // row max (4 lanes)
         int k = 0;
@@ -1313,31 +1022,21 @@ __device__ __forceinline__ void stage_q_fp8(unsigned char *qlds, float (&crow)[R
             k = min(8 - e, 127);
         }
         crow[rt] = ldexpf(c, -k);
-        if (!writer)
-            continue;
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            uint32_t hi[8], lo[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float s0 = ldexpf(lo_f(raw[kc][2 * i]), k), s1 = ldexpf(hi_f(raw[kc][2 * i]), k);
-                const float s2 = ldexpf(lo_f(raw[kc][2 * i + 1]), k), s3 = ldexpf(hi_f(raw[kc][2 * i + 1]), k);
-                int hw = __builtin_amdgcn_cvt_pk_fp8_f32(s0, s1, 0, false);
-                hw = __builtin_amdgcn_cvt_pk_fp8_f32(s2, s3, hw, true);
-                const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
-                const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
-                int lw = __builtin_amdgcn_cvt_pk_fp8_f32(s0 - h01[0], s1 - h01[1], 0, false);
-                lw = __builtin_amdgcn_cvt_pk_fp8_f32(s2 - h23[0], s3 - h23[1], lw, true);
-                hi[i] = (uint32_t)hw;
-                lo[i] = (uint32_t)lw;
-            }
-            uint4 *dh = reinterpret_cast<uint4 *>(qlds + ((size_t)(((rg * RTW + rt) * 2 + kc) * 2) * 64 + lane) * 32);
-            uint4 *dl = reinterpret_cast<uint4 *>(qlds + ((size_t)(((rg * RTW + rt) * 2 + kc) * 2 + 1) * 64 + lane) * 32);
-            dh[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            dh[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
-            dl[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-            dl[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
-        }
+        kx[rt] = k;
+    }
+    __syncthreads();                                       // every wave holds its rows
+    // key group kg converts block (row tile kg / 2, dim half kg % 2)
+    if (kg >= 2 * RTW)
+        return;
+    if (kg == 0)
+        convert_q_block<RTW>(qlds, raw[0][0], kx[0], rg * RTW * 2 + 0, lane);
+    else if (kg == 1)
+        convert_q_block<RTW>(qlds, raw[0][1], kx[0], rg * RTW * 2 + 1, lane);
+    if constexpr (RTW == 2) {
+        if (kg == 2)
+            convert_q_block<RTW>(qlds, raw[1][0], kx[1], rg * RTW * 2 + 2, lane);
+        else if (kg == 3)
+            convert_q_block<RTW>(qlds, raw[1][1], kx[1], rg * RTW * 2 + 3, lane);
     }
 }
 
@@ -1382,6 +1081,312 @@ __device__ __forceinline__ void qk_lds_f8(floatx4_t (&S)[2][RTW], const unsigned
     }
 }
 
+// ------------------------------------------------------- piece epilogue --
+//
+// The 4 key groups of a row group hold softmax states (m, l, O) of the same
+// rows over disjoint keys.  Each wave publishes per row its m and l and its
+// normalised O/l in fp16 (|O/l| <= max |V| <= 448 for an e4m3 cache, so fp16
+// keeps 11 significant bits), then all 512 threads combine the four states
+// in fp32, one (row, 8-dim chunk) per thread, and store 16 contiguous bytes:
+// bf16 output when the piece is the whole (sequence, kv head), else the
+// piece's partial (fp16 O/L and the fp32 log2-domain LSE) for the reduce.
+//
+// LDS after the page loop: [0, 2 KiB) holds m, l of [kg][row]; the ring area
+// holds [kg][row] rows of 256 fp16 whose 16-byte chunk c sits at c ^ (row & 15)
+// (writes from the accumulator layout and row-wise reads are both free of
+// bank conflicts).
+
+// The thread index, hidden from loop-invariant code motion: address math of
+// the per-piece epilogue would otherwise be hoisted above the page loop and
+// hold registers (spilled) through it.
+__device__ __forceinline__ int opaque_tid()
+{
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
+// Partials cross workgroups that may sit on different XCDs, whose L2 caches
+// are not coherent with each other.  They are written and read with
+// agent-scope relaxed atomic accesses (the sc1 cache policy: written through
+// to, and read from, the device's point of coherence), so no L2 writeback or
+// invalidate is needed; the piece counter orders them (see the FP8 kernel).
+typedef unsigned int uintx4_t __attribute__((ext_vector_type(4)));
+constexpr int kCoherent = 16;           // buffer cache policy bit sc1: agent-scope coherent access
+
+// Buffer resource over the partial O region (raw, byte offsets; an access
+// past num_records reads zero instead of faulting).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const SplitParams &p)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(p.ws_o, 0, p.ws_o_bytes, 0x00020000);
+}
+
+// 8 fp16 of row sr (slot * rows_max + row), dims 8c .. 8c+7.
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, int64_t sr, int c, uint4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(uintx4_t{v.x, v.y, v.z, v.w}, r, (int)((sr * kHeadDim + 8 * c) * 2), 0,
+                                           kCoherent);
+}
+
+__device__ __forceinline__ uint4 load_coherent(__amdgpu_buffer_rsrc_t r, int64_t sr, int c)
+{
+    const uintx4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)((sr * kHeadDim + 8 * c) * 2), 0, kCoherent);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_coherent(float *dst, float v)
+{
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(dst), __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_coherent(const float *src)
+{
+    return __builtin_bit_cast(float, __hip_atomic_load(reinterpret_cast<const uint32_t *>(src), __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT));
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b)
+{
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+    const half2_t h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+
+__device__ __forceinline__ float f16_hi(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+template <int RTW>
+__device__ __forceinline__ void piece_epilogue(RowState<RTW> &st, unsigned char *lds, unsigned char *obuf,
+                                               const SplitParams &p, int kg, int rg, int lane, int lq,
+                                               int q0, int g, int slot, bool whole, float vd)
+{
+    constexpr int NG = 4;
+    constexpr int RT = 2 * RTW;                          // row tiles of the workgroup
+    const int G = 1 << p.log2g;
+    const int n = lane & 15, j = lane >> 4;
+    float *ml = reinterpret_cast<float *>(lds);
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        float t = st.l[rt];
+        t += __shfl_xor(t, 16);
+        t += __shfl_xor(t, 32);
+        st.l[rt] = t;
+    }
+    __syncthreads();                                     // every wave is past the page loop
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        const int row = (rg * RTW + rt) * 16 + n;
+        if (j == 0) {
+            ml[(kg * 64 + row) * 2] = st.m[rt];
+            ml[(kg * 64 + row) * 2 + 1] = st.l[rt];
+        }
+        const float inv = st.l[rt] > 0.f ? 1.0f / st.l[rt] : 0.f;
+        unsigned char *orow = obuf + (size_t)(kg * 64 + row) * 512;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {                    // dims 64 j + 16 e + t, t = 0..15
+            uint4 a, b;
+            a.x = pack_f16x2(st.o[0][rt][e] * inv, st.o[1][rt][e] * inv);
+            a.y = pack_f16x2(st.o[2][rt][e] * inv, st.o[3][rt][e] * inv);
+            a.z = pack_f16x2(st.o[4][rt][e] * inv, st.o[5][rt][e] * inv);
+            a.w = pack_f16x2(st.o[6][rt][e] * inv, st.o[7][rt][e] * inv);
+            b.x = pack_f16x2(st.o[8][rt][e] * inv, st.o[9][rt][e] * inv);
+            b.y = pack_f16x2(st.o[10][rt][e] * inv, st.o[11][rt][e] * inv);
+            b.z = pack_f16x2(st.o[12][rt][e] * inv, st.o[13][rt][e] * inv);
+            b.w = pack_f16x2(st.o[14][rt][e] * inv, st.o[15][rt][e] * inv);
+            const int c0 = 8 * j + 2 * e;
+            *reinterpret_cast<uint4 *>(orow + ((c0 ^ n) * 16)) = a;
+            *reinterpret_cast<uint4 *>(orow + (((c0 + 1) ^ n) * 16)) = b;
+        }
+    }
+    __syncthreads();
+    const int tid = opaque_tid();
+    const int c = tid & 31;
+    const int nrows = min(lq * G, RT * 16);
+    for (int r = tid >> 5; r < nrows; r += 16) {
+        float mk[NG], lk[NG];
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+            mk[k] = ml[(k * 64 + r) * 2];
+            lk[k] = ml[(k * 64 + r) * 2 + 1];
+            M = fmaxf(M, lk[k] > 0.f ? mk[k] : -INFINITY);
+        }
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float W = 0.f;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+            const float w = lk[k] > 0.f ? lk[k] * exp2_fast(mk[k] - M) : 0.f;
+            W += w;
+            const uint4 v = *reinterpret_cast<const uint4 *>(obuf + (size_t)(k * 64 + r) * 512 +
+                                                             ((c ^ (r & 15)) * 16));
+            acc[0] += w * f16_lo(v.x);
+            acc[1] += w * f16_hi(v.x);
+            acc[2] += w * f16_lo(v.y);
+            acc[3] += w * f16_hi(v.y);
+            acc[4] += w * f16_lo(v.z);
+            acc[5] += w * f16_hi(v.z);
+            acc[6] += w * f16_lo(v.w);
+            acc[7] += w * f16_hi(v.w);
+        }
+        const int t = r >> p.log2g, h = r & (G - 1);
+        if (whole) {
+            const float sc = W > 0.f ? vd / W : 0.f;
+            uint4 o;
+            o.x = pack_bf16x2(acc[0] * sc, acc[1] * sc);
+            o.y = pack_bf16x2(acc[2] * sc, acc[3] * sc);
+            o.z = pack_bf16x2(acc[4] * sc, acc[5] * sc);
+            o.w = pack_bf16x2(acc[6] * sc, acc[7] * sc);
+            *reinterpret_cast<uint4 *>(p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + 8 * c) = o;
+        } else {
+            const float sc = W > 0.f ? 1.0f / W : 0.f;
+            uint4 o;
+            o.x = pack_f16x2(acc[0] * sc, acc[1] * sc);
+            o.y = pack_f16x2(acc[2] * sc, acc[3] * sc);
+            o.z = pack_f16x2(acc[4] * sc, acc[5] * sc);
+            o.w = pack_f16x2(acc[6] * sc, acc[7] * sc);
+            store_coherent(partial_rsrc(p), (int64_t)slot * p.rows_max + r, c, o);
+            if (c == 0)
+                store_coherent(p.ws_lse + (int64_t)slot * p.rows_max + r, W > 0.f ? M + __log2f(W) : -INFINITY);
+        }
+    }
+}
+
+// ------------------------------------------------------- segment reduce --
+//
+// In the FP8 kernel the workgroups that finish last merge the partials, so no
+// second kernel runs.  The S pieces of a (sequence, kv head) form groups of
+// GS = ceil(sqrt(S)) consecutive pieces.  A piece publishes its partial and
+// counts itself in its group's counter; the workgroup that completes a group
+// merges the group's partials into the group's first slot and counts the
+// group in the pair's counter; the workgroup that completes the pair merges
+// the group partials into the output rows.  Every counter is reset by the
+// workgroup that completes it, so all are zero again when the call ends.
+// Merges run in slot order, so the result does not depend on which
+// workgroup finishes last; and no workgroup reads more than about sqrt(S)
+// partials.
+//
+// Thread mapping: 32 threads per row, 8 dims each (16-byte accesses); a
+// thread takes rows r0, r0 + 16, r0 + 32, r0 + 48 and reads their partials 8
+// slots at a time with all loads of a round in flight.  Slots are slot0,
+// slot0 + stride, ...; the result goes to the output rows (out_slot < 0) or,
+// as a partial, to out_slot.
+__device__ __forceinline__ void reduce_pieces(const SplitParams &p, int slot0, int stride, int nslots, int nrows,
+                                              int q0, int g, float vd, int out_slot)
+{
+    constexpr int kRows = 4, kChunk = 8;
+    const int G = 1 << p.log2g;
+    const int tid = opaque_tid();
+    const int c = tid & 31;
+    const int r0 = tid >> 5;
+    const __amdgpu_buffer_rsrc_t rs = partial_rsrc(p);
+    float M[kRows], W[kRows], acc[kRows][8];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+        M[i] = -INFINITY;
+        W[i] = 0.f;
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+            acc[i][d] = 0.f;
+    }
+    for (int s0 = 0; s0 < nslots; s0 += kChunk) {
+        float l[kRows][kChunk];
+        uint4 v[kRows][kChunk];
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            const int r = r0 + 16 * i;
+#pragma unroll
+            for (int k = 0; k < kChunk; ++k) {
+                const bool in = r < nrows && s0 + k < nslots;
+                const int64_t sr = (int64_t)(slot0 + (s0 + k) * stride) * p.rows_max + r;
+                l[i][k] = in ? load_coherent(p.ws_lse + sr) : -INFINITY;
+                v[i][k] = in ? load_coherent(rs, sr, c) : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            float mc = l[i][0];
+#pragma unroll
+            for (int k = 1; k < kChunk; ++k)
+                mc = fmaxf(mc, l[i][k]);
+            if (mc > M[i]) {
+                const float f = M[i] == -INFINITY ? 0.f : exp2_fast(M[i] - mc);
+                W[i] *= f;
+#pragma unroll
+                for (int d = 0; d < 8; ++d)
+                    acc[i][d] *= f;
+                M[i] = mc;
+            }
+#pragma unroll
+            for (int k = 0; k < kChunk; ++k) {
+                const float w = l[i][k] == -INFINITY ? 0.f : exp2_fast(l[i][k] - M[i]);
+                W[i] += w;
+                acc[i][0] += w * f16_lo(v[i][k].x);
+                acc[i][1] += w * f16_hi(v[i][k].x);
+                acc[i][2] += w * f16_lo(v[i][k].y);
+                acc[i][3] += w * f16_hi(v[i][k].y);
+                acc[i][4] += w * f16_lo(v[i][k].z);
+                acc[i][5] += w * f16_hi(v[i][k].z);
+                acc[i][6] += w * f16_lo(v[i][k].w);
+                acc[i][7] += w * f16_hi(v[i][k].w);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+        const int r = r0 + 16 * i;
+        if (r >= nrows)
+            continue;
+        if (out_slot < 0) {
+            const int t = r >> p.log2g, h = r & (G - 1);
+            const float sc = W[i] > 0.f ? vd / W[i] : 0.f;
+            uint4 o;
+            o.x = pack_bf16x2(acc[i][0] * sc, acc[i][1] * sc);
+            o.y = pack_bf16x2(acc[i][2] * sc, acc[i][3] * sc);
+            o.z = pack_bf16x2(acc[i][4] * sc, acc[i][5] * sc);
+            o.w = pack_bf16x2(acc[i][6] * sc, acc[i][7] * sc);
+            *reinterpret_cast<uint4 *>(p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + 8 * c) = o;
+        } else {
+            const float sc = W[i] > 0.f ? 1.0f / W[i] : 0.f;
+            uint4 o;
+            o.x = pack_f16x2(acc[i][0] * sc, acc[i][1] * sc);
+            o.y = pack_f16x2(acc[i][2] * sc, acc[i][3] * sc);
+            o.z = pack_f16x2(acc[i][4] * sc, acc[i][5] * sc);
+            o.w = pack_f16x2(acc[i][6] * sc, acc[i][7] * sc);
+            const int64_t sr = (int64_t)out_slot * p.rows_max + r;
+            store_coherent(rs, sr, c, o);
+            if (c == 0)
+                store_coherent(p.ws_lse + sr, W[i] > 0.f ? M[i] + __log2f(W[i]) : -INFINITY);
+        }
+    }
+}
+
+// Count one arrival at `counter` (thread 0, agent scope) after every wave's
+// written-through partial stores have completed; true (uniform) for the
+// workgroup whose arrival makes the count reach `expected`, which also resets
+// the counter.  `flag` is a word of LDS free for the exchange.
+__device__ __forceinline__ bool arrive_last(int32_t *counter, int expected, int *flag)
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev == expected - 1;
+        if (last)
+            __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        flag[0] = last;
+    }
+    __syncthreads();
+    return flag[0] != 0;    // the next writer of flag passes a barrier first
+}
+
 // FP8 split-KV kernel, 8 waves (two per SIMD, so one wave's MFMA work runs
 // while the other's vector work issues).  The waves form 4 key groups x 2 row
 // groups: a wave holds RTW row tiles (row group rg) and computes every 4th
@@ -1394,9 +1399,7 @@ template <int RTW>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void va_split_kv_fp8_w8_kernel(SplitParams p)
 {
-    constexpr int NR = 2;
     constexpr int NG = 4;
-    constexpr int RT = RTW * NR;                             // row tiles per piece
     constexpr int kQBytes = kQf8Bytes;                      // fp8 hi/lo Q operands, 4 row tiles
     constexpr int kRingBytes = 2 * kStageBytes;              // per key group
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kQBytes + NG * kRingBytes];
@@ -1423,13 +1426,18 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
     unsigned char *ring = lds + kQBytes + kg * kRingBytes;
     const uint32_t ring_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(ring));
     const unsigned char *qw = lds + (size_t)rg * RTW * 2 * 2 * 64 * 32;
-    uint32_t off[4];
-    dma_lane_offsets(off, p.hkv, lane);
     const int64_t page_bytes = (int64_t)kPage * p.hkv * kHeadDim;
 
     const int bh = p.num_seqs * p.hkv;
     int s = sh.s, bg = sh.bg, base = sh.base;
     while (s < sh.e && bg < bh) {
+        // Per-lane values are rederived for each piece from an opaque lane
+        // index, so their address math is not hoisted above the piece loop
+        // (it would hold registers through the page loop and be spilled).
+        int pl = lane;
+        asm volatile("" : "+v"(pl));
+        uint32_t off[4];
+        dma_lane_offsets(off, p.hkv, pl);
         const int b = uniform(bg / p.hkv);
         const int g = bg - b * p.hkv;
         const int q0 = load_uniform(p.cu, b);
@@ -1464,13 +1472,30 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
             dma_step_part(ring_addr + stage * kStageBytes, pool, rg, ya, yb, page_bytes, off);
         };
 
-        __syncthreads();                                // previous piece's merge reads done
+        // ---- prologue: Q rows and the first two steps' pages are copied
+        // straight into LDS; the Q conversion overlaps the page copies.
+        __syncthreads();                                // previous piece's LDS reads done
+        const uint32_t lds_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(lds));
+        for (int i = wave; i < ((lq * G) >> 1); i += NG * 2) {        // row pairs: 1 KiB each
+            const int r = 2 * i;                               // rows r, r + 1 share a token (G even)
+            const int64_t row0 = uniform((int)((int64_t)(q0 + (r >> p.log2g)) * p.hq + g * G + (r & (G - 1))));
+            const int rr = r + (pl >> 5), slot = pl & 31;      // lane's LDS row and slot
+            dma16(p.q + row0 * kHeadDim, (uint32_t)((pl >> 5) * 512 + ((slot ^ (rr & 15)) * 16)), lds_addr + r * 512);
+        }
+        const bool has1 = kg + NG < npairs;
         if (kg < npairs)
-            issue(kg, 0);                              // first copy overlaps the Q staging
-
-        // ---- packed Q rows of this piece in LDS (fp8 hi/lo operands), row multipliers
+            issue(kg, 0);
+        if (has1)
+            issue(kg + NG, 1);
+        if (has1)
+            wait_vmcnt<2 * kDmaPerPart>();                  // this wave's Q copies landed
+        else if (kg < npairs)
+            wait_vmcnt<kDmaPerPart>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();                                // every wave's Q copies landed
         float crow[RTW];                                       // logit multiplier of this lane's row
-        stage_q_fp8<RTW>(lds, crow, c, p, q0, lq, g, rg, kg == 0, lane);
+        stage_q_fp8<RTW>(lds, crow, c, p, lq, rg, kg, pl);
 
         RowState<RTW> st;
 #pragma unroll
@@ -1484,34 +1509,70 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
         int limit[RTW];
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt) {
-            const int t = ((rg * RTW + rt) * 16 + (lane & 15)) >> p.log2g;
+            const int t = ((rg * RTW + rt) * 16 + (pl & 15)) >> p.log2g;
             limit[rt] = min(ctx + t, lk - 1);
         }
 
 
         for (int t = 0; t < nsteps; ++t) {
             const int k = kg + t * NG;
-            wait_vmcnt<0>();                                   // own copies of step t landed
-            __syncthreads();                                   // partner's too; stage t+1 is free
+            if (t == 0 && k + NG < npairs)
+                wait_vmcnt<kDmaPerPart>();                     // own copies of step 0 landed (step 1 may not)
+            else
+                wait_vmcnt<0>();                               // own copies of step t landed
+            __syncthreads();                                   // partner's too; stage of step t-1 is free
 
-            if (k + NG < npairs)
+            if (t >= 1 && k + NG < npairs)                     // steps 0 and 1 came with the prologue
                 issue(k + NG, (t + 1) & 1);
             if (k < npairs && rows_live) {
                 const unsigned char *stage = ring + (t & 1) * kStageBytes;
                 floatx4_t S[2][RTW];
-                qk_lds_f8<RTW>(S, stage, qw, lane);
+                qk_lds_f8<RTW>(S, stage, qw, pl);
                 const int pa = p0 + 2 * k;
                 const bool hb = pa + 1 < p1;
                 const int key0 = pa * kPage;
                 const bool masked = !hb || key0 + 31 > ctx;
                 bf16x8_t pop[RTW];
-                softmax_step<RTW>(st, pop, S, limit, key0, hb, crow, lane, masked);
-                pv_lds<RTW>(st, stage, pop, masked, masked ? v_zero_mask(key0, hb, lk, lane) : 0u, lane);
+                softmax_step<RTW>(st, pop, S, limit, key0, hb, crow, pl, masked);
+                pv_lds<RTW>(st, stage, pop, masked, masked ? v_zero_mask(key0, hb, lk, pl) : 0u, pl);
             }
         }
         wait_vmcnt<0>();
 
-        merge_and_write<RTW, NR, NG>(st, lds, p, kg, rg, lane, lq, q0, g, slot, whole, vd);
+        piece_epilogue<RTW>(st, lds, lds + kQBytes, p, kg, rg, pl, lq, q0, g, slot, whole, vd);
+
+        if (!whole) {                                          // uniform over the workgroup
+            // pieces of bg: workgroups w0 .. w1 (those holding its first and last page)
+            const int64_t N = sh.n_eff, P = sh.total;
+            const int w0 = (int)(((int64_t)(base + 1) * N - 1) / P);
+            const int w1 = (int)(((int64_t)(base + cnt) * N - 1) / P);
+            const int S = w1 - w0 + 1;
+            int GS = 2;
+            while (GS * GS < S)
+                ++GS;
+            const int ngroups = (S + GS - 1) / GS;
+            const int grp = (w - w0) / GS;
+            const int first = w0 + grp * GS + bg;              // slot of the group's first piece
+            const int gsize = min(GS, S - grp * GS);
+            const int nrows = min(lq * G, 2 * RTW * 16);
+            int *flag = reinterpret_cast<int *>(lds);
+            // Publishing: partials are written through (agent-scope stores)
+            // and every wave waits for their completion before the count
+            // moves; mergers read them with agent-scope loads.  No L2
+            // writeback or invalidate is needed (a release/acquire pair at
+            // agent scope would write back and invalidate a whole L2 per
+            // workgroup, which costs microseconds).
+            if (arrive_last(p.ws_count + first, gsize, flag)) {
+                if (ngroups == 1) {
+                    reduce_pieces(p, first, 1, gsize, nrows, q0, g, vd, -1);
+                } else {
+                    if (gsize > 1)
+                        reduce_pieces(p, first, 1, gsize, nrows, q0, g, vd, first);
+                    if (arrive_last(p.ws_count2 + bg, ngroups, flag))
+                        reduce_pieces(p, w0 + bg, GS, ngroups, nrows, q0, g, vd, -1);
+                }
+            }
+        }
 
         s = base + p1;
         base += cnt;
@@ -1522,6 +1583,18 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
 // Segment reduce.  One workgroup = 4 consecutive heads of one query token;
 // 64 threads per row, 4 dims each.  The partials of a row are read in chunks of
 // 8 slots with all loads of a chunk issued before any is used.
+template <bool kHalf>
+__device__ __forceinline__ float4 load_partial4(const void *base, int64_t idx)
+{
+    if constexpr (kHalf) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + idx);
+        return make_float4(f16_lo(u.x), f16_hi(u.x), f16_lo(u.y), f16_hi(u.y));
+    } else {
+        return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + idx);
+    }
+}
+
+template <bool kHalf>
 __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
 {
     constexpr int kChunk = 8;
@@ -1552,7 +1625,7 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
     const int row = (t << p.log2g) + h;
     const int d = (threadIdx.x & 63) * 4;
     const float *lse = p.ws_lse + (int64_t)(w0 + bg) * p.rows_max + row;
-    const float *o = p.ws_o + ((int64_t)(w0 + bg) * p.rows_max + row) * kHeadDim + d;
+    const int64_t o0 = ((int64_t)(w0 + bg) * p.rows_max + row) * kHeadDim + d;
     const int64_t lstride = p.rows_max;
     const int64_t ostride = (int64_t)p.rows_max * kHeadDim;
     const int ns = w1 - w0 + 1;
@@ -1577,7 +1650,7 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
             for (int i = 0; i < kChunk; ++i) {
                 const bool in = c0 + i < ns;
                 l[i] = in ? lse[(c0 + i) * lstride] : -INFINITY;
-                v[i] = in ? *reinterpret_cast<const float4 *>(o + (c0 + i) * ostride)
+                v[i] = in ? load_partial4<kHalf>(p.ws_o, o0 + (c0 + i) * ostride)
                           : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
@@ -1598,6 +1671,13 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
     pk.y = pack_bf16x2(acc.z * inv, acc.w * inv);
     const int G = 1 << p.log2g;
     *reinterpret_cast<uint2 *>(p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + d) = pk;
+}
+
+__global__ __launch_bounds__(kThreads) void va_zero_kernel(int32_t *p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n)
+        p[i] = 0;
 }
 
 __global__ __launch_bounds__(kThreads) void va_fp8_to_bf16_kernel(const uint8_t *in, uint16_t *out, int64_t n)
@@ -1627,12 +1707,6 @@ void launch_split(SplitParams p, int grid, hipStream_t s)
 }
 
 typedef void (*launch_fn)(SplitParams, int, hipStream_t);
-
-template <int RTW, int NR>
-void launch_fp8(SplitParams p, int grid, hipStream_t s)
-{
-    hipLaunchKernelGGL((va_split_kv_fp8_kernel<RTW, NR>), dim3(grid), dim3(kThreads), 0, s, p);
-}
 
 template <int RTW>
 void launch_fp8_w8(SplitParams p, int grid, hipStream_t s)
@@ -1668,7 +1742,8 @@ struct va_plan_s {
     int min_pages;
     int rows_max;
     int64_t slots;
-    size_t off_prefix, off_lse, off_o, ws_bytes;
+    size_t off_count, off_count2, off_prefix, off_lse, off_o, ws_bytes;
+    bool fused_reduce;  // the main kernel also reduces the segments (FP8 cache)
 };
 
 extern "C" {
@@ -1712,6 +1787,8 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
         return VA_ERR_UNSUPPORTED;
     if (p.max_seqlen_q > 4)
         return VA_ERR_UNSUPPORTED;
+    if (p.total_q * (int64_t)p.num_q_heads >= INT32_MAX)    // q rows are indexed with 32-bit integers
+        return VA_ERR_UNSUPPORTED;
     const int64_t bh = (int64_t)p.num_seqs * p.num_kv_heads;
     if (bh > 65536 || bh * (int64_t)p.max_blocks_per_seq > INT32_MAX)
         return VA_ERR_UNSUPPORTED;
@@ -1745,13 +1822,23 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     pl->grid = p.force_grid > 0 ? p.force_grid : cus;
     pl->min_pages = 8;
     pl->slots = (int64_t)pl->grid + bh;
+    pl->fused_reduce = p.kv_dtype == VA_DT_FP8_E4M3FN;
     size_t off = 256;                                   // meta
+    pl->off_count = off;
+    off = align_up(off + (size_t)pl->slots * 4, 256);
+    pl->off_count2 = off;
+    off = align_up(off + (size_t)bh * 4, 256);
     pl->off_prefix = off;
     off = align_up(off + (size_t)(bh + 1) * 4, 256);
     pl->off_lse = off;
     off = align_up(off + (size_t)pl->slots * pl->rows_max * 4, 256);
     pl->off_o = off;
-    off = align_up(off + (size_t)pl->slots * pl->rows_max * kHeadDim * 4, 256);
+    const size_t part_elt = p.kv_dtype == VA_DT_FP8_E4M3FN ? 2 : 4;   // fp16 or fp32 partial O
+    off = align_up(off + (size_t)pl->slots * pl->rows_max * kHeadDim * part_elt, 256);
+    if (off - pl->off_o > (size_t)INT32_MAX) {          // partials are addressed with 32-bit offsets
+        delete pl;
+        return VA_ERR_UNSUPPORTED;
+    }
     pl->ws_bytes = off;
     *out = pl;
     return VA_OK;
@@ -1813,9 +1900,12 @@ va_status va_run_stage(va_plan_t plan, int32_t stage, const void *q, const void 
         sp.kdesc = k_descale;
         sp.vdesc = v_descale;
         sp.out = static_cast<uint16_t *>(out);
-        sp.ws_o = reinterpret_cast<float *>(ws + plan->off_o);
+        sp.ws_o = ws + plan->off_o;
+        sp.ws_o_bytes = (int32_t)(plan->ws_bytes - plan->off_o);
         sp.ws_lse = reinterpret_cast<float *>(ws + plan->off_lse);
         sp.ws_prefix = reinterpret_cast<int32_t *>(ws + plan->off_prefix);
+        sp.ws_count = reinterpret_cast<int32_t *>(ws + plan->off_count);
+        sp.ws_count2 = reinterpret_cast<int32_t *>(ws + plan->off_count2);
         sp.ws_meta = reinterpret_cast<int32_t *>(ws);
         sp.scale_log2 = softmax_scale * 1.4426950408889634f;
         sp.num_seqs = pr.num_seqs;
@@ -1833,11 +1923,11 @@ va_status va_run_stage(va_plan_t plan, int32_t stage, const void *q, const void 
         if (hipGetLastError() != hipSuccess)
             return VA_ERR_HIP;
     }
-    if (stage == VA_STAGE_ALL || stage == VA_STAGE_MERGE) {
+    if ((stage == VA_STAGE_ALL || stage == VA_STAGE_MERGE) && !plan->fused_reduce) {
         MergeParams mp;
         mp.cu = cu_seqlens_q;
         mp.vdesc = v_descale;
-        mp.ws_o = reinterpret_cast<const float *>(ws + plan->off_o);
+        mp.ws_o = ws + plan->off_o;
         mp.ws_lse = reinterpret_cast<const float *>(ws + plan->off_lse);
         mp.ws_prefix = reinterpret_cast<const int32_t *>(ws + plan->off_prefix);
         mp.ws_meta = reinterpret_cast<const int32_t *>(ws);
@@ -1851,7 +1941,10 @@ va_status va_run_stage(va_plan_t plan, int32_t stage, const void *q, const void 
         const int64_t blocks = (int64_t)pr.num_seqs * pr.num_kv_heads * pr.max_seqlen_q *
                                ((pr.num_q_heads / pr.num_kv_heads) / 4);
         if (blocks > 0) {
-            hipLaunchKernelGGL(va_merge_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, mp);
+            if (pr.kv_dtype == VA_DT_FP8_E4M3FN)
+                hipLaunchKernelGGL(va_merge_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s, mp);
+            else
+                hipLaunchKernelGGL(va_merge_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, s, mp);
             if (hipGetLastError() != hipSuccess)
                 return VA_ERR_HIP;
         }
@@ -1868,6 +1961,22 @@ va_status va_run(va_plan_t plan, const void *q, const void *k_pool, const void *
     return va_run_stage(plan, VA_STAGE_ALL, q, k_pool, v_pool, block_table, cu_seqlens_q,
                         seqused_k, softmax_scale, k_descale, v_descale, out, workspace,
                         workspace_bytes, stream);
+}
+
+va_status va_workspace_init(va_plan_t plan, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!plan)
+        return VA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < plan->ws_bytes)
+        return VA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+        return VA_ERR_INVALID_ARG;
+    // the metadata word and the per-(sequence, kv head) piece counters
+    const int64_t n = (int64_t)(plan->off_prefix / 4);
+    const int64_t blocks = (n + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(va_zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), static_cast<int32_t *>(workspace), n);
+    return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
 va_status va_fp8_to_bf16(const uint8_t *in, uint16_t *out, int64_t n, void *stream)
