@@ -109,19 +109,6 @@ va_status va_plan(const va_problem *problem, va_plan_t *out);
 /* Bytes of device workspace va_run needs for this plan. */
 va_status va_plan_workspace_bytes(va_plan_t plan, size_t *bytes);
 
-/*
- * Prepare a newly allocated workspace: enqueue one small kernel on `stream`
- * that zeroes its counter area (the per-(sequence, kv head) piece counters
- * used by the FP8 kernel's in-kernel segment reduce).  Call it once after
- * allocating a workspace, or zero the whole buffer instead; every completed
- * va_run leaves the counters at zero again, so a workspace stays ready for the
- * next call.  It does not use hipMemset, so it may be captured in a graph.
- * Errors: VA_ERR_INVALID_ARG (null plan, misaligned workspace),
- * VA_ERR_WORKSPACE (null or short workspace), VA_ERR_HIP (launch failure).
- */
-va_status va_workspace_init(va_plan_t plan, void *workspace, size_t workspace_bytes,
-                            void *stream);
-
 /* Number of split-KV workgroups the plan launches (after force_grid). */
 va_status va_plan_grid(va_plan_t plan, int32_t *grid);
 
@@ -140,14 +127,10 @@ va_status va_plan_grid(va_plan_t plan, int32_t *grid);
  *   k_descale, v_descale  device pointers to one float each, or NULL for 1.0
  *   out          [total_q, Hq, 256] bf16, written for every query row
  *   workspace    device buffer of >= va_plan_workspace_bytes bytes, 256-byte
- *                aligned, prepared once with va_workspace_init (or zero-filled);
- *                a call leaves it prepared.  Calls that overlap in time must
- *                use different workspaces.
- * All device pointers must be 16-byte aligned.  Returns VA_OK once the work
- * is enqueued: for an FP8 cache one kernel (the main kernel reduces the
- * segments itself: the last workgroup to finish a piece of a (sequence, kv
- * head) merges that pair's partials), for a bf16 cache the main kernel and
- * the segment-reduce kernel.
+ *                aligned; its contents need not be initialised.  Calls that
+ *                overlap in time must use different workspaces.
+ * All device pointers must be 16-byte aligned.  Returns VA_OK once both kernels
+ * (split-KV main kernel, segment reduce) are enqueued.
  */
 va_status va_run(va_plan_t plan, const void *q, const void *k_pool, const void *v_pool,
                  const int32_t *block_table, const int32_t *cu_seqlens_q,
@@ -159,12 +142,9 @@ va_status va_run(va_plan_t plan, const void *q, const void *k_pool, const void *
  * The kernels of va_run, enqueued one at a time (same arguments).
  *   stage VA_STAGE_SPLIT_KV: the split-KV main kernel.  It writes the per-segment
  *                            partials to the workspace, and writes rows whose
- *                            sequence fits one segment straight to out.  For an
- *                            FP8 cache it also reduces the segments, so this
- *                            stage alone writes every row.
+ *                            sequence fits one segment straight to out.
  *   stage VA_STAGE_MERGE:    the segment-reduce kernel; it reads the partials and
- *                            writes the remaining rows of out.  For an FP8 cache
- *                            it enqueues nothing.
+ *                            writes the remaining rows of out.
  * VA_STAGE_MERGE must follow VA_STAGE_SPLIT_KV of the same call on the same
  * stream (with the same workspace).  va_run == SPLIT_KV then MERGE.  These exist
  * so a caller can time or profile each kernel on its own stream.

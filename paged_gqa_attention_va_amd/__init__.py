@@ -26,7 +26,7 @@ VA_OK, VA_ERR_INVALID_ARG, VA_ERR_UNSUPPORTED, VA_ERR_WORKSPACE, VA_ERR_HIP = ra
 VA_DT_BF16, VA_DT_FP8_E4M3FN = 1, 2
 VA_STAGE_ALL, VA_STAGE_SPLIT_KV, VA_STAGE_MERGE = 0, 1, 2
 
-EXPORTED = ("va_plan", "va_plan_workspace_bytes", "va_workspace_init", "va_plan_grid", "va_run", "va_run_stage",
+EXPORTED = ("va_plan", "va_plan_workspace_bytes", "va_plan_grid", "va_run", "va_run_stage",
             "va_plan_destroy", "va_status_str", "va_fp8_to_bf16")
 
 _lib = None
@@ -75,8 +75,6 @@ def library(path: str = LIB_PATH):
     lib.va_plan_destroy.argtypes = [P]
     lib.va_status_str.restype = ctypes.c_char_p
     lib.va_status_str.argtypes = [ctypes.c_int]
-    lib.va_workspace_init.restype = ctypes.c_int
-    lib.va_workspace_init.argtypes = [P, P, ctypes.c_size_t, P]
     lib.va_fp8_to_bf16.restype = ctypes.c_int
     lib.va_fp8_to_bf16.argtypes = [P, P, ctypes.c_int64, P]
     if path == LIB_PATH:
@@ -142,17 +140,9 @@ class Plan:
                    max_blocks_per_seq=int(p.block_table.shape[1]), num_blocks=p.num_blocks,
                    total_q=p.total_q, kv_dtype=p.kv_dtype, **kw)
 
-    def workspace(self, device=None, stream=None):
-        """A new device workspace, prepared with va_workspace_init on ``stream``."""
+    def workspace(self, device=None):
         import torch
-        ws = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=device or "cuda")
-        if stream is None:
-            stream = torch.cuda.current_stream(ws.device)
-        sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-        _check(self._lib.va_workspace_init(self._h, ctypes.c_void_p(ws.data_ptr()),
-                                           ctypes.c_size_t(self.workspace_bytes),
-                                           ctypes.c_void_p(sptr)), "va_workspace_init")
-        return ws
+        return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=device or "cuda")
 
     def run(self, q, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k, softmax_scale: float,
             k_descale=None, v_descale=None, out=None, workspace=None, stream=None,

@@ -74,12 +74,9 @@ struct SplitParams {
     const float *vdesc;
     uint16_t *out;
     void *ws_o;           // [slots][rows_max][256]: fp16 (FP8 cache) or fp32 (bf16 cache)
-    int32_t ws_o_bytes;   // size of the ws_o region
     float *ws_lse;        // [slots][rows_max]   log2-domain LSE of the scaled logits
     int32_t *ws_prefix;   // [BH + 1] exclusive prefix of page counts, [BH] = total
     int32_t *ws_meta;     // [0] = workgroups in use
-    int32_t *ws_count;    // [slots] pieces of a group finished, at the group's first slot; zero between calls
-    int32_t *ws_count2;   // [BH] groups of a (sequence, kv head) finished; zero between calls
     float scale_log2;     // softmax_scale * log2(e)
     int32_t num_seqs, hq, hkv, log2g, mbps, grid_n, min_pages, rows_max;
     int64_t num_blocks;
@@ -1106,46 +1103,6 @@ __device__ __forceinline__ int opaque_tid()
     return t;
 }
 
-// Partials cross workgroups that may sit on different XCDs, whose L2 caches
-// are not coherent with each other.  They are written and read with
-// agent-scope relaxed atomic accesses (the sc1 cache policy: written through
-// to, and read from, the device's point of coherence), so no L2 writeback or
-// invalidate is needed; the piece counter orders them (see the FP8 kernel).
-typedef unsigned int uintx4_t __attribute__((ext_vector_type(4)));
-constexpr int kCoherent = 16;           // buffer cache policy bit sc1: agent-scope coherent access
-
-// Buffer resource over the partial O region (raw, byte offsets; an access
-// past num_records reads zero instead of faulting).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const SplitParams &p)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(p.ws_o, 0, p.ws_o_bytes, 0x00020000);
-}
-
-// 8 fp16 of row sr (slot * rows_max + row), dims 8c .. 8c+7.
-__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, int64_t sr, int c, uint4 v)
-{
-    __builtin_amdgcn_raw_buffer_store_b128(uintx4_t{v.x, v.y, v.z, v.w}, r, (int)((sr * kHeadDim + 8 * c) * 2), 0,
-                                           kCoherent);
-}
-
-__device__ __forceinline__ uint4 load_coherent(__amdgpu_buffer_rsrc_t r, int64_t sr, int c)
-{
-    const uintx4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)((sr * kHeadDim + 8 * c) * 2), 0, kCoherent);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ void store_coherent(float *dst, float v)
-{
-    __hip_atomic_store(reinterpret_cast<uint32_t *>(dst), __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float load_coherent(const float *src)
-{
-    return __builtin_bit_cast(float, __hip_atomic_load(reinterpret_cast<const uint32_t *>(src), __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT));
-}
-
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b)
 {
     typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -1252,139 +1209,12 @@ __device__ __forceinline__ void piece_epilogue(RowState<RTW> &st, unsigned char 
             o.y = pack_f16x2(acc[2] * sc, acc[3] * sc);
             o.z = pack_f16x2(acc[4] * sc, acc[5] * sc);
             o.w = pack_f16x2(acc[6] * sc, acc[7] * sc);
-            store_coherent(partial_rsrc(p), (int64_t)slot * p.rows_max + r, c, o);
+            uint16_t *dst = static_cast<uint16_t *>(p.ws_o) + ((int64_t)slot * p.rows_max + r) * kHeadDim + 8 * c;
+            *reinterpret_cast<uint4 *>(dst) = o;
             if (c == 0)
-                store_coherent(p.ws_lse + (int64_t)slot * p.rows_max + r, W > 0.f ? M + __log2f(W) : -INFINITY);
+                p.ws_lse[(int64_t)slot * p.rows_max + r] = W > 0.f ? M + __log2f(W) : -INFINITY;
         }
     }
-}
-
-// ------------------------------------------------------- segment reduce --
-//
-// In the FP8 kernel the workgroups that finish last merge the partials, so no
-// second kernel runs.  The S pieces of a (sequence, kv head) form groups of
-// GS = ceil(sqrt(S)) consecutive pieces.  A piece publishes its partial and
-// counts itself in its group's counter; the workgroup that completes a group
-// merges the group's partials into the group's first slot and counts the
-// group in the pair's counter; the workgroup that completes the pair merges
-// the group partials into the output rows.  Every counter is reset by the
-// workgroup that completes it, so all are zero again when the call ends.
-// Merges run in slot order, so the result does not depend on which
-// workgroup finishes last; and no workgroup reads more than about sqrt(S)
-// partials.
-//
-// Thread mapping: 32 threads per row, 8 dims each (16-byte accesses); a
-// thread takes rows r0, r0 + 16, r0 + 32, r0 + 48 and reads their partials 8
-// slots at a time with all loads of a round in flight.  Slots are slot0,
-// slot0 + stride, ...; the result goes to the output rows (out_slot < 0) or,
-// as a partial, to out_slot.
-__device__ __forceinline__ void reduce_pieces(const SplitParams &p, int slot0, int stride, int nslots, int nrows,
-                                              int q0, int g, float vd, int out_slot)
-{
-    constexpr int kRows = 4, kChunk = 8;
-    const int G = 1 << p.log2g;
-    const int tid = opaque_tid();
-    const int c = tid & 31;
-    const int r0 = tid >> 5;
-    const __amdgpu_buffer_rsrc_t rs = partial_rsrc(p);
-    float M[kRows], W[kRows], acc[kRows][8];
-#pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-        M[i] = -INFINITY;
-        W[i] = 0.f;
-#pragma unroll
-        for (int d = 0; d < 8; ++d)
-            acc[i][d] = 0.f;
-    }
-    for (int s0 = 0; s0 < nslots; s0 += kChunk) {
-        float l[kRows][kChunk];
-        uint4 v[kRows][kChunk];
-#pragma unroll
-        for (int i = 0; i < kRows; ++i) {
-            const int r = r0 + 16 * i;
-#pragma unroll
-            for (int k = 0; k < kChunk; ++k) {
-                const bool in = r < nrows && s0 + k < nslots;
-                const int64_t sr = (int64_t)(slot0 + (s0 + k) * stride) * p.rows_max + r;
-                l[i][k] = in ? load_coherent(p.ws_lse + sr) : -INFINITY;
-                v[i][k] = in ? load_coherent(rs, sr, c) : make_uint4(0, 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < kRows; ++i) {
-            float mc = l[i][0];
-#pragma unroll
-            for (int k = 1; k < kChunk; ++k)
-                mc = fmaxf(mc, l[i][k]);
-            if (mc > M[i]) {
-                const float f = M[i] == -INFINITY ? 0.f : exp2_fast(M[i] - mc);
-                W[i] *= f;
-#pragma unroll
-                for (int d = 0; d < 8; ++d)
-                    acc[i][d] *= f;
-                M[i] = mc;
-            }
-#pragma unroll
-            for (int k = 0; k < kChunk; ++k) {
-                const float w = l[i][k] == -INFINITY ? 0.f : exp2_fast(l[i][k] - M[i]);
-                W[i] += w;
-                acc[i][0] += w * f16_lo(v[i][k].x);
-                acc[i][1] += w * f16_hi(v[i][k].x);
-                acc[i][2] += w * f16_lo(v[i][k].y);
-                acc[i][3] += w * f16_hi(v[i][k].y);
-                acc[i][4] += w * f16_lo(v[i][k].z);
-                acc[i][5] += w * f16_hi(v[i][k].z);
-                acc[i][6] += w * f16_lo(v[i][k].w);
-                acc[i][7] += w * f16_hi(v[i][k].w);
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-        const int r = r0 + 16 * i;
-        if (r >= nrows)
-            continue;
-        if (out_slot < 0) {
-            const int t = r >> p.log2g, h = r & (G - 1);
-            const float sc = W[i] > 0.f ? vd / W[i] : 0.f;
-            uint4 o;
-            o.x = pack_bf16x2(acc[i][0] * sc, acc[i][1] * sc);
-            o.y = pack_bf16x2(acc[i][2] * sc, acc[i][3] * sc);
-            o.z = pack_bf16x2(acc[i][4] * sc, acc[i][5] * sc);
-            o.w = pack_bf16x2(acc[i][6] * sc, acc[i][7] * sc);
-            *reinterpret_cast<uint4 *>(p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + 8 * c) = o;
-        } else {
-            const float sc = W[i] > 0.f ? 1.0f / W[i] : 0.f;
-            uint4 o;
-            o.x = pack_f16x2(acc[i][0] * sc, acc[i][1] * sc);
-            o.y = pack_f16x2(acc[i][2] * sc, acc[i][3] * sc);
-            o.z = pack_f16x2(acc[i][4] * sc, acc[i][5] * sc);
-            o.w = pack_f16x2(acc[i][6] * sc, acc[i][7] * sc);
-            const int64_t sr = (int64_t)out_slot * p.rows_max + r;
-            store_coherent(rs, sr, c, o);
-            if (c == 0)
-                store_coherent(p.ws_lse + sr, W[i] > 0.f ? M[i] + __log2f(W[i]) : -INFINITY);
-        }
-    }
-}
-
-// Count one arrival at `counter` (thread 0, agent scope) after every wave's
-// written-through partial stores have completed; true (uniform) for the
-// workgroup whose arrival makes the count reach `expected`, which also resets
-// the counter.  `flag` is a word of LDS free for the exchange.
-__device__ __forceinline__ bool arrive_last(int32_t *counter, int expected, int *flag)
-{
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = prev == expected - 1;
-        if (last)
-            __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        flag[0] = last;
-    }
-    __syncthreads();
-    return flag[0] != 0;    // the next writer of flag passes a barrier first
 }
 
 // FP8 split-KV kernel, 8 waves (two per SIMD, so one wave's MFMA work runs
@@ -1541,38 +1371,6 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
 
         piece_epilogue<RTW>(st, lds, lds + kQBytes, p, kg, rg, pl, lq, q0, g, slot, whole, vd);
 
-        if (!whole) {                                          // uniform over the workgroup
-            // pieces of bg: workgroups w0 .. w1 (those holding its first and last page)
-            const int64_t N = sh.n_eff, P = sh.total;
-            const int w0 = (int)(((int64_t)(base + 1) * N - 1) / P);
-            const int w1 = (int)(((int64_t)(base + cnt) * N - 1) / P);
-            const int S = w1 - w0 + 1;
-            int GS = 2;
-            while (GS * GS < S)
-                ++GS;
-            const int ngroups = (S + GS - 1) / GS;
-            const int grp = (w - w0) / GS;
-            const int first = w0 + grp * GS + bg;              // slot of the group's first piece
-            const int gsize = min(GS, S - grp * GS);
-            const int nrows = min(lq * G, 2 * RTW * 16);
-            int *flag = reinterpret_cast<int *>(lds);
-            // Publishing: partials are written through (agent-scope stores)
-            // and every wave waits for their completion before the count
-            // moves; mergers read them with agent-scope loads.  No L2
-            // writeback or invalidate is needed (a release/acquire pair at
-            // agent scope would write back and invalidate a whole L2 per
-            // workgroup, which costs microseconds).
-            if (arrive_last(p.ws_count + first, gsize, flag)) {
-                if (ngroups == 1) {
-                    reduce_pieces(p, first, 1, gsize, nrows, q0, g, vd, -1);
-                } else {
-                    if (gsize > 1)
-                        reduce_pieces(p, first, 1, gsize, nrows, q0, g, vd, first);
-                    if (arrive_last(p.ws_count2 + bg, ngroups, flag))
-                        reduce_pieces(p, w0 + bg, GS, ngroups, nrows, q0, g, vd, -1);
-                }
-            }
-        }
 
         s = base + p1;
         base += cnt;
@@ -1597,7 +1395,7 @@ __device__ __forceinline__ float4 load_partial4(const void *base, int64_t idx)
 template <bool kHalf>
 __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
 {
-    constexpr int kChunk = 8;
+    constexpr int kChunk = 16;
     const int gq = (1 << p.log2g) >> 2;               // head quads per group
     int idx = blockIdx.x;
     const int hq4 = idx % gq;
@@ -1630,38 +1428,41 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
     const int64_t ostride = (int64_t)p.rows_max * kHeadDim;
     const int ns = w1 - w0 + 1;
 
+    // One pass over the slots, kChunk at a time with every load of a chunk in
+    // flight; the running max moves per chunk (the sum is rescaled then).
     float mx = -INFINITY;
-    for (int c0 = 0; c0 < ns; c0 += kChunk) {
-        float l[kChunk];
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i)
-            l[i] = c0 + i < ns ? lse[(c0 + i) * lstride] : -INFINITY;
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i)
-            mx = fmaxf(mx, l[i]);
-    }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float den = 0.f;
-    if (mx > -INFINITY) {
-        for (int c0 = 0; c0 < ns; c0 += kChunk) {
-            float l[kChunk];
-            float4 v[kChunk];
+    for (int c0 = 0; c0 < ns; c0 += kChunk) {
+        float l[kChunk];
+        float4 v[kChunk];
 #pragma unroll
-            for (int i = 0; i < kChunk; ++i) {
-                const bool in = c0 + i < ns;
-                l[i] = in ? lse[(c0 + i) * lstride] : -INFINITY;
-                v[i] = in ? load_partial4<kHalf>(p.ws_o, o0 + (c0 + i) * ostride)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+        for (int i = 0; i < kChunk; ++i) {
+            const bool in = c0 + i < ns;
+            l[i] = in ? lse[(c0 + i) * lstride] : -INFINITY;
+            v[i] = in ? load_partial4<kHalf>(p.ws_o, o0 + (c0 + i) * ostride) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float mc = l[0];
 #pragma unroll
-            for (int i = 0; i < kChunk; ++i) {
-                const float f = l[i] == -INFINITY ? 0.f : exp2_fast(l[i] - mx);
-                den += f;
-                acc.x += f * v[i].x;
-                acc.y += f * v[i].y;
-                acc.z += f * v[i].z;
-                acc.w += f * v[i].w;
-            }
+        for (int i = 1; i < kChunk; ++i)
+            mc = fmaxf(mc, l[i]);
+        if (mc > mx) {
+            const float f = mx == -INFINITY ? 0.f : exp2_fast(mx - mc);
+            den *= f;
+            acc.x *= f;
+            acc.y *= f;
+            acc.z *= f;
+            acc.w *= f;
+            mx = mc;
+        }
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            const float f = l[i] == -INFINITY ? 0.f : exp2_fast(l[i] - mx);
+            den += f;
+            acc.x += f * v[i].x;
+            acc.y += f * v[i].y;
+            acc.z += f * v[i].z;
+            acc.w += f * v[i].w;
         }
     }
     const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
@@ -1671,13 +1472,6 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
     pk.y = pack_bf16x2(acc.z * inv, acc.w * inv);
     const int G = 1 << p.log2g;
     *reinterpret_cast<uint2 *>(p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + d) = pk;
-}
-
-__global__ __launch_bounds__(kThreads) void va_zero_kernel(int32_t *p, int64_t n)
-{
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i < n)
-        p[i] = 0;
 }
 
 __global__ __launch_bounds__(kThreads) void va_fp8_to_bf16_kernel(const uint8_t *in, uint16_t *out, int64_t n)
@@ -1742,8 +1536,7 @@ struct va_plan_s {
     int min_pages;
     int rows_max;
     int64_t slots;
-    size_t off_count, off_count2, off_prefix, off_lse, off_o, ws_bytes;
-    bool fused_reduce;  // the main kernel also reduces the segments (FP8 cache)
+    size_t off_prefix, off_lse, off_o, ws_bytes;
 };
 
 extern "C" {
@@ -1822,12 +1615,7 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     pl->grid = p.force_grid > 0 ? p.force_grid : cus;
     pl->min_pages = 8;
     pl->slots = (int64_t)pl->grid + bh;
-    pl->fused_reduce = p.kv_dtype == VA_DT_FP8_E4M3FN;
     size_t off = 256;                                   // meta
-    pl->off_count = off;
-    off = align_up(off + (size_t)pl->slots * 4, 256);
-    pl->off_count2 = off;
-    off = align_up(off + (size_t)bh * 4, 256);
     pl->off_prefix = off;
     off = align_up(off + (size_t)(bh + 1) * 4, 256);
     pl->off_lse = off;
@@ -1835,10 +1623,7 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     pl->off_o = off;
     const size_t part_elt = p.kv_dtype == VA_DT_FP8_E4M3FN ? 2 : 4;   // fp16 or fp32 partial O
     off = align_up(off + (size_t)pl->slots * pl->rows_max * kHeadDim * part_elt, 256);
-    if (off - pl->off_o > (size_t)INT32_MAX) {          // partials are addressed with 32-bit offsets
-        delete pl;
-        return VA_ERR_UNSUPPORTED;
-    }
+
     pl->ws_bytes = off;
     *out = pl;
     return VA_OK;
@@ -1901,11 +1686,8 @@ va_status va_run_stage(va_plan_t plan, int32_t stage, const void *q, const void 
         sp.vdesc = v_descale;
         sp.out = static_cast<uint16_t *>(out);
         sp.ws_o = ws + plan->off_o;
-        sp.ws_o_bytes = (int32_t)(plan->ws_bytes - plan->off_o);
         sp.ws_lse = reinterpret_cast<float *>(ws + plan->off_lse);
         sp.ws_prefix = reinterpret_cast<int32_t *>(ws + plan->off_prefix);
-        sp.ws_count = reinterpret_cast<int32_t *>(ws + plan->off_count);
-        sp.ws_count2 = reinterpret_cast<int32_t *>(ws + plan->off_count2);
         sp.ws_meta = reinterpret_cast<int32_t *>(ws);
         sp.scale_log2 = softmax_scale * 1.4426950408889634f;
         sp.num_seqs = pr.num_seqs;
@@ -1923,7 +1705,7 @@ va_status va_run_stage(va_plan_t plan, int32_t stage, const void *q, const void 
         if (hipGetLastError() != hipSuccess)
             return VA_ERR_HIP;
     }
-    if ((stage == VA_STAGE_ALL || stage == VA_STAGE_MERGE) && !plan->fused_reduce) {
+    if (stage == VA_STAGE_ALL || stage == VA_STAGE_MERGE) {
         MergeParams mp;
         mp.cu = cu_seqlens_q;
         mp.vdesc = v_descale;
@@ -1961,22 +1743,6 @@ va_status va_run(va_plan_t plan, const void *q, const void *k_pool, const void *
     return va_run_stage(plan, VA_STAGE_ALL, q, k_pool, v_pool, block_table, cu_seqlens_q,
                         seqused_k, softmax_scale, k_descale, v_descale, out, workspace,
                         workspace_bytes, stream);
-}
-
-va_status va_workspace_init(va_plan_t plan, void *workspace, size_t workspace_bytes, void *stream)
-{
-    if (!plan)
-        return VA_ERR_INVALID_ARG;
-    if (!workspace || workspace_bytes < plan->ws_bytes)
-        return VA_ERR_WORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
-        return VA_ERR_INVALID_ARG;
-    // the metadata word and the per-(sequence, kv head) piece counters
-    const int64_t n = (int64_t)(plan->off_prefix / 4);
-    const int64_t blocks = (n + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(va_zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       reinterpret_cast<hipStream_t>(stream), static_cast<int32_t *>(workspace), n);
-    return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
 va_status va_fp8_to_bf16(const uint8_t *in, uint16_t *out, int64_t n, void *stream)
