@@ -108,8 +108,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first (the clocks settle over the first ~100)")
+    ap.add_argument("--warmup", type=int, default=200, help="untimed steps before timing")
+    ap.add_argument("--warmup-seconds", type=float, default=3.0,
+                    help="keep running untimed steps for at least this long (memory and core "
+                         "clocks take about a second of sustained load to settle)")
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = the headline)")
     ap.add_argument("--variant", type=int, default=0, help="sweep variant of workload 4")
     ap.add_argument("--copies", type=int, default=4, help="KV pool copies to rotate over")
@@ -200,12 +202,17 @@ def main():
     if args.stage == "merge":      # the merge reads what a split pass left in the workspace
         plan.run(q, ks[0], vs[0], bt, cu, sk, p.scale, kd, vd, out=out, workspace=ws,
                  stream=stream, stage=va.VA_STAGE_SPLIT_KV)
-    for i in range(args.warmup):
-        step(i)
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
+        step(n_warm)
+        n_warm += 1
+        if n_warm % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    log(f"bench: {args.warmup} warmup steps done")
+    log(f"bench: {n_warm} warmup steps done in {time.perf_counter() - t_w:.1f} s")
 
-    ms_step = timed(args.steps, args.warmup)
+    ms_step = timed(args.steps, n_warm)
     alg = algorithmic_bytes(p)
     value = alg / (ms_step * 1e-3) / 1e9
     log(f"bench: {args.steps} steps, {ms_step * 1e3:.2f} us/step, {value:.1f} GB/s effective")
@@ -216,7 +223,7 @@ def main():
         if stages == (va.VA_STAGE_SPLIT_KV,):
             main_ms = ms_step
         else:
-            main_ms = timed(args.steps, args.warmup, (va.VA_STAGE_SPLIT_KV,))
+            main_ms = timed(args.steps, n_warm, (va.VA_STAGE_SPLIT_KV,))
         achieved = alg / (main_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),

@@ -1404,17 +1404,19 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
     const int bg = idx / p.max_q;
     const int b = bg / p.hkv;
     const int g = bg - b * p.hkv;
-    const int q0 = load_uniform(p.cu, b);
-    const int lq = load_uniform(p.cu, b + 1) - q0;
-    if (t >= lq)
-        return;
     const int bh = p.num_seqs * p.hkv;
+    // every metadata word is loaded before any is used: one round trip
+    const int q0 = load_uniform(p.cu, b);
+    const int q1 = load_uniform(p.cu, b + 1);
     const int s = load_uniform(p.ws_prefix, bg);
     const int e = load_uniform(p.ws_prefix, bg + 1);
     const int total = load_uniform(p.ws_prefix, bh);
-    if (e <= s || total <= 0)
+    const int nw = load_uniform(p.ws_meta, 0);
+    asm volatile("" :: "s"(q0), "s"(q1), "s"(s), "s"(e), "s"(total), "s"(nw));   // keep the loads together
+    const int64_t n = nw;
+    const int lq = q1 - q0;
+    if (t >= lq || e <= s || total <= 0)
         return;
-    const int64_t n = load_uniform(p.ws_meta, 0);
     const int w0 = (int)(((int64_t)(s + 1) * n - 1) / total);
     const int w1 = (int)(((int64_t)e * n - 1) / total);
     if (w0 == w1)
@@ -1437,11 +1439,15 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
         float l[kChunk];
         float4 v[kChunk];
 #pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-            const bool in = c0 + i < ns;
-            l[i] = in ? lse[(c0 + i) * lstride] : -INFINITY;
-            v[i] = in ? load_partial4<kHalf>(p.ws_o, o0 + (c0 + i) * ostride) : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = 0; i < kChunk; ++i) {                 // unconditional loads (a slot past the
+            const int si = min(c0 + i, ns - 1);             // end re-reads the last one), then masked
+            l[i] = lse[si * lstride];
+            v[i] = load_partial4<kHalf>(p.ws_o, o0 + si * ostride);
         }
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i)
+            if (c0 + i >= ns)
+                l[i] = -INFINITY;
         float mc = l[0];
 #pragma unroll
         for (int i = 1; i < kChunk; ++i)
