@@ -61,6 +61,13 @@ def _declare(lib) -> None:
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_double, ctypes.c_double, ctypes.c_double,
         P, P, P, ctypes.c_int64, P, P, ctypes.c_int]
+    lib.va_oracle_attn_ex.restype = ctypes.c_int
+    lib.va_oracle_attn_ex.argtypes = [
+        P, P, P, ctypes.c_int, P, ctypes.c_int64, P, P,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_double, ctypes.c_double, ctypes.c_double,
+        ctypes.c_int, ctypes.c_double, P,
+        P, P, P, ctypes.c_int64, P, P, ctypes.c_int]
 
 
 def fp8_e4m3fn_to_float(code: int) -> float:
@@ -87,7 +94,8 @@ def attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, kv_dtype: str,
          num_kv_heads: int, scale: float, k_descale: float = 1.0,
          v_descale: float = 1.0, rows: Optional[Sequence[int]] = None,
          segments: Optional[Sequence[Sequence[int]]] = None,
-         threads: Optional[int] = None, lib=None) -> Tuple[np.ndarray, np.ndarray]:
+         threads: Optional[int] = None, lib=None, window_left: int = -1,
+         softcap: float = 0.0, sinks: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Attention output [n_rows, D] and natural-log LSE [n_rows], float64.
 
     q: uint16 [total_q, Hq, D]; k, v: uint8 (fp8 e4m3fn) or uint16 (bf16)
@@ -96,6 +104,8 @@ def attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, kv_dtype: str,
     contiguous split of [0, seqused_k) (first start 0); the oracle then merges
     per-segment partials by log-sum-exp instead of one pass.  lib: an
     alternative build of the oracle (tests that plant mistakes use this).
+    window_left (-1 = none), softcap (0 = none) and sinks ([Hq] logits or None)
+    select the optional sliding window, logit softcap and attention sinks.
     """
     if lib is None:
         lib = _load()
@@ -131,10 +141,15 @@ def attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, kv_dtype: str,
         seg_ptr = np.asarray(ptr, dtype=np.int32)
     out = np.zeros((n, d), dtype=np.float64)
     lse = np.zeros((n,), dtype=np.float64)
-    st = lib.va_oracle_attn(
+    sk_arr = None
+    if sinks is not None:
+        sk_arr = np.ascontiguousarray(sinks, dtype=np.float64)
+        assert sk_arr.shape == (hq,)
+    st = lib.va_oracle_attn_ex(
         _ptr(q), _ptr(k), _ptr(v), 1 if kv_dtype == "fp8" else 0,
         _ptr(bt), bt.shape[1], _ptr(cu), _ptr(sk), sk.shape[0], hq, num_kv_heads,
         d, page, float(scale), float(k_descale), float(v_descale),
+        int(window_left), float(softcap), _ptr(sk_arr),
         _ptr(seg_start), _ptr(seg_ptr), _ptr(rows_arr), n, _ptr(out), _ptr(lse),
         default_threads() if threads is None else int(threads))
     if st != 0:
@@ -146,4 +161,6 @@ def attn_problem(p, rows=None, segments=None, threads=None, lib=None):
     """``attn`` on a ``va_inputs.Problem``-like object (duck typed)."""
     return attn(p.q, p.k, p.v, p.kv_dtype, p.block_table, p.cu_seqlens_q,
                 p.seqused_k, p.num_kv_heads, p.scale, p.k_descale, p.v_descale,
-                rows=rows, segments=segments, threads=threads, lib=lib)
+                rows=rows, segments=segments, threads=threads, lib=lib,
+                window_left=getattr(p, "window_left", -1), softcap=getattr(p, "softcap", 0.0),
+                sinks=None if getattr(p, "sinks", None) is None else p.sinks.astype(np.float64))

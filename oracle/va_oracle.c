@@ -29,6 +29,20 @@
  *    log-sum-exp is exact algebra: with lse_s = log sum_{j in s} exp(s_j),
  *    O = sum_s exp(lse_s - lse) * o_s, lse = log sum_s exp(lse_s).
  *
+ * Optional features, as the verify call of the PR #30105 summary page passes
+ * them to the shared attention kernel ("Key source snippets": window_size,
+ * softcap, sinks; the PR #36330 gate excludes all three):
+ *  - sliding window: window_size = (window_left, 0), window_left = sliding
+ *    window - 1; a query at absolute position i = Lk-Lq+t also needs key
+ *    j >= i - window_left (keys i-window_left .. i).  -1 = no window;
+ *  - logit softcap: s <- softcap * tanh(s / softcap) on the scaled logit
+ *    (0 = off);
+ *  - attention sinks: one logit per query head that joins the softmax
+ *    denominator and carries no value: out = sum_j e^s_j V_j / (sum_j e^s_j
+ *    + e^sink_h).
+ * The pages name these features but do not define them; the readings above
+ * are the ones their parameter names carry in common attention APIs.
+ *
  * FP8 format: OCP E4M3FN (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
  * no infinities, S.1111.111 = NaN, subnormals m/8 * 2^-6).  The pages only say
  * "FP8 KV"; gfx950's native fp8 is this format (reading recorded in the design doc).
@@ -78,6 +92,9 @@ typedef struct {
     const int32_t *seqused_k;   /* [B] */
     int num_seqs, num_q_heads, num_kv_heads, head_dim, page_size;
     double scale, k_descale, v_descale;
+    int window_left;            /* -1: no sliding window */
+    double softcap;             /* 0: no logit softcap */
+    const double *sinks;        /* [Hq] sink logits, or NULL */
     /* split mode (optional): segments of sequence b are
      * seg_start[seg_ptr[b] .. seg_ptr[b+1]), each running to the next start
      * (or to seqused_k[b] for the last one).  NULL = one segment. */
@@ -136,6 +153,8 @@ static int64_t row_segment(const va_oracle_problem *p, int b, int g,
         for (d = 0; d < D; ++d)
             dot += va_oracle_bf16_to_double(qrow[d]) * kv_at(p, p->k_pool, base + d);
         logits[j] = p->scale * p->k_descale * dot;
+        if (p->softcap > 0.0)
+            logits[j] = p->softcap * tanh(logits[j] / p->softcap);
         if (logits[j] > m)
             m = logits[j];
     }
@@ -170,7 +189,8 @@ static int compute_row(const va_oracle_problem *p, int64_t flat, double *out,
     int h = (int)(flat % p->num_q_heads);
     int b = seq_of_row(p, qr);
     int g = h / G, d;
-    int64_t Lq, Lk, t, visible;
+    int64_t Lq, Lk, t, visible, first;
+    double sink = -INFINITY;
     const uint16_t *qrow = p->q + flat * D;
     if (b < 0)
         return -1;
@@ -180,10 +200,23 @@ static int compute_row(const va_oracle_problem *p, int64_t flat, double *out,
     visible = Lk - Lq + t + 1;          /* keys 0 .. Lk-Lq+t (bottom-right causal) */
     if (visible > Lk)
         visible = Lk;
+    first = 0;                          /* sliding window: keys from i - window_left on */
+    if (p->window_left >= 0 && visible - 1 - p->window_left > 0)
+        first = visible - 1 - p->window_left;
+    if (p->sinks)
+        sink = p->sinks[h];
 
     if (p->seg_start == NULL) {
         double m, L;
-        row_segment(p, b, g, qrow, 0, visible, &m, &L, acc, logits);
+        row_segment(p, b, g, qrow, first, visible, &m, &L, acc, logits);
+        if (sink > -INFINITY) {         /* the sink joins the denominator only */
+            double mm = m > sink ? m : sink;
+            double f = L > 0.0 ? exp(m - mm) : 0.0;
+            L = L * f + exp(sink - mm);
+            for (d = 0; d < D; ++d)
+                acc[d] *= f;
+            m = mm;
+        }
         if (L > 0.0) {
             for (d = 0; d < D; ++d)
                 out[d] = p->v_descale * acc[d] / L;
@@ -213,6 +246,8 @@ static int compute_row(const va_oracle_problem *p, int64_t flat, double *out,
             double m, L;
             if (hi > visible)
                 hi = visible;
+            if (lo < first)
+                lo = first;
             row_segment(p, b, g, qrow, lo, hi, &m, &L, acc, logits);
             if (L > 0.0) {
                 seg_lse[s - s0] = m + log(L);
@@ -226,6 +261,8 @@ static int compute_row(const va_oracle_problem *p, int64_t flat, double *out,
             if (seg_lse[s - s0] > lse_max)
                 lse_max = seg_lse[s - s0];
         }
+        if (sink > lse_max)
+            lse_max = sink;
         for (d = 0; d < D; ++d)
             acc2[d] = 0.0;
         if (lse_max > -INFINITY) {
@@ -235,6 +272,8 @@ static int compute_row(const va_oracle_problem *p, int64_t flat, double *out,
                 for (d = 0; d < D; ++d)
                     acc2[d] += w * seg_o[(int64_t)(s - s0) * D + d];
             }
+            if (sink > -INFINITY)       /* the sink joins the denominator once */
+                denom += exp(sink - lse_max);
             for (d = 0; d < D; ++d)
                 out[d] = p->v_descale * acc2[d] / denom;
             *lse = lse_max + log(denom);
@@ -282,16 +321,18 @@ static void *worker(void *vp)
 /*
  * Exported entry.  Returns 0 on success, -1 on a row that belongs to no
  * sequence, -2 on allocation failure, -3 on bad arguments.
+ * window_left: -1 or >= 0; softcap: 0 or > 0; sinks: NULL or [num_q_heads].
  */
-int va_oracle_attn(const uint16_t *q, const void *k_pool, const void *v_pool,
-                   int kv_is_fp8, const int32_t *block_table, int64_t bt_stride,
-                   const int32_t *cu_seqlens_q, const int32_t *seqused_k,
-                   int num_seqs, int num_q_heads, int num_kv_heads,
-                   int head_dim, int page_size, double scale,
-                   double k_descale, double v_descale,
-                   const int32_t *seg_start, const int32_t *seg_ptr,
-                   const int64_t *rows, int64_t n_rows,
-                   double *out, double *lse, int num_threads)
+int va_oracle_attn_ex(const uint16_t *q, const void *k_pool, const void *v_pool,
+                      int kv_is_fp8, const int32_t *block_table, int64_t bt_stride,
+                      const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                      int num_seqs, int num_q_heads, int num_kv_heads,
+                      int head_dim, int page_size, double scale,
+                      double k_descale, double v_descale,
+                      int window_left, double softcap, const double *sinks,
+                      const int32_t *seg_start, const int32_t *seg_ptr,
+                      const int64_t *rows, int64_t n_rows,
+                      double *out, double *lse, int num_threads)
 {
     va_oracle_problem p;
     pthread_t *th;
@@ -304,12 +345,15 @@ int va_oracle_attn(const uint16_t *q, const void *k_pool, const void *v_pool,
         return -3;
     if ((seg_start == NULL) != (seg_ptr == NULL))
         return -3;
+    if (window_left < -1 || !(softcap >= 0.0))
+        return -3;
     p.q = q; p.k_pool = k_pool; p.v_pool = v_pool; p.kv_is_fp8 = kv_is_fp8;
     p.block_table = block_table; p.bt_stride = bt_stride;
     p.cu_seqlens_q = cu_seqlens_q; p.seqused_k = seqused_k;
     p.num_seqs = num_seqs; p.num_q_heads = num_q_heads; p.num_kv_heads = num_kv_heads;
     p.head_dim = head_dim; p.page_size = page_size;
     p.scale = scale; p.k_descale = k_descale; p.v_descale = v_descale;
+    p.window_left = window_left; p.softcap = softcap; p.sinks = sinks;
     p.seg_start = seg_start; p.seg_ptr = seg_ptr;
     p.rows = rows; p.n_rows = n_rows; p.out = out; p.lse = lse;
     for (i = 0; i < 256; ++i)
@@ -345,4 +389,21 @@ int va_oracle_attn(const uint16_t *q, const void *k_pool, const void *v_pool,
     free(th);
     free(args);
     return status;
+}
+
+/* The plain call: no window, softcap or sinks. */
+int va_oracle_attn(const uint16_t *q, const void *k_pool, const void *v_pool,
+                   int kv_is_fp8, const int32_t *block_table, int64_t bt_stride,
+                   const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                   int num_seqs, int num_q_heads, int num_kv_heads,
+                   int head_dim, int page_size, double scale,
+                   double k_descale, double v_descale,
+                   const int32_t *seg_start, const int32_t *seg_ptr,
+                   const int64_t *rows, int64_t n_rows,
+                   double *out, double *lse, int num_threads)
+{
+    return va_oracle_attn_ex(q, k_pool, v_pool, kv_is_fp8, block_table, bt_stride, cu_seqlens_q,
+                             seqused_k, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                             scale, k_descale, v_descale, -1, 0.0, NULL, seg_start, seg_ptr, rows,
+                             n_rows, out, lse, num_threads);
 }

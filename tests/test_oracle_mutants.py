@@ -14,7 +14,9 @@ import numpy as np
 import pytest
 
 import oracle
+from test_oracle_features import FEATURE_CASES, dense_reference_ex
 from test_oracle_pins import BRUTE_CASES, dec_fp8, dense_reference, rel_err, small_problem
+import va_inputs
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "va_oracle.c")
 
@@ -34,6 +36,14 @@ MUTANTS = {
     "q_k_same_operand": ("va_oracle_bf16_to_double(qrow[d]) * kv_at(p, p->k_pool, base + d)",
                          "va_oracle_bf16_to_double(qrow[d]) * kv_at(p, p->v_pool, base + d)"),
     "lse_log_dropped": ("*lse = m + log(L);", "*lse = m;"),
+    # optional features (sliding window, softcap, sinks)
+    "feat_window_off_by_one": ("first = visible - 1 - p->window_left;", "first = visible - p->window_left;"),
+    "feat_window_ignored": ("if (lo < first)\n                lo = first;", "if (0)\n                lo = first;"),
+    "feat_softcap_unscaled": ("logits[j] = p->softcap * tanh(logits[j] / p->softcap);",
+                              "logits[j] = tanh(logits[j] / p->softcap);"),
+    "feat_sink_kv_head": ("sink = p->sinks[h];", "sink = p->sinks[g];"),
+    "feat_sink_dropped": ("L = L * f + exp(sink - mm);", "L = L * f;"),
+    "feat_sink_in_split_dropped": ("                denom += exp(sink - lse_max);", "                ;"),
 }
 
 
@@ -70,14 +80,33 @@ def _pins_pass(lib) -> bool:
     return True
 
 
+def _feature_pins_pass(lib) -> bool:
+    """Dense brute force with window / softcap / sinks, unsplit and split."""
+    for ql, kl, hq, hkv, dt, wl, cap, use_sinks in FEATURE_CASES:
+        p = va_inputs.custom(ql, kl, hq, hkv, dt, seed=sum(kl) + hq)
+        sinks = np.linspace(-1.5, 2.5, hq) if use_sinks else None
+        ref_out, ref_lse = dense_reference_ex(p, wl, cap, sinks)
+        for segs in (None, [[0] + list(range(7, k, 23)) for k in kl]):
+            out, lse = oracle.attn(p.q, p.k, p.v, p.kv_dtype, p.block_table, p.cu_seqlens_q,
+                                   p.seqused_k, p.num_kv_heads, p.scale, p.k_descale, p.v_descale,
+                                   threads=2, lib=lib, window_left=wl, softcap=cap, sinks=sinks,
+                                   segments=segs)
+            if not np.all(np.isfinite(out)) or rel_err(out, ref_out) > 1e-12:
+                return False
+            if np.max(np.abs(lse - ref_lse)) > 1e-12 * max(1.0, np.max(np.abs(ref_lse))):
+                return False
+    return True
+
+
 def test_unmutated_copy_passes(tmp_path):
     so = tmp_path / "libclean.so"
     subprocess.check_call(["gcc", "-O1", "-std=c99", "-D_DEFAULT_SOURCE", "-shared", "-fPIC",
                            SRC, "-o", str(so), "-lm", "-lpthread"])
-    assert _pins_pass(oracle.load_library(str(so)))
+    lib = oracle.load_library(str(so))
+    assert _pins_pass(lib) and _feature_pins_pass(lib)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(tmp_path, name):
     lib = _build_mutant(tmp_path, name)
-    assert not _pins_pass(lib), f"pins failed to catch mutant {name}"
+    assert not (_pins_pass(lib) and _feature_pins_pass(lib)), f"pins failed to catch mutant {name}"

@@ -53,6 +53,9 @@ class Problem:
     v_descale: float             # fp32 value
     head_dim: int = HEAD_DIM
     page_size: int = PAGE
+    window_left: int = -1                  # sliding window: keys from i - window_left (-1 = none)
+    softcap: float = 0.0                   # logit softcap (0 = none)
+    sinks: Optional[np.ndarray] = None     # float32 [Hq] sink logits, or None
 
     @property
     def num_seqs(self) -> int:
@@ -113,7 +116,8 @@ def custom(q_lens: Sequence[int], kv_lens: Sequence[int], num_q_heads: int,
            table: str = "perm", k_descale: float = 1.0, v_descale: float = 1.0,
            scale: Optional[float] = None, poison: bool = True,
            extra_blocks: int = 0, name: str = "custom",
-           max_blocks_per_seq: Optional[int] = None) -> Problem:
+           max_blocks_per_seq: Optional[int] = None, window_left: int = -1,
+           softcap: float = 0.0, sinks: Optional[Sequence[float]] = None) -> Problem:
     """Build one problem.
 
     table: "perm"     -- pages of all sequences are a seeded random permutation
@@ -172,10 +176,14 @@ def custom(q_lens: Sequence[int], kv_lens: Sequence[int], num_q_heads: int,
 
     if scale is None:
         scale = HEAD_DIM ** -0.5
+    sk_arr = None if sinks is None else np.asarray(sinks, dtype=np.float32)
+    if sk_arr is not None:
+        assert sk_arr.shape == (num_q_heads,)
     return Problem(name=name, q=q, k=k, v=v, kv_dtype=kv_dtype, block_table=bt,
                    cu_seqlens_q=cu, seqused_k=seqused, num_q_heads=num_q_heads,
                    num_kv_heads=num_kv_heads, scale=_f32(scale),
-                   k_descale=_f32(k_descale), v_descale=_f32(v_descale))
+                   k_descale=_f32(k_descale), v_descale=_f32(v_descale),
+                   window_left=int(window_left), softcap=_f32(softcap), sinks=sk_arr)
 
 
 # ----------------------------------------------------------------- workloads --
