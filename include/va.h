@@ -84,6 +84,12 @@ typedef struct {
     int32_t force_grid;          /* 0 = automatic; > 0 = number of split-KV workgroups
                                     (a testing hook: every value gives the same result
                                     up to floating-point merge order) */
+    int32_t window_left;         /* sliding window: -1 = none; >= 0: the query at absolute
+                                    position i also needs key j >= i - window_left (the
+                                    window_size = (sliding_window - 1, 0) of the PR #30105
+                                    page's verify call) */
+    float softcap;               /* logit softcap: 0 = none; > 0: every scaled logit s is
+                                    replaced by softcap * tanh(s / softcap) */
 } va_problem;
 
 typedef struct va_plan_s *va_plan_t;
@@ -95,7 +101,8 @@ typedef struct va_plan_s *va_plan_t;
  *   - Q and out bf16; KV fp8 e4m3fn or bf16;
  *   - G = Hq/Hkv in {4, 8, 16}; 1 <= max_seqlen_q <= 4;
  *   - num_seqs * num_kv_heads <= 65536;
- *   - causal only; no sliding window, softcap or sinks.
+ *   - causal only, with an optional sliding window, logit softcap and attention
+ *     sinks (window_left >= -1, softcap >= 0; else VA_ERR_INVALID_ARG).
  *   - With num_cus == 0, the current HIP device must be gfx950.
  * The domain is the PR #36330 page's gate (gfx950, q len 2..4, G = 16, D = 256,
  * page 16, bf16 Q, fp8 KV), widened:
@@ -139,23 +146,33 @@ va_status va_run(va_plan_t plan, const void *q, const void *k_pool, const void *
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * The kernels of va_run, enqueued one at a time (same arguments).
+ * va_run with its optional arguments, and one kernel at a time.
+ *   sinks        device pointer to Hq floats, one sink logit per query head, or
+ *                NULL for none.  A sink is a logit in the units of the scaled
+ *                logits (softmax_scale * k_descale * q.k, natural log); it joins
+ *                the softmax denominator and carries no value:
+ *                out = v_descale * sum_j e^s_j V_j / (sum_j e^s_j + e^sink).
+ *                Not softcapped.  (The PR #30105 page's verify call passes sinks
+ *                to the attention kernel; the pages do not define them, this is
+ *                the reading.)
+ *   stage VA_STAGE_ALL:      both kernels, as va_run.
  *   stage VA_STAGE_SPLIT_KV: the split-KV main kernel.  It writes the per-segment
  *                            partials to the workspace, and writes rows whose
  *                            sequence fits one segment straight to out.
  *   stage VA_STAGE_MERGE:    the segment-reduce kernel; it reads the partials and
  *                            writes the remaining rows of out.
  * VA_STAGE_MERGE must follow VA_STAGE_SPLIT_KV of the same call on the same
- * stream (with the same workspace).  va_run == SPLIT_KV then MERGE.  These exist
- * so a caller can time or profile each kernel on its own stream.
+ * stream (with the same workspace).  The single stages exist so a caller can
+ * time or profile each kernel on its own.  Other arguments and errors as va_run;
+ * an unknown stage is VA_ERR_INVALID_ARG.
  */
 enum { VA_STAGE_ALL = 0, VA_STAGE_SPLIT_KV = 1, VA_STAGE_MERGE = 2 };
-va_status va_run_stage(va_plan_t plan, int32_t stage, const void *q, const void *k_pool,
-                       const void *v_pool, const int32_t *block_table,
-                       const int32_t *cu_seqlens_q, const int32_t *seqused_k,
-                       float softmax_scale, const float *k_descale,
-                       const float *v_descale, void *out, void *workspace,
-                       size_t workspace_bytes, void *stream);
+va_status va_run_ex(va_plan_t plan, int32_t stage, const void *q, const void *k_pool,
+                    const void *v_pool, const int32_t *block_table,
+                    const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                    float softmax_scale, const float *k_descale,
+                    const float *v_descale, const float *sinks, void *out,
+                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* Release a plan (NULL is ignored). */
 void va_plan_destroy(va_plan_t plan);

@@ -26,7 +26,7 @@ VA_OK, VA_ERR_INVALID_ARG, VA_ERR_UNSUPPORTED, VA_ERR_WORKSPACE, VA_ERR_HIP = ra
 VA_DT_BF16, VA_DT_FP8_E4M3FN = 1, 2
 VA_STAGE_ALL, VA_STAGE_SPLIT_KV, VA_STAGE_MERGE = 0, 1, 2
 
-EXPORTED = ("va_plan", "va_plan_workspace_bytes", "va_plan_grid", "va_run", "va_run_stage",
+EXPORTED = ("va_plan", "va_plan_workspace_bytes", "va_plan_grid", "va_run", "va_run_ex",
             "va_plan_destroy", "va_status_str", "va_fp8_to_bf16")
 
 _lib = None
@@ -47,6 +47,7 @@ class _Problem(ctypes.Structure):
         ("num_blocks", ctypes.c_int64), ("total_q", ctypes.c_int64),
         ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
         ("num_cus", ctypes.c_int32), ("force_grid", ctypes.c_int32),
+        ("window_left", ctypes.c_int32), ("softcap", ctypes.c_float),
     ]
 
 
@@ -69,8 +70,8 @@ def library(path: str = LIB_PATH):
     run_args = [P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, ctypes.c_size_t, P]
     lib.va_run.restype = ctypes.c_int
     lib.va_run.argtypes = run_args
-    lib.va_run_stage.restype = ctypes.c_int
-    lib.va_run_stage.argtypes = [P, ctypes.c_int32] + run_args[1:]
+    lib.va_run_ex.restype = ctypes.c_int
+    lib.va_run_ex.argtypes = [P, ctypes.c_int32] + run_args[1:10] + [P] + run_args[10:]
     lib.va_plan_destroy.restype = None
     lib.va_plan_destroy.argtypes = [P]
     lib.va_status_str.restype = ctypes.c_char_p
@@ -109,11 +110,13 @@ class Plan:
                  max_seqlen_q: int, max_seqlen_k: int, max_blocks_per_seq: int,
                  num_blocks: int, total_q: int, kv_dtype: str = "fp8",
                  num_cus: int = 0, force_grid: int = 0, head_dim: int = 256,
+                 window_left: int = -1, softcap: float = 0.0,
                  page_size: int = 16, q_dtype: str = "bf16"):
         self._lib = library()
         pr = _Problem(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                       max_seqlen_q, max_seqlen_k, max_blocks_per_seq, num_blocks, total_q,
-                      _dtype_code(q_dtype), _dtype_code(kv_dtype), num_cus, force_grid)
+                      _dtype_code(q_dtype), _dtype_code(kv_dtype), num_cus, force_grid,
+                      int(window_left), float(softcap))
         self.problem = pr
         self.kv_dtype = kv_dtype
         h = ctypes.c_void_p()
@@ -138,7 +141,8 @@ class Plan:
         return cls(num_seqs=p.num_seqs, num_q_heads=p.num_q_heads, num_kv_heads=p.num_kv_heads,
                    max_seqlen_q=max(1, p.max_seqlen_q), max_seqlen_k=p.max_seqlen_k,
                    max_blocks_per_seq=int(p.block_table.shape[1]), num_blocks=p.num_blocks,
-                   total_q=p.total_q, kv_dtype=p.kv_dtype, **kw)
+                   total_q=p.total_q, kv_dtype=p.kv_dtype,
+                   window_left=getattr(p, "window_left", -1), softcap=getattr(p, "softcap", 0.0), **kw)
 
     def workspace(self, device=None):
         import torch
@@ -146,11 +150,15 @@ class Plan:
 
     def run(self, q, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k, softmax_scale: float,
             k_descale=None, v_descale=None, out=None, workspace=None, stream=None,
-            stage: int = VA_STAGE_ALL):
-        """Enqueue the attention on ``stream`` (default: torch's current stream)."""
+            stage: int = VA_STAGE_ALL, sinks=None):
+        """Enqueue the attention on ``stream`` (default: torch's current stream).
+        sinks: optional float32 device tensor [Hq] of sink logits."""
         import torch
         self._check_tensors(q, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k,
                             k_descale, v_descale)
+        if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != self.problem.num_q_heads
+                                  or not sinks.is_cuda or not sinks.is_contiguous()):
+            raise ValueError("sinks must be a contiguous float32 device tensor with num_q_heads elements")
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
@@ -163,10 +171,10 @@ class Plan:
             stream = torch.cuda.current_stream(q.device)
         sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
         ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
-        st = self._lib.va_run_stage(
+        st = self._lib.va_run_ex(
             self._h, int(stage), ptr(q), ptr(k_pool), ptr(v_pool), ptr(block_table),
             ptr(cu_seqlens_q), ptr(seqused_k), ctypes.c_float(softmax_scale),
-            ptr(k_descale), ptr(v_descale), ptr(out), ptr(workspace),
+            ptr(k_descale), ptr(v_descale), ptr(sinks), ptr(out), ptr(workspace),
             ctypes.c_size_t(workspace.numel() * workspace.element_size()),
             ctypes.c_void_p(sptr))
         _check(st, "va_run")

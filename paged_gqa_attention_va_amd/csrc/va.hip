@@ -78,6 +78,9 @@ struct SplitParams {
     int32_t *ws_prefix;   // [BH + 1] exclusive prefix of page counts, [BH] = total
     int32_t *ws_meta;     // [0] = workgroups in use
     float scale_log2;     // softmax_scale * log2(e)
+    float cap_log2;       // logit softcap * log2(e) (0 = no softcap)
+    const float *sinks;   // [Hq] sink logits (natural-log units) or null
+    int32_t window_left;  // sliding window: keys from i - window_left on (-1 = none)
     int32_t num_seqs, hq, hkv, log2g, mbps, grid_n, min_pages, rows_max;
     int64_t num_blocks;
 };
@@ -85,6 +88,7 @@ struct SplitParams {
 struct MergeParams {
     const int32_t *cu;
     const float *vdesc;
+    const float *sinks;   // [Hq] sink logits (natural-log units) or null
     const void *ws_o;     // fp16 or fp32 partials, see SplitParams
     const float *ws_lse;
     const int32_t *ws_prefix;
@@ -174,15 +178,24 @@ __device__ __forceinline__ int load_uniform(const int32_t *base, int64_t idx)
 
 // Pages of (sequence, kv head) bg that hold keys for at least one query row.
 // Clamped to the block-table row so a bad length cannot index past it.
+// First page any query row of a sequence can see: with a sliding window the
+// lowest visible key is that of query token 0, (lk - lq) - window_left.
+__device__ __forceinline__ int first_page(int lk, int lq, int wl)
+{
+    return wl < 0 ? 0 : max(0, lk - lq - wl) / kPage;
+}
+
+// Pages of (sequence, kv head) bg that the split covers: first_page .. the
+// last page holding a key below seqused_k (clamped to the block-table row).
 __device__ __forceinline__ int pages_of(const int32_t *cu, const int32_t *seqused, int hkv,
-                                        int mbps, int bg)
+                                        int mbps, int wl, int bg)
 {
     const int b = bg / hkv;
     const int lq = cu[b + 1] - cu[b];
     const int lk = seqused[b];
     if (lq <= 0 || lk <= 0)
         return 0;
-    return min((lk + kPage - 1) / kPage, mbps);
+    return max(0, min((lk + kPage - 1) / kPage, mbps) - first_page(lk, lq, wl));
 }
 
 // ----------------------------------------------------------- K/V loading --
@@ -328,15 +341,24 @@ __device__ __forceinline__ void qk_step(floatx4_t (&S)[2][RTW], const StepRegs<K
 // B-operands (bf16) of this wave's row tiles.
 //   masked  this step holds keys some row may not see (the causal tail, keys
 //           at or past seqused_k, or a missing second page); uniform
-//   limit   per row tile: the last key index row (lane%16) may see
+//   limit   per row tile: the last key index row (lane%16) may see; with a
+//           sliding window the first is limit - window_left (wlim)
 //   key0    index of key 0 of page a; has_b: page b is part of this piece
 //   c       per row tile: logit multiplier (softmax_scale * k_descale * log2 e,
 //           times the row's Q scale where Q was rescaled)
-template <int RTW>
+// Logit softcap in log2 units: x = C tanh(x / C) with C = softcap log2(e),
+// tanh(y) = 1 - 2 / (e^(2y) + 1) (saturates to +-C; -inf stays -inf).
+__device__ __forceinline__ float softcap_log2(float x, float C)
+{
+    const float e = exp2_fast(x * (2.8853900817779268f / C));     // e^(2 x / C) = 2^(2 log2(e) x / C)
+    return C - 2.0f * C / (e + 1.0f);
+}
+
+template <int RTW, bool CAP>
 __device__ __forceinline__ void softmax_step(RowState<RTW> &st, bf16x8_t (&pop)[RTW],
                                              const floatx4_t (&S)[2][RTW], const int (&limit)[RTW],
-                                             int key0, bool has_b, const float (&c)[RTW], int lane,
-                                             bool masked)
+                                             uint32_t wlim, int key0, bool has_b, const float (&c)[RTW],
+                                             float cap, int lane, bool masked)
 {
     const int j = lane >> 4;
     // Logits in log2 units, masked by select (NaN garbage in masked slots is
@@ -353,9 +375,12 @@ __device__ __forceinline__ void softmax_step(RowState<RTW> &st, bf16x8_t (&pop)[
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float v = S[a][rt][e] * c[rt];
+                if constexpr (CAP)
+                    v = softcap_log2(v, cap);
                 if (masked) {
+                    // visible: limit - window_left <= key <= limit (wlim = window_left, or 2^31 - 1)
                     const int key = key0 + 16 * a + 4 * j + e;
-                    const bool ok = (a == 0 || has_b) && key <= limit[rt];
+                    const bool ok = (a == 0 || has_b) && (uint32_t)(limit[rt] - key) <= wlim;
                     v = ok ? v : -INFINITY;
                 }
                 x[rt][4 * a + e] = v;
@@ -538,7 +563,7 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
 {
     const int bh = p.num_seqs * p.hkv;
     if (bh <= 64) {                                    // one pass: one count per lane
-        const int cnt = lane < bh ? pages_of(p.cu, p.seqused, p.hkv, p.mbps, lane) : 0;
+        const int cnt = lane < bh ? pages_of(p.cu, p.seqused, p.hkv, p.mbps, p.window_left, lane) : 0;
         const int incl = wave_incl_scan(cnt, lane);
         const int total = __shfl(incl, 63);
         Share sh;
@@ -568,7 +593,7 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
     int total = 0;
     for (int c0 = 0; c0 < bh; c0 += 64) {
         const int bg = c0 + lane;
-        const int cnt = bg < bh ? pages_of(p.cu, p.seqused, p.hkv, p.mbps, bg) : 0;
+        const int cnt = bg < bh ? pages_of(p.cu, p.seqused, p.hkv, p.mbps, p.window_left, bg) : 0;
         total += wave_sum(cnt);
     }
     Share sh;
@@ -582,7 +607,7 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
     int base = 0;
     for (int c0 = 0; c0 < bh; c0 += 64) {
         const int bg = c0 + lane;
-        const int cnt = bg < bh ? pages_of(p.cu, p.seqused, p.hkv, p.mbps, bg) : 0;
+        const int cnt = bg < bh ? pages_of(p.cu, p.seqused, p.hkv, p.mbps, p.window_left, bg) : 0;
         const int incl = wave_incl_scan(cnt, lane);
         if (write_prefix && bg < bh)
             p.ws_prefix[bg] = base + incl - cnt;
@@ -610,7 +635,7 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
 
 // RTW: row tiles per wave; NR: row groups (waves sharing the same keys for
 // different rows); NG = 4 / NR key groups splitting each piece's page pairs.
-template <int RTW, int NR, int KVT>
+template <int RTW, int NR, int KVT, bool CAP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void va_split_kv_kernel(SplitParams p)
 {
@@ -648,7 +673,7 @@ void va_split_kv_kernel(SplitParams p)
     const int bh = p.num_seqs * p.hkv;
     int s = sh.s, bg = sh.bg, base = sh.base;
     while (s < sh.e && bg < bh) {
-        const int cnt = uniform(pages_of(p.cu, p.seqused, p.hkv, p.mbps, bg));
+        const int cnt = uniform(pages_of(p.cu, p.seqused, p.hkv, p.mbps, p.window_left, bg));
         if (cnt == 0) {
             ++bg;
             continue;
@@ -659,10 +684,14 @@ void va_split_kv_kernel(SplitParams p)
         const int lq = uniform(p.cu[b + 1]) - q0;
         const int lk = uniform(p.seqused[b]);
         const int ctx = lk - lq;
-        const int p0 = s - base;
-        const int p1 = min(sh.e, base + cnt) - base;
-        const bool whole = (p0 == 0 && p1 == cnt);
+        const int r0 = s - base;                               // piece = pages r0 .. r1 of the pair's range
+        const int r1 = min(sh.e, base + cnt) - base;
+        const bool whole = (r0 == 0 && r1 == cnt);
+        const int pb = first_page(lk, lq, p.window_left);      // the range starts at logical page pb
+        const int p0 = pb + r0, p1 = pb + r1;
         const int slot = w + bg;
+        const int lo_max = p.window_left < 0 ? INT_MIN : ctx + lq - 1 - p.window_left;
+        const uint32_t wlim = p.window_left < 0 ? 0x7FFFFFFFu : (uint32_t)p.window_left;
 
         // ---- stage this piece's packed Q rows in LDS, in operand order
         __syncthreads();                                // previous piece's merge reads done
@@ -732,14 +761,14 @@ void va_split_kv_kernel(SplitParams p)
                     load_k<KVT>(r, kbase, yna, ynb, hn, p.hkv, lane);
                 }
                 const int key0 = pa * kPage;
-                const bool masked = !hb || key0 + 31 > ctx;
+                const bool masked = !hb || key0 + 31 > ctx || key0 < lo_max;
                 bf16x8_t pop[RTW];
                 {
                     float cr[RTW];
 #pragma unroll
                     for (int rt = 0; rt < RTW; ++rt)
                         cr[rt] = c;
-                    softmax_step<RTW>(st, pop, S, limit, key0, hb, cr, lane, masked);
+                    softmax_step<RTW, CAP>(st, pop, S, limit, wlim, key0, hb, cr, p.cap_log2, lane, masked);
                 }
                 pv_regs<RTW, KVT>(st, r, pop, masked ? v_zero_mask(key0, hb, lk, lane) : 0u);
                 if (!more)
@@ -814,7 +843,13 @@ void va_split_kv_kernel(SplitParams p)
                 if (t < lq) {
                     const float L = st.l[rt];
                     if (whole) {
-                        const float inv = L > 0.f ? vd / L : 0.f;
+                        float inv = L > 0.f ? vd / L : 0.f;
+                        if (p.sinks) {                   // the sink joins the denominator only
+                            const float sk = p.sinks[g * G + h] * 1.4426950408889634f;
+                            const float mm = fmaxf(st.m[rt], sk);
+                            const float f = L > 0.f ? exp2_fast(st.m[rt] - mm) : 0.f;
+                            inv = vd * f / (L * f + exp2_fast(sk - mm));
+                        }
                         uint16_t *dst = p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -850,7 +885,7 @@ void va_split_kv_kernel(SplitParams p)
             }
         }
 
-        s = base + p1;
+        s = base + r1;
         base += cnt;
         ++bg;
     }
@@ -1195,6 +1230,15 @@ __device__ __forceinline__ void piece_epilogue(RowState<RTW> &st, unsigned char 
         }
         const int t = r >> p.log2g, h = r & (G - 1);
         if (whole) {
+            if (p.sinks) {                               // the sink joins the denominator only
+                const float sk = p.sinks[g * G + h] * 1.4426950408889634f;
+                const float mm = fmaxf(M, sk);
+                const float f = W > 0.f ? exp2_fast(M - mm) : 0.f;
+                W = W * f + exp2_fast(sk - mm);
+#pragma unroll
+                for (int d = 0; d < 8; ++d)
+                    acc[d] *= f;
+            }
             const float sc = W > 0.f ? vd / W : 0.f;
             uint4 o;
             o.x = pack_bf16x2(acc[0] * sc, acc[1] * sc);
@@ -1225,7 +1269,7 @@ __device__ __forceinline__ void piece_epilogue(RowState<RTW> &st, unsigned char 
 // the V pages, straight from HBM, one step ahead of the compute.  One
 // workgroup barrier per step makes a stage visible to both waves and frees the
 // stage the next copy overwrites.
-template <int RTW>
+template <int RTW, bool CAP>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void va_split_kv_fp8_w8_kernel(SplitParams p)
 {
@@ -1273,16 +1317,20 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
         const int q0 = load_uniform(p.cu, b);
         const int lq = load_uniform(p.cu, b + 1) - q0;
         const int lk = load_uniform(p.seqused, b);
-        const int cnt = (lq <= 0 || lk <= 0) ? 0 : min((lk + kPage - 1) / kPage, p.mbps);
+        const int pb = first_page(lk, lq, p.window_left);      // the range starts at logical page pb
+        const int cnt = (lq <= 0 || lk <= 0) ? 0 : max(0, min((lk + kPage - 1) / kPage, p.mbps) - pb);
         if (cnt == 0) {
             ++bg;
             continue;
         }
         const int ctx = lk - lq;
-        const int p0 = s - base;
-        const int p1 = min(sh.e, base + cnt) - base;
-        const bool whole = (p0 == 0 && p1 == cnt);
+        const int r0 = s - base;                               // piece = pages r0 .. r1 of the pair's range
+        const int r1 = min(sh.e, base + cnt) - base;
+        const bool whole = (r0 == 0 && r1 == cnt);
+        const int p0 = pb + r0, p1 = pb + r1;
         const int slot = w + bg;
+        const int lo_max = p.window_left < 0 ? INT_MIN : ctx + lq - 1 - p.window_left;
+        const uint32_t wlim = p.window_left < 0 ? 0x7FFFFFFFu : (uint32_t)p.window_left;
 
         const int npairs = (p1 - p0 + 1) >> 1;
         const int nsteps = (npairs + NG - 1) / NG;             // uniform over the workgroup
@@ -1361,9 +1409,9 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
                 const int pa = p0 + 2 * k;
                 const bool hb = pa + 1 < p1;
                 const int key0 = pa * kPage;
-                const bool masked = !hb || key0 + 31 > ctx;
+                const bool masked = !hb || key0 + 31 > ctx || key0 < lo_max;
                 bf16x8_t pop[RTW];
-                softmax_step<RTW>(st, pop, S, limit, key0, hb, crow, pl, masked);
+                softmax_step<RTW, CAP>(st, pop, S, limit, wlim, key0, hb, crow, p.cap_log2, pl, masked);
                 pv_lds<RTW>(st, stage, pop, masked, masked ? v_zero_mask(key0, hb, lk, pl) : 0u, pl);
             }
         }
@@ -1372,7 +1420,7 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
         piece_epilogue<RTW>(st, lds, lds + kQBytes, p, kg, rg, pl, lq, q0, g, slot, whole, vd);
 
 
-        s = base + p1;
+        s = base + r1;
         base += cnt;
         ++bg;
     }
@@ -1471,6 +1519,16 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
             acc.w += f * v[i].w;
         }
     }
+    if (p.sinks) {                                     // the sink joins the denominator once
+        const float sk = p.sinks[g * (1 << p.log2g) + h] * 1.4426950408889634f;
+        const float mm = fmaxf(mx, sk);
+        const float f = den > 0.f ? exp2_fast(mx - mm) : 0.f;
+        den = den * f + exp2_fast(sk - mm);
+        acc.x *= f;
+        acc.y *= f;
+        acc.z *= f;
+        acc.w *= f;
+    }
     const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
     const float inv = den > 0.f ? vd / den : 0.f;
     uint2 pk;
@@ -1500,34 +1558,38 @@ __global__ __launch_bounds__(kThreads) void va_fp8_to_bf16_kernel(const uint8_t 
 
 typedef void (*split_fn)(SplitParams);
 
-template <int RTW, int NR, int KVT>
+template <int RTW, int NR, int KVT, bool CAP>
 void launch_split(SplitParams p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((va_split_kv_kernel<RTW, NR, KVT>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((va_split_kv_kernel<RTW, NR, KVT, CAP>), dim3(grid), dim3(kThreads), 0, s, p);
 }
 
 typedef void (*launch_fn)(SplitParams, int, hipStream_t);
 
-template <int RTW>
+template <int RTW, bool CAP>
 void launch_fp8_w8(SplitParams p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((va_split_kv_fp8_w8_kernel<RTW>), dim3(grid), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((va_split_kv_fp8_w8_kernel<RTW, CAP>), dim3(grid), dim3(512), 0, s, p);
 }
 
 struct Variant {
     int rtw, nr;        // bf16 kernel: row tiles per wave, row groups
-    launch_fn fp8, bf16;
+    launch_fn fp8, bf16, fp8_cap, bf16_cap;   // without / with the logit softcap
 };
 
 // Row tiles needed -> kernels.  Three or four row tiles use two row groups of
 // two, so a wave's O^T accumulators stay at 128 registers (three or four row
 // tiles in one wave do not fit the register file without spilling).
 const Variant kVariants[5] = {
-    {1, 1, nullptr, nullptr},
-    {1, 1, launch_fp8_w8<1>, launch_split<1, 1, kKvBf16>},
-    {2, 1, launch_fp8_w8<1>, launch_split<2, 1, kKvBf16>},
-    {2, 2, launch_fp8_w8<2>, launch_split<2, 2, kKvBf16>},
-    {2, 2, launch_fp8_w8<2>, launch_split<2, 2, kKvBf16>},
+    {1, 1, nullptr, nullptr, nullptr, nullptr},
+    {1, 1, launch_fp8_w8<1, false>, launch_split<1, 1, kKvBf16, false>,
+     launch_fp8_w8<1, true>, launch_split<1, 1, kKvBf16, true>},
+    {2, 1, launch_fp8_w8<1, false>, launch_split<2, 1, kKvBf16, false>,
+     launch_fp8_w8<1, true>, launch_split<2, 1, kKvBf16, true>},
+    {2, 2, launch_fp8_w8<2, false>, launch_split<2, 2, kKvBf16, false>,
+     launch_fp8_w8<2, true>, launch_split<2, 2, kKvBf16, true>},
+    {2, 2, launch_fp8_w8<2, false>, launch_split<2, 2, kKvBf16, false>,
+     launch_fp8_w8<2, true>, launch_split<2, 2, kKvBf16, true>},
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1586,6 +1648,8 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
         return VA_ERR_UNSUPPORTED;
     if (p.max_seqlen_q > 4)
         return VA_ERR_UNSUPPORTED;
+    if (p.window_left < -1 || !(p.softcap >= 0.f) || p.softcap > 3.0e38f)
+        return VA_ERR_INVALID_ARG;
     if (p.total_q * (int64_t)p.num_q_heads >= INT32_MAX)    // q rows are indexed with 32-bit integers
         return VA_ERR_UNSUPPORTED;
     const int64_t bh = (int64_t)p.num_seqs * p.num_kv_heads;
@@ -1656,11 +1720,12 @@ void va_plan_destroy(va_plan_t plan)
     delete plan;
 }
 
-va_status va_run_stage(va_plan_t plan, int32_t stage, const void *q, const void *k_pool,
-                       const void *v_pool, const int32_t *block_table,
-                       const int32_t *cu_seqlens_q, const int32_t *seqused_k,
-                       float softmax_scale, const float *k_descale, const float *v_descale,
-                       void *out, void *workspace, size_t workspace_bytes, void *stream)
+va_status va_run_ex(va_plan_t plan, int32_t stage, const void *q, const void *k_pool,
+                    const void *v_pool, const int32_t *block_table,
+                    const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                    float softmax_scale, const float *k_descale, const float *v_descale,
+                    const float *sinks, void *out, void *workspace, size_t workspace_bytes,
+                    void *stream)
 {
     if (!plan)
         return VA_ERR_INVALID_ARG;
@@ -1696,6 +1761,9 @@ va_status va_run_stage(va_plan_t plan, int32_t stage, const void *q, const void 
         sp.ws_prefix = reinterpret_cast<int32_t *>(ws + plan->off_prefix);
         sp.ws_meta = reinterpret_cast<int32_t *>(ws);
         sp.scale_log2 = softmax_scale * 1.4426950408889634f;
+        sp.cap_log2 = pr.softcap * 1.4426950408889634f;
+        sp.sinks = sinks;
+        sp.window_left = pr.window_left;
         sp.num_seqs = pr.num_seqs;
         sp.hq = pr.num_q_heads;
         sp.hkv = pr.num_kv_heads;
@@ -1706,7 +1774,8 @@ va_status va_run_stage(va_plan_t plan, int32_t stage, const void *q, const void 
         sp.rows_max = plan->rows_max;
         sp.num_blocks = pr.num_blocks;
         const Variant &v = kVariants[plan->rt];
-        launch_fn fn = pr.kv_dtype == VA_DT_FP8_E4M3FN ? v.fp8 : v.bf16;
+        const bool cap = pr.softcap > 0.f;
+        launch_fn fn = pr.kv_dtype == VA_DT_FP8_E4M3FN ? (cap ? v.fp8_cap : v.fp8) : (cap ? v.bf16_cap : v.bf16);
         fn(sp, plan->grid, s);
         if (hipGetLastError() != hipSuccess)
             return VA_ERR_HIP;
@@ -1715,6 +1784,7 @@ va_status va_run_stage(va_plan_t plan, int32_t stage, const void *q, const void 
         MergeParams mp;
         mp.cu = cu_seqlens_q;
         mp.vdesc = v_descale;
+        mp.sinks = sinks;
         mp.ws_o = ws + plan->off_o;
         mp.ws_lse = reinterpret_cast<const float *>(ws + plan->off_lse);
         mp.ws_prefix = reinterpret_cast<const int32_t *>(ws + plan->off_prefix);
@@ -1746,9 +1816,9 @@ va_status va_run(va_plan_t plan, const void *q, const void *k_pool, const void *
                  const float *v_descale, void *out, void *workspace, size_t workspace_bytes,
                  void *stream)
 {
-    return va_run_stage(plan, VA_STAGE_ALL, q, k_pool, v_pool, block_table, cu_seqlens_q,
-                        seqused_k, softmax_scale, k_descale, v_descale, out, workspace,
-                        workspace_bytes, stream);
+    return va_run_ex(plan, VA_STAGE_ALL, q, k_pool, v_pool, block_table, cu_seqlens_q,
+                     seqused_k, softmax_scale, k_descale, v_descale, nullptr, out, workspace,
+                     workspace_bytes, stream);
 }
 
 va_status va_fp8_to_bf16(const uint8_t *in, uint16_t *out, int64_t n, void *stream)

@@ -36,6 +36,7 @@ def to_device(p, device="cuda"):
         sk=torch.from_numpy(p.seqused_k).to(device),
         kd=torch.tensor([p.k_descale], dtype=torch.float32, device=device),
         vd=torch.tensor([p.v_descale], dtype=torch.float32, device=device),
+        sinks=None if getattr(p, "sinks", None) is None else torch.from_numpy(p.sinks).to(device),
     )
     assert d["k"].dtype == kv_t
     return d
@@ -50,7 +51,7 @@ def run(p, dev=None, plan=None, out=None, workspace=None, **plan_kw):
     note(f"  run {p.name}: B={p.num_seqs} Hq={p.num_q_heads} Hkv={p.num_kv_heads} "
          f"kv={p.kv_dtype} grid={plan.grid} ws={plan.workspace_bytes}")
     out = plan.run(dev["q"], dev["k"], dev["v"], dev["bt"], dev["cu"], dev["sk"], p.scale,
-                   dev["kd"], dev["vd"], out=out, workspace=workspace)
+                   dev["kd"], dev["vd"], out=out, workspace=workspace, sinks=dev["sinks"])
     torch.cuda.synchronize()
     return out
 

@@ -104,7 +104,17 @@ def test_run_rejects_null_pointers_and_short_workspace():
     assert lib.va_run(*_run_args(plan, n, ws=ctypes.c_void_p(0x10010))) == va.VA_ERR_INVALID_ARG
     assert lib.va_run(*_run_args(plan, n, q=ctypes.c_void_p(0x10002))) == va.VA_ERR_INVALID_ARG
     assert lib.va_run(None, *_run_args(plan, n)[1:]) == va.VA_ERR_INVALID_ARG
-    assert lib.va_run_stage(plan._h, 7, *_run_args(plan, n)[1:]) == va.VA_ERR_INVALID_ARG
+    a = _run_args(plan, n)
+    ex = (plan._h, 7) + a[1:10] + (None,) + a[10:]          # va_run_ex: stage, ..., sinks, ...
+    assert lib.va_run_ex(*ex) == va.VA_ERR_INVALID_ARG
+
+
+def test_plan_checks_window_and_softcap():
+    for kw in (dict(window_left=-2), dict(softcap=-1.0), dict(softcap=float("nan"))):
+        with pytest.raises(va.VaError) as e:
+            va.Plan(**base_problem(), **kw)
+        assert e.value.status == va.VA_ERR_INVALID_ARG
+    assert va.Plan(**base_problem(), window_left=0, softcap=30.0).grid == 256
 
 
 def test_status_strings():
