@@ -43,15 +43,19 @@ COMPUTE_DTYPE = {"fp8": "fp8/bf16", "bf16": "bf16"}
 
 def algorithmic_bytes(p, seqs=None) -> int:
     """Unique KV pages referenced within seqused_k (K and V, each page once per
-    kv head) plus Q and O bytes, optionally restricted to some sequences."""
+    kv head) plus Q and O bytes, optionally restricted to some sequences.  With
+    a sliding window only the pages some query row can see count."""
     elt = 1 if p.kv_dtype == "fp8" else 2
     idx = np.arange(p.num_seqs) if seqs is None else np.asarray(seqs)
+    wl = getattr(p, "window_left", -1)
     pages = 0
     rows = 0
     for b in idx:
         lq = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
+        lk = int(p.seqused_k[b])
         if lq > 0:
-            pages += -(-int(p.seqused_k[b]) // p.page_size)
+            first = 0 if wl < 0 else max(0, lk - lq - wl) // p.page_size
+            pages += -(-lk // p.page_size) - first
             rows += lq
     kv = pages * p.num_kv_heads * p.page_size * p.head_dim * elt * 2
     qo = rows * p.num_q_heads * p.head_dim * 2 * 2
@@ -117,6 +121,10 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="KV pool copies to rotate over")
     ap.add_argument("--grid", type=int, default=0, help="force the split-KV grid (0 = plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--window", type=int, default=-1,
+                    help="sliding window size (keys a query sees, itself included; -1 = none)")
+    ap.add_argument("--softcap", type=float, default=0.0, help="logit softcap (0 = none)")
+    ap.add_argument("--sinks", action="store_true", help="add one sink logit per query head")
     ap.add_argument("--stage", choices=["all", "split", "merge"], default="all",
                     help="profiling aid: time only one kernel per step")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -152,6 +160,18 @@ def main():
     t0 = time.perf_counter()
     p = va_inputs.config(args.config, args.variant)
     workload = va_inputs.CONFIG_NAMES[args.config] if args.config != 4 else p.name
+    features = []
+    if args.window > 0:
+        p.window_left = args.window - 1
+        features.append(f"window {args.window}")
+    if args.softcap > 0:
+        p.softcap = float(np.float32(args.softcap))
+        features.append(f"softcap {args.softcap:g}")
+    if args.sinks:
+        p.sinks = np.linspace(-1.0, 1.0, p.num_q_heads).astype(np.float32)
+        features.append("sinks")
+    if features:
+        workload += " + " + ", ".join(features)
     log(f"bench: generated {p.name} in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
     q = torch.from_numpy(p.q.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -170,6 +190,7 @@ def main():
     sk = torch.from_numpy(p.seqused_k).to(dev)
     kd = torch.tensor([p.k_descale], dtype=torch.float32, device=dev)
     vd = torch.tensor([p.v_descale], dtype=torch.float32, device=dev)
+    sinks = None if p.sinks is None else torch.from_numpy(p.sinks).to(dev)
     plan = va.Plan.for_problem(p, force_grid=args.grid)
     ws = plan.workspace(dev)
     out = torch.empty_like(q)
@@ -184,7 +205,7 @@ def main():
         c = i % args.copies
         for s in stage_list:
             plan.run(q, ks[c], vs[c], bt, cu, sk, p.scale, kd, vd, out=out, workspace=ws,
-                     stream=stream, stage=s)
+                     stream=stream, stage=s, sinks=sinks)
 
     def timed(n, first, stage_list=stages):
         """Average ms per step over n back-to-back steps, HIP events on `stream`
@@ -201,7 +222,7 @@ def main():
 
     if args.stage == "merge":      # the merge reads what a split pass left in the workspace
         plan.run(q, ks[0], vs[0], bt, cu, sk, p.scale, kd, vd, out=out, workspace=ws,
-                 stream=stream, stage=va.VA_STAGE_SPLIT_KV)
+                 stream=stream, stage=va.VA_STAGE_SPLIT_KV, sinks=sinks)
     t_w = time.perf_counter()
     n_warm = 0
     while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:

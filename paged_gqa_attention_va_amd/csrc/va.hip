@@ -351,7 +351,7 @@ __device__ __forceinline__ void qk_step(floatx4_t (&S)[2][RTW], const StepRegs<K
 __device__ __forceinline__ float softcap_log2(float x, float C)
 {
     const float e = exp2_fast(x * (2.8853900817779268f / C));     // e^(2 x / C) = 2^(2 log2(e) x / C)
-    return C - 2.0f * C / (e + 1.0f);
+    return C - (2.0f * C) * __builtin_amdgcn_rcpf(e + 1.0f);      // v_rcp_f32 (1 ulp): rcp(inf) = 0
 }
 
 template <int RTW, bool CAP>
