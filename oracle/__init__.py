@@ -164,3 +164,28 @@ def attn_problem(p, rows=None, segments=None, threads=None, lib=None):
                 rows=rows, segments=segments, threads=threads, lib=lib,
                 window_left=getattr(p, "window_left", -1), softcap=getattr(p, "softcap", 0.0),
                 sinks=None if getattr(p, "sinks", None) is None else p.sinks.astype(np.float64))
+
+
+def spec_block_table(kv_indptr, kv_indices, page_size: int, max_blocks_per_seq: int):
+    """Block table and KV lengths of a draft-extend (KV catch-up) call, from
+    speculative-decoding metadata.
+
+    The PR #30105 summary page ("Key source snippets", draft_extend_v2 routed to
+    the verify kernel) builds a 2D page table from the spec metadata and takes
+    each sequence's KV length as the kv_indptr difference.  Reading: kv_indices
+    lists, per sequence, the pool slot of every KV token in order (slot = page *
+    page_size + offset, pages filled from offset 0), so page p of sequence b is
+    the slot of its token p * page_size divided by page_size.  Plain loops;
+    entries past a sequence's last page are 0.
+    """
+    kv_indptr = np.asarray(kv_indptr, dtype=np.int64)
+    kv_indices = np.asarray(kv_indices, dtype=np.int64)
+    B = kv_indptr.shape[0] - 1
+    bt = np.zeros((B, max_blocks_per_seq), dtype=np.int32)
+    seqused = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        n = int(kv_indptr[b + 1] - kv_indptr[b])
+        seqused[b] = n
+        for pg in range(-(-n // page_size)):
+            bt[b, pg] = int(kv_indices[kv_indptr[b] + pg * page_size]) // page_size
+    return bt, seqused

