@@ -125,6 +125,9 @@ def main():
                     help="sliding window size (keys a query sees, itself included; -1 = none)")
     ap.add_argument("--softcap", type=float, default=0.0, help="logit softcap (0 = none)")
     ap.add_argument("--sinks", action="store_true", help="add one sink logit per query head")
+    ap.add_argument("--draft-extend", action="store_true",
+                    help="draft-extend call: each step first builds the block table and seqused_k "
+                         "from kv_indptr / kv_indices on the device (va_spec_block_table)")
     ap.add_argument("--stage", choices=["all", "split", "merge"], default="all",
                     help="profiling aid: time only one kernel per step")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -170,6 +173,8 @@ def main():
     if args.sinks:
         p.sinks = np.linspace(-1.0, 1.0, p.num_q_heads).astype(np.float32)
         features.append("sinks")
+    if args.draft_extend:
+        features.append("draft-extend metadata")
     if features:
         workload += " + " + ", ".join(features)
     log(f"bench: generated {p.name} in {time.perf_counter() - t0:.1f} s")
@@ -191,6 +196,16 @@ def main():
     kd = torch.tensor([p.k_descale], dtype=torch.float32, device=dev)
     vd = torch.tensor([p.v_descale], dtype=torch.float32, device=dev)
     sinks = None if p.sinks is None else torch.from_numpy(p.sinks).to(dev)
+    if args.draft_extend:                 # every KV token's pool slot, sequence by sequence
+        indptr = np.zeros(p.num_seqs + 1, dtype=np.int32)
+        slots = []
+        for b in range(p.num_seqs):
+            n = int(p.seqused_k[b])
+            indptr[b + 1] = indptr[b] + n
+            j = np.arange(n)
+            slots.append(p.block_table[b, j // p.page_size].astype(np.int64) * p.page_size + j % p.page_size)
+        kv_indptr = torch.from_numpy(indptr).to(dev)
+        kv_indices = torch.from_numpy(np.concatenate(slots).astype(np.int32)).to(dev)
     plan = va.Plan.for_problem(p, force_grid=args.grid)
     ws = plan.workspace(dev)
     out = torch.empty_like(q)
@@ -203,8 +218,12 @@ def main():
 
     def step(i, stage_list=stages):
         c = i % args.copies
+        bt_i, sk_i = bt, sk
+        if args.draft_extend:
+            bt_i, sk_i = va.spec_block_table(kv_indptr, kv_indices, p.block_table.shape[1],
+                                             p.page_size, stream=stream)
         for s in stage_list:
-            plan.run(q, ks[c], vs[c], bt, cu, sk, p.scale, kd, vd, out=out, workspace=ws,
+            plan.run(q, ks[c], vs[c], bt_i, cu, sk_i, p.scale, kd, vd, out=out, workspace=ws,
                      stream=stream, stage=s, sinks=sinks)
 
     def timed(n, first, stage_list=stages):

@@ -181,6 +181,28 @@ void va_plan_destroy(va_plan_t plan);
 const char *va_status_str(va_status status);
 
 /*
+ * Draft-extend (EAGLE-style KV catch-up) metadata, converted on the device into
+ * the block_table / seqused_k that va_run takes, so that call runs through the
+ * same kernels as target verification.  This is the PR #30105 summary page's
+ * draft_extend_v2 routing ("Key source snippets": seqused_k is the kv_indptr
+ * difference; a 2D page table is built from the spec metadata).
+ *   kv_indptr   [num_seqs + 1] int32, prefix sums of the KV token counts
+ *   kv_indices  int32 pool slot of every KV token, sequence by sequence
+ *               (slot = page * page_size + offset; pages are filled from
+ *               offset 0, as a paged allocator hands them out)
+ *   block_table [num_seqs, max_blocks_per_seq] int32, written: entry p = the
+ *               page of token p * page_size, 0 past the sequence's last page
+ *   seqused_k   [num_seqs] int32, written: kv_indptr[b + 1] - kv_indptr[b]
+ * All pointers are device pointers; one kernel is enqueued on `stream`.  A
+ * sequence longer than max_blocks_per_seq pages gets only the first pages
+ * (invalid device data).  Errors: VA_ERR_INVALID_ARG (null pointer, sizes < 1),
+ * VA_ERR_HIP.
+ */
+va_status va_spec_block_table(const int32_t *kv_indptr, const int32_t *kv_indices, int32_t num_seqs,
+                              int32_t page_size, int32_t max_blocks_per_seq, int32_t *block_table,
+                              int32_t *seqused_k, void *stream);
+
+/*
  * Decode n fp8 e4m3fn bytes to bf16 bits on the device, with the same in-register
  * conversion the attention kernel uses on K and V.  It is a diagnostic that
  * checks the dequant step over all 256 codes.  Both pointers are device

@@ -27,7 +27,7 @@ VA_DT_BF16, VA_DT_FP8_E4M3FN = 1, 2
 VA_STAGE_ALL, VA_STAGE_SPLIT_KV, VA_STAGE_MERGE = 0, 1, 2
 
 EXPORTED = ("va_plan", "va_plan_workspace_bytes", "va_plan_grid", "va_run", "va_run_ex",
-            "va_plan_destroy", "va_status_str", "va_fp8_to_bf16")
+            "va_plan_destroy", "va_status_str", "va_fp8_to_bf16", "va_spec_block_table")
 
 _lib = None
 
@@ -76,6 +76,8 @@ def library(path: str = LIB_PATH):
     lib.va_plan_destroy.argtypes = [P]
     lib.va_status_str.restype = ctypes.c_char_p
     lib.va_status_str.argtypes = [ctypes.c_int]
+    lib.va_spec_block_table.restype = ctypes.c_int
+    lib.va_spec_block_table.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P]
     lib.va_fp8_to_bf16.restype = ctypes.c_int
     lib.va_fp8_to_bf16.argtypes = [P, P, ctypes.c_int64, P]
     if path == LIB_PATH:
@@ -223,3 +225,25 @@ def build(verbose: bool = False) -> str:
     global _lib
     _lib = None
     return _b.build(verbose=verbose)
+
+
+def spec_block_table(kv_indptr, kv_indices, max_blocks_per_seq: int, page_size: int = 16,
+                     stream=None):
+    """Device block table and seqused_k of a draft-extend call from its spec
+    metadata (kv_indptr [B+1], kv_indices: int32 device tensors)."""
+    import torch
+    lib = library()
+    B = kv_indptr.numel() - 1
+    for t in (kv_indptr, kv_indices):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("kv_indptr and kv_indices must be contiguous int32 device tensors")
+    bt = torch.empty((B, max_blocks_per_seq), dtype=torch.int32, device=kv_indptr.device)
+    sk = torch.empty((B,), dtype=torch.int32, device=kv_indptr.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(kv_indptr.device)
+    idx = kv_indices if kv_indices.numel() else torch.zeros(1, dtype=torch.int32, device=kv_indptr.device)
+    _check(lib.va_spec_block_table(ctypes.c_void_p(kv_indptr.data_ptr()), ctypes.c_void_p(idx.data_ptr()),
+                                   B, page_size, max_blocks_per_seq, ctypes.c_void_p(bt.data_ptr()),
+                                   ctypes.c_void_p(sk.data_ptr()), ctypes.c_void_p(stream.cuda_stream)),
+           "va_spec_block_table")
+    return bt, sk

@@ -1538,6 +1538,27 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
     *reinterpret_cast<uint2 *>(p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + d) = pk;
 }
 
+// Draft-extend metadata: one thread per block-table entry (b, page).  Page pg
+// of sequence b is the pool page of its token pg * page_size, whose slot is
+// kv_indices[kv_indptr[b] + pg * page_size]; the page-0 thread also writes
+// seqused_k[b] = kv_indptr[b + 1] - kv_indptr[b].
+__global__ __launch_bounds__(kThreads) void va_spec_block_table_kernel(const int32_t *indptr, const int32_t *indices,
+                                                                       int32_t num_seqs, int32_t page_size,
+                                                                       int32_t mbps, int32_t *bt, int32_t *seqused)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= (int64_t)num_seqs * mbps)
+        return;
+    const int b = (int)(i / mbps);
+    const int pg = (int)(i - (int64_t)b * mbps);
+    const int64_t t0 = indptr[b];
+    const int64_t n = (int64_t)indptr[b + 1] - t0;
+    if (pg == 0)
+        seqused[b] = (int32_t)n;
+    const int64_t tok = (int64_t)pg * page_size;
+    bt[i] = tok < n ? indices[t0 + tok] / page_size : 0;
+}
+
 __global__ __launch_bounds__(kThreads) void va_fp8_to_bf16_kernel(const uint8_t *in, uint16_t *out, int64_t n)
 {
     const int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
@@ -1819,6 +1840,23 @@ va_status va_run(va_plan_t plan, const void *q, const void *k_pool, const void *
     return va_run_ex(plan, VA_STAGE_ALL, q, k_pool, v_pool, block_table, cu_seqlens_q,
                      seqused_k, softmax_scale, k_descale, v_descale, nullptr, out, workspace,
                      workspace_bytes, stream);
+}
+
+va_status va_spec_block_table(const int32_t *kv_indptr, const int32_t *kv_indices, int32_t num_seqs,
+                              int32_t page_size, int32_t max_blocks_per_seq, int32_t *block_table,
+                              int32_t *seqused_k, void *stream)
+{
+    if (!kv_indptr || !kv_indices || !block_table || !seqused_k || num_seqs < 1 || page_size < 1 ||
+        max_blocks_per_seq < 1)
+        return VA_ERR_INVALID_ARG;
+    const int64_t n = (int64_t)num_seqs * max_blocks_per_seq;
+    const int64_t blocks = (n + kThreads - 1) / kThreads;
+    if (blocks > INT32_MAX)
+        return VA_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(va_spec_block_table_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), kv_indptr, kv_indices, num_seqs, page_size,
+                       max_blocks_per_seq, block_table, seqused_k);
+    return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
 va_status va_fp8_to_bf16(const uint8_t *in, uint16_t *out, int64_t n, void *stream)

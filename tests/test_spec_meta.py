@@ -48,3 +48,28 @@ def test_page_ids_come_from_the_first_token_of_each_page():
     bt, sk = oracle.spec_block_table(indptr, idx, 16, 3)
     assert sk.tolist() == [19, 0, 1]
     assert bt.tolist() == [[5, 2, 0], [0, 0, 0], [7, 0, 0]]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", [
+    ([4, 2], [1024, 769], 16, 1, "fp8"),
+    ([1, 3, 2, 4], [5000, 17, 1, 2049], 16, 1, "fp8"),
+    ([3, 3], [700, 1300], 8, 2, "bf16"),
+])
+def test_device_conversion_and_attention_through_it(case):
+    import torch
+    import paged_gqa_attention_va_amd as va
+    from gpu_util import as_f64, compare, run, to_device
+    ql, kl, hq, hkv, dt = case
+    p = va_inputs.custom(ql, kl, hq, hkv, dt, seed=sum(kl), name="draft-extend")
+    indptr, idx = token_slots(p)
+    mbps = p.block_table.shape[1]
+    ref_bt, ref_sk = oracle.spec_block_table(indptr, idx, 16, mbps)
+    bt, sk = va.spec_block_table(torch.from_numpy(indptr).cuda(), torch.from_numpy(idx).cuda(), mbps)
+    torch.cuda.synchronize()
+    assert np.array_equal(bt.cpu().numpy(), ref_bt) and np.array_equal(sk.cpu().numpy(), ref_sk)
+    dev = to_device(p)
+    dev["bt"], dev["sk"] = bt, sk                       # attention through the converted metadata
+    out = as_f64(run(p, dev=dev, force_grid=64))
+    ref, _ = oracle.attn_problem(p)
+    compare(out, ref, p.name)
