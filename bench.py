@@ -35,7 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
-MAIN_KERNEL = {"fp8": "va_split_kv_fp8_w8_kernel", "bf16": "va_split_kv_kernel"}
+MAIN_KERNEL = {"fp8": "va_split_kv_fp8_w8_kernel", "bf16": "va_split_kv_bf16_w8_kernel"}
 # Arithmetic of the path: FP8 KV runs QK^T on fp8 MFMA (Q as an exact hi/lo fp8
 # pair) and PV on bf16 MFMA; bf16 KV runs both on bf16 MFMA; fp32 accumulation.
 COMPUTE_DTYPE = {"fp8": "fp8/bf16", "bf16": "bf16"}

@@ -1,17 +1,18 @@
 // va.hip -- paged GQA target-verify attention for MI355X (gfx950 / CDNA4).
 //
-// Two kernels and the host side of the C ABI declared in include/va.h.
+// The kernels and the host side of the C ABI declared in include/va.h.
 //
-//  va_split_kv_kernel   Split-KV main kernel.  Each workgroup takes a contiguous
-//                       share of the flattened page space of all (sequence, kv
-//                       head) pairs.  For each piece it loads every K/V page
-//                       once and reuses it for all G*q_len packed query rows
-//                       (GQA packing).  It dequantises FP8 in registers, runs
-//                       MFMA QK^T and PV with an online softmax, and writes
-//                       either the final rows or a partial (o, lse) per piece.
+//  va_split_kv_fp8_w8_kernel   Split-KV main kernel for an FP8 e4m3 cache.
+//  va_split_kv_bf16_w8_kernel  The same for a bf16 cache.
+//      Each workgroup (8 waves) takes a contiguous share of the flattened page
+//      space of all (sequence, kv head) pairs.  For each piece it copies every
+//      K/V page once, straight from HBM into an LDS ring, and reuses it for all
+//      G*q_len packed query rows (GQA packing); MFMA QK^T and PV with an online
+//      softmax; then either the final rows or a partial (o, lse) per piece.
 //  va_merge_kernel      Segment reduce: log-sum-exp merge of the partials of
 //                       every (sequence, kv head) that was split over
 //                       workgroups.
+//  va_spec_block_table_kernel, va_fp8_to_bf16_kernel   metadata and test helpers.
 //
 // The method comes from the sglang PR #36330 summary page ("Implementation
 // breakdown", item 1: pack the G query heads and speculative tokens of a group
@@ -23,12 +24,9 @@
 //
 // Layout of the packed rows of one (sequence b, kv head g): row r = t*G + h
 // (t = speculative token, h = head within the group), padded to 16-row MFMA
-// tiles.  Each wave computes S^T = K Q^T and O^T = V^T P^T with
-// v_mfma_f32_16x16x32_bf16.  Then:
+// tiles.  Each wave computes S^T = K Q^T and O^T = V^T P^T, so
 //   - the S^T accumulator already is the P^T B-operand, so no shuffle is needed;
-//   - row statistics (max, sum) stay inside one lane column;
-//   - the K and V operands are loaded straight from HBM into registers in
-//     operand order, with 64- and 256-byte contiguous runs per key row.
+//   - row statistics (max, sum) stay inside one lane column.
 //
 // Stream-K partition: WG w of N handles flat pages [floor(w*P/N),
 // floor((w+1)*P/N)) where P is the total page count, computed on the device from
@@ -54,8 +52,7 @@ typedef int intx8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kHeadDim = 256;
 constexpr int kPage = 16;
-constexpr int kThreads = 256;            // 4 waves of 64
-constexpr int kWaves = 4;
+constexpr int kThreads = 256;            // merge and helper kernels: 4 waves of 64
 // Online-softmax rescale threshold (log2 units).  The running max m is only
 // moved when a new logit exceeds it by more than kTau.  Then p = 2^(x - m) <= 2^8
 // and O, l stay exact up to rounding; the final O/l does not depend on m.
@@ -198,101 +195,9 @@ __device__ __forceinline__ int pages_of(const int32_t *cu, const int32_t *sequse
     return max(0, min((lk + kPage - 1) / kPage, mbps) - first_page(lk, lq, wl));
 }
 
-// ----------------------------------------------------------- K/V loading --
-
-// Raw K/V registers of one step: two pages (32 keys) of one kv head.
-//  K (fp8): lane (n = l%16, j = l/16) holds key n of each page, bytes
-//           [16(4i+j), +16) for i = 0..3 (the 4 uint4).  k-step s = 2i+h of the
-//           QK MFMA uses dims 16(4i+j) + 8h .. +8 in lane group j.
-//  K (bf16): 8 uint4 per page, uint4 s = bytes [16(4s+j), +16) = dims 8(4s+j) .. +8.
-//  V (fp8): lane (m = l%16, j) holds, for e = 0..7, the 16 bytes of dims
-//           16m .. 16m+15 of key slot 4j + e%4 of page e/4.
-//  V (bf16): same keys, 32 bytes (2 uint4) per key.
-template <int KVT>
-struct StepRegs {
-    static constexpr int kK = KVT == kKvFp8 ? 4 : 8;   // uint4 per page of K per lane
-    static constexpr int kV = KVT == kKvFp8 ? 1 : 2;   // uint4 per key of V per lane
-    uint4 k[2][kK];
-    uint4 v[8][kV];
-};
-
-template <int KVT>
-__device__ __forceinline__ void load_k(StepRegs<KVT> &r, const uint8_t *kbase, int64_t phys_a,
-                                       int64_t phys_b, bool has_b, int hkv, int lane)
-{
-    constexpr int elt = KVT == kKvFp8 ? 1 : 2;
-    const int n = lane & 15, j = lane >> 4;
-    const int64_t row_bytes = (int64_t)kHeadDim * elt;
-    const uint8_t *ra = kbase + ((phys_a * kPage + n) * hkv) * row_bytes;
-#pragma unroll
-    for (int i = 0; i < StepRegs<KVT>::kK; ++i)
-        r.k[0][i] = *(const uint4 *)(ra + (4 * i + j) * 16);
-    if (has_b) {
-        const uint8_t *rb = kbase + ((phys_b * kPage + n) * hkv) * row_bytes;
-#pragma unroll
-        for (int i = 0; i < StepRegs<KVT>::kK; ++i)
-            r.k[1][i] = *(const uint4 *)(rb + (4 * i + j) * 16);
-    } else {
-#pragma unroll
-        for (int i = 0; i < StepRegs<KVT>::kK; ++i)
-            r.k[1][i] = make_uint4(0, 0, 0, 0);
-    }
-}
-
-template <int KVT>
-__device__ __forceinline__ void load_v(StepRegs<KVT> &r, const uint8_t *vbase, int64_t phys_a,
-                                       int64_t phys_b, bool has_b, int hkv, int lane)
-{
-    constexpr int elt = KVT == kKvFp8 ? 1 : 2;
-    constexpr int kV = StepRegs<KVT>::kV;
-    const int m = lane & 15, j = lane >> 4;
-    const int64_t row_bytes = (int64_t)kHeadDim * elt;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const uint8_t *ra = vbase + ((phys_a * kPage + 4 * j + e) * hkv) * row_bytes + m * 16 * kV;
-#pragma unroll
-        for (int c = 0; c < kV; ++c)
-            r.v[e][c] = *(const uint4 *)(ra + 16 * c);
-    }
-    if (has_b) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint8_t *rb = vbase + ((phys_b * kPage + 4 * j + e) * hkv) * row_bytes + m * 16 * kV;
-#pragma unroll
-            for (int c = 0; c < kV; ++c)
-                r.v[4 + e][c] = *(const uint4 *)(rb + 16 * c);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int c = 0; c < kV; ++c)
-                r.v[4 + e][c] = make_uint4(0, 0, 0, 0);
-    }
-}
-
 __device__ __forceinline__ uint32_t u4get(const uint4 &u, int i)
 {
     return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
-
-// K operand (16 keys x 32 dims, bf16) of k-step s for page a.
-template <int KVT>
-__device__ __forceinline__ bf16x8_t k_operand(const StepRegs<KVT> &r, int a, int s)
-{
-    if constexpr (KVT == kKvFp8) {
-        const uint4 &u = r.k[a][s >> 1];
-        const uint32_t w0 = (s & 1) ? u.z : u.x;
-        const uint32_t w1 = (s & 1) ? u.w : u.y;
-        uint4 o;
-        o.x = fp8x2_lo_to_bf16x2(w0);
-        o.y = fp8x2_hi_to_bf16x2(w0);
-        o.z = fp8x2_lo_to_bf16x2(w1);
-        o.w = fp8x2_hi_to_bf16x2(w1);
-        return __builtin_bit_cast(bf16x8_t, o);
-    } else {
-        return __builtin_bit_cast(bf16x8_t, r.k[a][s]);
-    }
 }
 
 // ------------------------------------------------------- per-step compute --
@@ -305,37 +210,6 @@ struct RowState {
     float l[RTW];           // this lane's partial sum of 2^(x - m)
 };
 
-// QK half of a 32-key step: S^T[a][rt] = K(page a) Q^T(rt), 16 keys x 16 rows each.
-//   qs  LDS Q operands of this wave's row tiles: [rt][s][lane] uint4
-template <int RTW, int KVT>
-__device__ __forceinline__ void qk_step(floatx4_t (&S)[2][RTW], const StepRegs<KVT> &r,
-                                        const uint4 *qs, int lane)
-{
-    // The Q operand reads are loop-invariant LDS reads; keep them here rather
-    // than letting them be hoisted out of the page loop (that would pin
-    // RTW*32 registers for the whole loop).
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt)
-            S[a][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        bf16x8_t qop[RTW];
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt)
-            qop[rt] = __builtin_bit_cast(bf16x8_t, qs[(rt * 8 + s) * 64 + lane]);
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            const bf16x8_t kop = k_operand<KVT>(r, a, s);
-#pragma unroll
-            for (int rt = 0; rt < RTW; ++rt)
-                S[a][rt] = mfma16(kop, qop[rt], S[a][rt]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
 
 // Softmax part of a 32-key step: online softmax on S^T; returns the P^T
 // B-operands (bf16) of this wave's row tiles.
@@ -444,60 +318,6 @@ __device__ __forceinline__ uint32_t v_zero_mask(int key0, bool has_b, int key_en
     return z;
 }
 
-// PV from V rows in registers (v[e] = dims 16m .. 16m+15 of key slot 4j + e%4
-// of page e/4): O^T += V^T P^T.  V^T operand of dim tile t = dims {16m + t}.
-template <int RTW, int KVT>
-__device__ __forceinline__ void pv_regs(RowState<RTW> &st, StepRegs<KVT> &r, const bf16x8_t (&pop)[RTW],
-                                        uint32_t zmask)
-{
-    if (zmask) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (zmask & (1u << e))
-#pragma unroll
-                for (int cc = 0; cc < StepRegs<KVT>::kV; ++cc)
-                    r.v[e][cc] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        uint32_t A[4][4];      // [x][kp]: tile 4q+x, key pair kp
-        if constexpr (KVT == kKvFp8) {
-#pragma unroll
-            for (int kp = 0; kp < 4; ++kp) {
-                const uint32_t X = u4get(r.v[2 * kp][0], q);
-                const uint32_t Y = u4get(r.v[2 * kp + 1][0], q);
-                const uint32_t lo = byte_perm(Y, X, 0x05010400u);   // X0 Y0 X1 Y1
-                const uint32_t hi = byte_perm(Y, X, 0x07030602u);   // X2 Y2 X3 Y3
-                A[0][kp] = fp8x2_lo_to_bf16x2(lo);
-                A[1][kp] = fp8x2_hi_to_bf16x2(lo);
-                A[2][kp] = fp8x2_lo_to_bf16x2(hi);
-                A[3][kp] = fp8x2_hi_to_bf16x2(hi);
-            }
-        } else {
-            // dims 4q..4q+3 of the lane's 16: uint4 c = q/2, dwords 2(q%2), 2(q%2)+1
-#pragma unroll
-            for (int kp = 0; kp < 4; ++kp) {
-                const int cc = q >> 1;
-                const uint32_t X0 = u4get(r.v[2 * kp][cc], 2 * (q & 1));
-                const uint32_t Y0 = u4get(r.v[2 * kp + 1][cc], 2 * (q & 1));
-                const uint32_t X1 = u4get(r.v[2 * kp][cc], 2 * (q & 1) + 1);
-                const uint32_t Y1 = u4get(r.v[2 * kp + 1][cc], 2 * (q & 1) + 1);
-                A[0][kp] = byte_perm(Y0, X0, 0x05040100u);   // X.lo Y.lo
-                A[1][kp] = byte_perm(Y0, X0, 0x07060302u);   // X.hi Y.hi
-                A[2][kp] = byte_perm(Y1, X1, 0x05040100u);
-                A[3][kp] = byte_perm(Y1, X1, 0x07060302u);
-            }
-        }
-#pragma unroll
-        for (int xx = 0; xx < 4; ++xx) {
-            const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, make_uint4(A[xx][0], A[xx][1], A[xx][2], A[xx][3]));
-#pragma unroll
-            for (int rt = 0; rt < RTW; ++rt)
-                st.o[4 * q + xx][rt] = mfma16(vop, pop[rt], st.o[4 * q + xx][rt]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
 
 // PV with FP8 V rows read from a ring stage, 8 bytes (dims 8h .. 8h+7 of the
 // lane's 16) of each of the 8 keys at a time, so only 16 registers of raw V
@@ -629,266 +449,6 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
         p.ws_meta[0] = sh.n_eff;
     }
     return sh;
-}
-
-// -------------------------------------------------------------- the kernel --
-
-// RTW: row tiles per wave; NR: row groups (waves sharing the same keys for
-// different rows); NG = 4 / NR key groups splitting each piece's page pairs.
-template <int RTW, int NR, int KVT, bool CAP>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
-void va_split_kv_kernel(SplitParams p)
-{
-    constexpr int NG = kWaves / NR;
-    constexpr int RT = RTW * NR;                       // row tiles per piece
-    constexpr int kQBytes = RT * 8 * 64 * 16;
-    constexpr int kMergeSlot = (64 * 64 + 2 * 64) * 4;   // one row tile of one wave: O^T, m, l
-    constexpr int kMergeBytes = (NG - 1) * NR * kMergeSlot;
-    constexpr int kLds = kQBytes > kMergeBytes ? kQBytes : kMergeBytes;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
-    uint4 *qs_all = reinterpret_cast<uint4 *>(lds);
-
-    const int lane = threadIdx.x & 63;
-    const int wave = uniform(threadIdx.x >> 6);
-    const int rg = wave % NR;
-    const int kg = wave / NR;
-    const int w = blockIdx.x;
-    const int G = 1 << p.log2g;
-
-    Share sh = locate(p, w, lane, w == 0 && wave == 0);
-    sh.n_eff = uniform(sh.n_eff);
-    sh.s = uniform(sh.s);
-    sh.e = uniform(sh.e);
-    sh.bg = uniform(sh.bg);
-    sh.base = uniform(sh.base);
-    if (w >= sh.n_eff)
-        return;                                        // uniform over the workgroup
-
-    const float kd = p.kdesc ? p.kdesc[0] : 1.0f;
-    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
-    const float c = p.scale_log2 * kd;
-    constexpr int elt = KVT == kKvFp8 ? 1 : 2;
-    const uint4 *qs_wave = qs_all + rg * RTW * 8 * 64;
-
-    const int bh = p.num_seqs * p.hkv;
-    int s = sh.s, bg = sh.bg, base = sh.base;
-    while (s < sh.e && bg < bh) {
-        const int cnt = uniform(pages_of(p.cu, p.seqused, p.hkv, p.mbps, p.window_left, bg));
-        if (cnt == 0) {
-            ++bg;
-            continue;
-        }
-        const int b = bg / p.hkv;
-        const int g = bg - b * p.hkv;
-        const int q0 = uniform(p.cu[b]);
-        const int lq = uniform(p.cu[b + 1]) - q0;
-        const int lk = uniform(p.seqused[b]);
-        const int ctx = lk - lq;
-        const int r0 = s - base;                               // piece = pages r0 .. r1 of the pair's range
-        const int r1 = min(sh.e, base + cnt) - base;
-        const bool whole = (r0 == 0 && r1 == cnt);
-        const int pb = first_page(lk, lq, p.window_left);      // the range starts at logical page pb
-        const int p0 = pb + r0, p1 = pb + r1;
-        const int slot = w + bg;
-        const int lo_max = p.window_left < 0 ? INT_MIN : ctx + lq - 1 - p.window_left;
-        const uint32_t wlim = p.window_left < 0 ? 0x7FFFFFFFu : (uint32_t)p.window_left;
-
-        // ---- stage this piece's packed Q rows in LDS, in operand order
-        __syncthreads();                                // previous piece's merge reads done
-        for (int u = threadIdx.x; u < RT * 512; u += kThreads) {
-            const int rt = u >> 9, ss = (u >> 6) & 7, l = u & 63;
-            const int row = rt * 16 + (l & 15), jj = l >> 4;
-            const int dim = KVT == kKvFp8 ? (4 * (ss >> 1) + jj) * 16 + 8 * (ss & 1) : (4 * ss + jj) * 8;
-            const int t = row >> p.log2g, h = row & (G - 1);
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (t < lq)
-                val = *(const uint4 *)(p.q + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + dim);
-            qs_all[u] = val;
-        }
-        __syncthreads();
-
-        // ---- per-wave state
-        RowState<RTW> st;
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt) {
-            st.m[rt] = -INFINITY;
-            st.l[rt] = 0.f;
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-                st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        int limit[RTW];
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt) {
-            const int row = (rg * RTW + rt) * 16 + (lane & 15);
-            const int t = row >> p.log2g;
-            limit[rt] = min(ctx + t, lk - 1);
-        }
-
-        const int npairs = (p1 - p0 + 1) >> 1;
-        const bool rows_live = (rg * RTW * 16) < lq * G;
-        if (rows_live && kg < npairs) {
-            const int32_t *btrow = p.bt + (int64_t)b * p.mbps;
-            const uint8_t *kbase = p.k + (int64_t)g * kHeadDim * elt;
-            const uint8_t *vbase = p.v + (int64_t)g * kHeadDim * elt;
-            const int64_t maxpage = p.num_blocks - 1;
-            auto phys = [&](int page) -> int64_t {
-                int64_t v = btrow[page];
-                v = v < 0 ? 0 : v;
-                return v > maxpage ? maxpage : v;
-            };
-            // One register set.  K of the next step is issued as soon as this
-            // step's QK has consumed K, V of the next step as soon as PV has
-            // consumed V, so half of every step's loads overlap compute.
-            StepRegs<KVT> r;
-            int k = kg;
-            int pa = p0 + 2 * k;
-            bool hb = pa + 1 < p1;
-            int64_t ya = phys(pa), yb = hb ? phys(pa + 1) : ya;
-            load_k<KVT>(r, kbase, ya, yb, hb, p.hkv, lane);
-            load_v<KVT>(r, vbase, ya, yb, hb, p.hkv, lane);
-            while (true) {
-                floatx4_t S[2][RTW];
-                qk_step<RTW, KVT>(S, r, qs_wave, lane);
-                const int kn = k + NG;
-                const int pn = p0 + 2 * kn;
-                const bool hn = pn + 1 < p1;
-                const bool more = kn < npairs;
-                int64_t yna = 0, ynb = 0;
-                if (more) {
-                    yna = phys(pn);
-                    ynb = hn ? phys(pn + 1) : yna;
-                    load_k<KVT>(r, kbase, yna, ynb, hn, p.hkv, lane);
-                }
-                const int key0 = pa * kPage;
-                const bool masked = !hb || key0 + 31 > ctx || key0 < lo_max;
-                bf16x8_t pop[RTW];
-                {
-                    float cr[RTW];
-#pragma unroll
-                    for (int rt = 0; rt < RTW; ++rt)
-                        cr[rt] = c;
-                    softmax_step<RTW, CAP>(st, pop, S, limit, wlim, key0, hb, cr, p.cap_log2, lane, masked);
-                }
-                pv_regs<RTW, KVT>(st, r, pop, masked ? v_zero_mask(key0, hb, lk, lane) : 0u);
-                if (!more)
-                    break;
-                load_v<KVT>(r, vbase, yna, ynb, hn, p.hkv, lane);
-                k = kn;
-                pa = pn;
-                hb = hn;
-            }
-        }
-
-        // full row sums of this wave (the 4 lane groups share a row)
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt) {
-            float t = st.l[rt];
-            t += __shfl_xor(t, 16);
-            t += __shfl_xor(t, 32);
-            st.l[rt] = t;
-        }
-
-        // ---- merge the NG key groups of each row group through LDS
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt) {
-            __syncthreads();
-            float *slotbuf = reinterpret_cast<float *>(lds) + (size_t)(rg * (NG - 1)) * (kMergeSlot / 4);
-            if (kg > 0) {
-                float *mine = slotbuf + (size_t)(kg - 1) * (kMergeSlot / 4);
-#pragma unroll
-                for (int t = 0; t < 16; ++t)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        mine[(t * 4 + e) * 64 + lane] = st.o[t][rt][e];
-                mine[64 * 64 + lane] = st.m[rt];
-                mine[64 * 64 + 64 + lane] = st.l[rt];
-            }
-            __syncthreads();
-            if (kg == 0) {
-                float mm = st.m[rt];
-#pragma unroll
-                for (int o = 1; o < NG; ++o)
-                    mm = fmaxf(mm, slotbuf[(size_t)(o - 1) * (kMergeSlot / 4) + 64 * 64 + lane]);
-                const float f0 = st.m[rt] == -INFINITY ? 0.f : exp2_fast(st.m[rt] - mm);
-                float L = f0 * st.l[rt];
-#pragma unroll
-                for (int t = 0; t < 16; ++t)
-                    st.o[t][rt] *= f0;
-#pragma unroll
-                for (int o = 1; o < NG; ++o) {
-                    const float *oth = slotbuf + (size_t)(o - 1) * (kMergeSlot / 4);
-                    const float mo = oth[64 * 64 + lane];
-                    const float fo = mo == -INFINITY ? 0.f : exp2_fast(mo - mm);
-                    L += fo * oth[64 * 64 + 64 + lane];
-#pragma unroll
-                    for (int t = 0; t < 16; ++t)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            st.o[t][rt][e] += fo * oth[(t * 4 + e) * 64 + lane];
-                }
-                st.m[rt] = mm;
-                st.l[rt] = L;
-            }
-        }
-
-        // ---- write: final rows for a whole sequence, else a partial
-        if (kg == 0) {
-            const int j = lane >> 4;
-#pragma unroll
-            for (int rt = 0; rt < RTW; ++rt) {
-                const int row = (rg * RTW + rt) * 16 + (lane & 15);
-                const int t = row >> p.log2g;
-                const int h = row & (G - 1);
-                if (t < lq) {
-                    const float L = st.l[rt];
-                    if (whole) {
-                        float inv = L > 0.f ? vd / L : 0.f;
-                        if (p.sinks) {                   // the sink joins the denominator only
-                            const float sk = p.sinks[g * G + h] * 1.4426950408889634f;
-                            const float mm = fmaxf(st.m[rt], sk);
-                            const float f = L > 0.f ? exp2_fast(st.m[rt] - mm) : 0.f;
-                            inv = vd * f / (L * f + exp2_fast(sk - mm));
-                        }
-                        uint16_t *dst = p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            uint4 lo, hi;
-                            lo.x = pack_bf16x2(st.o[0][rt][e] * inv, st.o[1][rt][e] * inv);
-                            lo.y = pack_bf16x2(st.o[2][rt][e] * inv, st.o[3][rt][e] * inv);
-                            lo.z = pack_bf16x2(st.o[4][rt][e] * inv, st.o[5][rt][e] * inv);
-                            lo.w = pack_bf16x2(st.o[6][rt][e] * inv, st.o[7][rt][e] * inv);
-                            hi.x = pack_bf16x2(st.o[8][rt][e] * inv, st.o[9][rt][e] * inv);
-                            hi.y = pack_bf16x2(st.o[10][rt][e] * inv, st.o[11][rt][e] * inv);
-                            hi.z = pack_bf16x2(st.o[12][rt][e] * inv, st.o[13][rt][e] * inv);
-                            hi.w = pack_bf16x2(st.o[14][rt][e] * inv, st.o[15][rt][e] * inv);
-                            uint4 *d4 = reinterpret_cast<uint4 *>(dst + 64 * j + 16 * e);
-                            d4[0] = lo;
-                            d4[1] = hi;
-                        }
-                    } else {
-                        const float inv = L > 0.f ? 1.0f / L : 0.f;
-                        float *dst = static_cast<float *>(p.ws_o) + ((int64_t)slot * p.rows_max + row) * kHeadDim;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            float4 *d4 = reinterpret_cast<float4 *>(dst + 64 * j + 16 * e);
-#pragma unroll
-                            for (int qq = 0; qq < 4; ++qq)
-                                d4[qq] = make_float4(st.o[4 * qq][rt][e] * inv, st.o[4 * qq + 1][rt][e] * inv,
-                                                     st.o[4 * qq + 2][rt][e] * inv, st.o[4 * qq + 3][rt][e] * inv);
-                        }
-                        if (j == 0)
-                            p.ws_lse[(int64_t)slot * p.rows_max + row] =
-                                L > 0.f ? st.m[rt] + __log2f(L) : -INFINITY;
-                    }
-                }
-            }
-        }
-
-        s = base + r1;
-        base += cnt;
-        ++bg;
-    }
 }
 
 // ------------------------------------------------- FP8 kernel, LDS ring --
@@ -1155,7 +715,35 @@ __device__ __forceinline__ float f16_hi(uint32_t w)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-template <int RTW>
+// Key-group exchange format of the epilogue: fp16 (FP8 cache) or bf16 (bf16 cache).
+template <int KVT>
+__device__ __forceinline__ uint32_t xpack(float a, float b)
+{
+    if constexpr (KVT == kKvFp8)
+        return pack_f16x2(a, b);
+    else
+        return pack_bf16x2(a, b);
+}
+
+template <int KVT>
+__device__ __forceinline__ float xlo(uint32_t w)
+{
+    if constexpr (KVT == kKvFp8)
+        return f16_lo(w);
+    else
+        return __builtin_bit_cast(float, w << 16);
+}
+
+template <int KVT>
+__device__ __forceinline__ float xhi(uint32_t w)
+{
+    if constexpr (KVT == kKvFp8)
+        return f16_hi(w);
+    else
+        return __builtin_bit_cast(float, w & 0xFFFF0000u);
+}
+
+template <int RTW, int KVT>
 __device__ __forceinline__ void piece_epilogue(RowState<RTW> &st, unsigned char *lds, unsigned char *obuf,
                                                const SplitParams &p, int kg, int rg, int lane, int lq,
                                                int q0, int g, int slot, bool whole, float vd)
@@ -1185,14 +773,14 @@ __device__ __forceinline__ void piece_epilogue(RowState<RTW> &st, unsigned char 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {                    // dims 64 j + 16 e + t, t = 0..15
             uint4 a, b;
-            a.x = pack_f16x2(st.o[0][rt][e] * inv, st.o[1][rt][e] * inv);
-            a.y = pack_f16x2(st.o[2][rt][e] * inv, st.o[3][rt][e] * inv);
-            a.z = pack_f16x2(st.o[4][rt][e] * inv, st.o[5][rt][e] * inv);
-            a.w = pack_f16x2(st.o[6][rt][e] * inv, st.o[7][rt][e] * inv);
-            b.x = pack_f16x2(st.o[8][rt][e] * inv, st.o[9][rt][e] * inv);
-            b.y = pack_f16x2(st.o[10][rt][e] * inv, st.o[11][rt][e] * inv);
-            b.z = pack_f16x2(st.o[12][rt][e] * inv, st.o[13][rt][e] * inv);
-            b.w = pack_f16x2(st.o[14][rt][e] * inv, st.o[15][rt][e] * inv);
+            a.x = xpack<KVT>(st.o[0][rt][e] * inv, st.o[1][rt][e] * inv);
+            a.y = xpack<KVT>(st.o[2][rt][e] * inv, st.o[3][rt][e] * inv);
+            a.z = xpack<KVT>(st.o[4][rt][e] * inv, st.o[5][rt][e] * inv);
+            a.w = xpack<KVT>(st.o[6][rt][e] * inv, st.o[7][rt][e] * inv);
+            b.x = xpack<KVT>(st.o[8][rt][e] * inv, st.o[9][rt][e] * inv);
+            b.y = xpack<KVT>(st.o[10][rt][e] * inv, st.o[11][rt][e] * inv);
+            b.z = xpack<KVT>(st.o[12][rt][e] * inv, st.o[13][rt][e] * inv);
+            b.w = xpack<KVT>(st.o[14][rt][e] * inv, st.o[15][rt][e] * inv);
             const int c0 = 8 * j + 2 * e;
             *reinterpret_cast<uint4 *>(orow + ((c0 ^ n) * 16)) = a;
             *reinterpret_cast<uint4 *>(orow + (((c0 + 1) ^ n) * 16)) = b;
@@ -1219,14 +807,14 @@ __device__ __forceinline__ void piece_epilogue(RowState<RTW> &st, unsigned char 
             W += w;
             const uint4 v = *reinterpret_cast<const uint4 *>(obuf + (size_t)(k * 64 + r) * 512 +
                                                              ((c ^ (r & 15)) * 16));
-            acc[0] += w * f16_lo(v.x);
-            acc[1] += w * f16_hi(v.x);
-            acc[2] += w * f16_lo(v.y);
-            acc[3] += w * f16_hi(v.y);
-            acc[4] += w * f16_lo(v.z);
-            acc[5] += w * f16_hi(v.z);
-            acc[6] += w * f16_lo(v.w);
-            acc[7] += w * f16_hi(v.w);
+            acc[0] += w * xlo<KVT>(v.x);
+            acc[1] += w * xhi<KVT>(v.x);
+            acc[2] += w * xlo<KVT>(v.y);
+            acc[3] += w * xhi<KVT>(v.y);
+            acc[4] += w * xlo<KVT>(v.z);
+            acc[5] += w * xhi<KVT>(v.z);
+            acc[6] += w * xlo<KVT>(v.w);
+            acc[7] += w * xhi<KVT>(v.w);
         }
         const int t = r >> p.log2g, h = r & (G - 1);
         if (whole) {
@@ -1248,13 +836,19 @@ __device__ __forceinline__ void piece_epilogue(RowState<RTW> &st, unsigned char 
             *reinterpret_cast<uint4 *>(p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + 8 * c) = o;
         } else {
             const float sc = W > 0.f ? 1.0f / W : 0.f;
-            uint4 o;
-            o.x = pack_f16x2(acc[0] * sc, acc[1] * sc);
-            o.y = pack_f16x2(acc[2] * sc, acc[3] * sc);
-            o.z = pack_f16x2(acc[4] * sc, acc[5] * sc);
-            o.w = pack_f16x2(acc[6] * sc, acc[7] * sc);
-            uint16_t *dst = static_cast<uint16_t *>(p.ws_o) + ((int64_t)slot * p.rows_max + r) * kHeadDim + 8 * c;
-            *reinterpret_cast<uint4 *>(dst) = o;
+            const int64_t sr = ((int64_t)slot * p.rows_max + r) * kHeadDim + 8 * c;
+            if constexpr (KVT == kKvFp8) {                  // fp16 partial: |O/l| <= 448
+                uint4 o;
+                o.x = pack_f16x2(acc[0] * sc, acc[1] * sc);
+                o.y = pack_f16x2(acc[2] * sc, acc[3] * sc);
+                o.z = pack_f16x2(acc[4] * sc, acc[5] * sc);
+                o.w = pack_f16x2(acc[6] * sc, acc[7] * sc);
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.ws_o) + sr) = o;
+            } else {                                        // fp32 partial: any bf16 V
+                float4 *dst = reinterpret_cast<float4 *>(static_cast<float *>(p.ws_o) + sr);
+                dst[0] = make_float4(acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc);
+                dst[1] = make_float4(acc[4] * sc, acc[5] * sc, acc[6] * sc, acc[7] * sc);
+            }
             if (c == 0)
                 p.ws_lse[(int64_t)slot * p.rows_max + r] = W > 0.f ? M + __log2f(W) : -INFINITY;
         }
@@ -1417,8 +1011,319 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
         }
         wait_vmcnt<0>();
 
-        piece_epilogue<RTW>(st, lds, lds + kQBytes, p, kg, rg, pl, lq, q0, g, slot, whole, vd);
+        piece_epilogue<RTW, kKvFp8>(st, lds, lds + kQBytes, p, kg, rg, pl, lq, q0, g, slot, whole, vd);
 
+
+        s = base + r1;
+        base += cnt;
+        ++bg;
+    }
+}
+
+// ------------------------------------------------- bf16 cache, LDS design --
+//
+// The same workgroup shape as the FP8 kernel (8 waves: 4 key groups x 2 row
+// groups, 2-stage ring per key group, direct global->LDS copies), with one
+// page (16 keys) per step: a stage holds the K page and the V page of one kv
+// head, 8 KiB each (16 rows of 512 bytes; the 16-byte chunk c of key row n sits
+// at slot c ^ (n & 15)).  QK runs on v_mfma_f32_16x16x32_bf16 with Q taken as
+// stored (bf16 operands copied into LDS in operand order, no conversion); PV
+// on v_mfma_f32_16x16x16_bf16 (K = the 16 keys of the page), its V^T operands
+// transposed from the key rows with byte permutes.
+
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+constexpr int kQbf16Bytes = 4 * 8 * 64 * 16;                // [rt][s][lane] x 16 B: 4 row tiles
+
+__device__ __forceinline__ floatx4_t mfma16k16(const shortx4_t &a, const shortx4_t &b, const floatx4_t &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Lane offsets of the 8 copy instructions of one bf16 page: instruction i,
+// lane l writes LDS bytes [1024 i + 16 l, +16) = key row n = 2 i + l/32, slot
+// l%32, so it fetches chunk (l%32) ^ (n & 15) of that key row.
+__device__ __forceinline__ void dma_lane_offsets_bf16(uint32_t (&off)[8], int hkv, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int n = 2 * i + (lane >> 5);
+        off[i] = (uint32_t)(n * hkv * kHeadDim * 2 + (((lane & 31) ^ (n & 15)) * 16));
+    }
+}
+
+__device__ __forceinline__ void dma_page_bf16(uint32_t dst, const uint8_t *pool, int64_t y, int64_t page_bytes,
+                                              const uint32_t (&off)[8])
+{
+    const uint8_t *a = pool + y * page_bytes;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        dma16(a, off[i], dst + 1024 * i);
+}
+
+// S^T[rt] (16 keys x 16 rows) of one page: K operand of lane (n = l%16, j =
+// l/16) for dims 32 s + 8 j .. +8 of key n = chunk 4 s + j.
+template <int RTW>
+__device__ __forceinline__ void qk_lds_bf16(floatx4_t (&S)[RTW], const unsigned char *stage,
+                                            const unsigned char *qw, int lane)
+{
+    const int n = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+        S[rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const bf16x8_t kop = *reinterpret_cast<const bf16x8_t *>(stage + 512 * n + (((4 * s + j) ^ n) * 16));
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            const bf16x8_t qop = *reinterpret_cast<const bf16x8_t *>(qw + ((size_t)(rt * 8 + s) * 64 + lane) * 16);
+            S[rt] = mfma16(kop, qop, S[rt]);
+        }
+    }
+}
+
+// Online softmax of a one-page step: lane (row n, j) holds the logits of keys
+// key0 + 4 j + e, e = 0..3; returns P^T B-operands (4 bf16).  Same rules as
+// softmax_step.
+template <int RTW, bool CAP>
+__device__ __forceinline__ void softmax_step1(RowState<RTW> &st, shortx4_t (&pop)[RTW], const floatx4_t (&S)[RTW],
+                                              const int (&limit)[RTW], uint32_t wlim, int key0, float c,
+                                              float cap, int lane, bool masked)
+{
+    const int j = lane >> 4;
+    float x[RTW][4];
+    bool need_any = false;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = S[rt][e] * c;
+            if constexpr (CAP)
+                v = softcap_log2(v, cap);
+            if (masked) {
+                const int key = key0 + 4 * j + e;
+                v = (uint32_t)(limit[rt] - key) <= wlim ? v : -INFINITY;
+            }
+            x[rt][e] = v;
+        }
+        const float lmax = fmaxf(fmaxf(x[rt][0], x[rt][1]), fmaxf(x[rt][2], x[rt][3]));
+        need_any |= lmax > st.m[rt] + kTau;
+    }
+    if (__any(need_any)) {
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            float t = fmaxf(fmaxf(x[rt][0], x[rt][1]), fmaxf(x[rt][2], x[rt][3]));
+            t = fmaxf(t, __shfl_xor(t, 16));
+            t = fmaxf(t, __shfl_xor(t, 32));
+            const bool need = t > st.m[rt] + kTau;
+            const float alpha = need ? exp2_fast(st.m[rt] - t) : 1.0f;
+            st.m[rt] = need ? t : st.m[rt];
+            st.l[rt] *= alpha;
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt)
+                st.o[tt][rt] *= alpha;
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        const float mref = st.m[rt] == -INFINITY ? 0.0f : st.m[rt];
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            pv[e] = exp2_fast(x[rt][e] - mref);
+        st.l[rt] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        pop[rt] = __builtin_bit_cast(shortx4_t, make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])));
+    }
+}
+
+// PV of a one-page step: lane (m = l%16, j = l/16) reads dims 16 m .. 16 m + 15
+// of keys 4 j + e (two 16-byte chunks per key row) and builds, for dim tile T,
+// the V^T operand {V[4j + e][16 m + T], e = 0..3}.  zmask bit e zeroes key
+// 4 j + e (at or past seqused_k: it may hold NaN bytes).
+template <int RTW>
+__device__ __forceinline__ void pv_lds_bf16(RowState<RTW> &st, const unsigned char *stage,
+                                            const shortx4_t (&pop)[RTW], uint32_t zmask, int lane)
+{
+    const int m = lane & 15, j = lane >> 4;
+    const unsigned char *vb = stage + 8192;
+    uint4 v[4][2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int n = 4 * j + e;
+        v[e][0] = *reinterpret_cast<const uint4 *>(vb + 512 * n + (((2 * m) ^ n) * 16));
+        v[e][1] = *reinterpret_cast<const uint4 *>(vb + 512 * n + (((2 * m + 1) ^ n) * 16));
+    }
+    if (zmask) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (zmask & (1u << e)) {
+                v[e][0] = make_uint4(0, 0, 0, 0);
+                v[e][1] = make_uint4(0, 0, 0, 0);
+            }
+    }
+#pragma unroll
+    for (int T = 0; T < 16; ++T) {
+        const int h = T >> 3, d = (T & 7) >> 1;
+        const uint32_t sel = (T & 1) ? 0x07060302u : 0x05040100u;     // high or low bf16 of each dword
+        const uint32_t w0 = byte_perm(u4get(v[1][h], d), u4get(v[0][h], d), sel);
+        const uint32_t w1 = byte_perm(u4get(v[3][h], d), u4get(v[2][h], d), sel);
+        const shortx4_t a = __builtin_bit_cast(shortx4_t, make_uint2(w0, w1));
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+            st.o[T][rt] = mfma16k16(a, pop[rt], st.o[T][rt]);
+    }
+}
+
+// bf16 split-KV kernel, LDS design.  Same structure as the FP8 kernel: the two
+// waves of a key group share a 2-stage ring (one copies each step's K page,
+// the other its V page), the prologue copies the Q operands and the first two
+// steps, one barrier per step.
+template <int RTW, bool CAP>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void va_split_kv_bf16_w8_kernel(SplitParams p)
+{
+    constexpr int NG = 4;
+    constexpr int RT = 2 * RTW;
+    constexpr int kQBytes = kQbf16Bytes;
+    constexpr int kRingBytes = 2 * kStageBytes;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kQBytes + NG * kRingBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const int rg = wave & 1;
+    const int kg = wave >> 1;
+    const int w = blockIdx.x;
+    const int G = 1 << p.log2g;
+
+    Share sh = locate(p, w, lane, w == 0 && wave == 0);
+    sh.n_eff = uniform(sh.n_eff);
+    sh.s = uniform(sh.s);
+    sh.e = uniform(sh.e);
+    sh.bg = uniform(sh.bg);
+    sh.base = uniform(sh.base);
+    if (w >= sh.n_eff)
+        return;                                        // uniform over the workgroup
+
+    const float kd = p.kdesc ? p.kdesc[0] : 1.0f;
+    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
+    const float c = p.scale_log2 * kd;
+    unsigned char *ring = lds + kQBytes + kg * kRingBytes;
+    const uint32_t ring_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(ring));
+    const uint32_t lds_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(lds));
+    const unsigned char *qw = lds + (size_t)rg * RTW * 8 * 64 * 16;
+    const int64_t page_bytes = (int64_t)kPage * p.hkv * kHeadDim * 2;
+
+    const int bh = p.num_seqs * p.hkv;
+    int s = sh.s, bg = sh.bg, base = sh.base;
+    while (s < sh.e && bg < bh) {
+        int pl = lane;                                 // opaque per piece (see the FP8 kernel)
+        asm volatile("" : "+v"(pl));
+        uint32_t off[8];
+        dma_lane_offsets_bf16(off, p.hkv, pl);
+        const int b = uniform(bg / p.hkv);
+        const int g = bg - b * p.hkv;
+        const int q0 = load_uniform(p.cu, b);
+        const int lq = load_uniform(p.cu, b + 1) - q0;
+        const int lk = load_uniform(p.seqused, b);
+        const int pb = first_page(lk, lq, p.window_left);
+        const int cnt = (lq <= 0 || lk <= 0) ? 0 : max(0, min((lk + kPage - 1) / kPage, p.mbps) - pb);
+        if (cnt == 0) {
+            ++bg;
+            continue;
+        }
+        const int ctx = lk - lq;
+        const int r0 = s - base;
+        const int r1 = min(sh.e, base + cnt) - base;
+        const bool whole = (r0 == 0 && r1 == cnt);
+        const int p0 = pb + r0;
+        const int slot = w + bg;
+        const int lo_max = p.window_left < 0 ? INT_MIN : ctx + lq - 1 - p.window_left;
+        const uint32_t wlim = p.window_left < 0 ? 0x7FFFFFFFu : (uint32_t)p.window_left;
+
+        const int nst = r1 - r0;                               // pages = steps of the piece
+        const int nsteps = (nst + NG - 1) / NG;                // uniform over the workgroup
+        const bool rows_live = (rg * RTW * 16) < lq * G;
+        const int32_t *btrow = p.bt + (int64_t)b * p.mbps;
+        const uint8_t *pool = (rg == 0 ? p.k : p.v) + (int64_t)g * kHeadDim * 2;
+        const int64_t maxpage = p.num_blocks - 1;
+        auto issue = [&](int k, int stage) {                   // this wave's page of step k
+            int64_t y = load_uniform(btrow, uniform(p0 + k));
+            y = y < 0 ? 0 : (y > maxpage ? maxpage : y);
+            dma_page_bf16(ring_addr + stage * kStageBytes + 8192 * rg, pool, y, page_bytes, off);
+        };
+
+        // ---- prologue: Q operands and the first two steps' pages
+        __syncthreads();                                       // previous piece's LDS reads done
+        {
+            // instruction i = rt * 8 + s: lane l gets dims 32 s + 8 (l/16) .. +8 of
+            // packed row 16 rt + l%16 (rows past the piece's tokens re-read token 0)
+            const uint16_t *qbase = p.q + ((int64_t)q0 * p.hq + g * G) * kHeadDim;
+            for (int i = wave; i < RT * 8; i += 2 * NG) {
+                const int rt = i >> 3, sc = i & 7;
+                const int r = 16 * rt + (pl & 15);
+                int t = r >> p.log2g;
+                t = t < lq ? t : 0;
+                const uint32_t voff = (uint32_t)(((t * p.hq + (r & (G - 1))) * kHeadDim + 32 * sc + 8 * (pl >> 4)) * 2);
+                dma16(qbase, voff, lds_addr + i * 1024);
+            }
+        }
+        const bool has1 = kg + NG < nst;
+        if (kg < nst)
+            issue(kg, 0);
+        if (has1)
+            issue(kg + NG, 1);
+        if (has1)
+            wait_vmcnt<16>();                                  // this wave's Q copies landed
+        else if (kg < nst)
+            wait_vmcnt<8>();
+        else
+            wait_vmcnt<0>();
+
+        RowState<RTW> st;
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            st.m[rt] = -INFINITY;
+            st.l[rt] = 0.f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        int limit[RTW];
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            const int t = ((rg * RTW + rt) * 16 + (pl & 15)) >> p.log2g;
+            limit[rt] = min(ctx + t, lk - 1);
+        }
+
+        for (int t = 0; t < nsteps; ++t) {
+            const int k = kg + t * NG;
+            if (t == 0 && k + NG < nst)
+                wait_vmcnt<8>();                               // own copies of step 0 landed
+            else
+                wait_vmcnt<0>();
+            __syncthreads();                                   // partner's too (and all Q copies)
+            if (t >= 1 && k + NG < nst)
+                issue(k + NG, (t + 1) & 1);
+            if (k < nst && rows_live) {
+                const unsigned char *stage = ring + (t & 1) * kStageBytes;
+                floatx4_t S[RTW];
+                qk_lds_bf16<RTW>(S, stage, qw, pl);
+                const int key0 = (p0 + k) * kPage;
+                const bool masked = key0 + 15 > ctx || key0 < lo_max;
+                shortx4_t pop[RTW];
+                softmax_step1<RTW, CAP>(st, pop, S, limit, wlim, key0, c, p.cap_log2, pl, masked);
+                uint32_t zmask = 0;
+                if (masked) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (key0 + 4 * (pl >> 4) + e >= lk)
+                            zmask |= 1u << e;
+                }
+                pv_lds_bf16<RTW>(st, stage, pop, zmask, pl);
+            }
+        }
+        wait_vmcnt<0>();
+
+        piece_epilogue<RTW, kKvBf16>(st, lds, lds + kQBytes, p, kg, rg, pl, lq, q0, g, slot, whole, vd);
 
         s = base + r1;
         base += cnt;
@@ -1579,11 +1484,6 @@ __global__ __launch_bounds__(kThreads) void va_fp8_to_bf16_kernel(const uint8_t 
 
 typedef void (*split_fn)(SplitParams);
 
-template <int RTW, int NR, int KVT, bool CAP>
-void launch_split(SplitParams p, int grid, hipStream_t s)
-{
-    hipLaunchKernelGGL((va_split_kv_kernel<RTW, NR, KVT, CAP>), dim3(grid), dim3(kThreads), 0, s, p);
-}
 
 typedef void (*launch_fn)(SplitParams, int, hipStream_t);
 
@@ -1593,24 +1493,25 @@ void launch_fp8_w8(SplitParams p, int grid, hipStream_t s)
     hipLaunchKernelGGL((va_split_kv_fp8_w8_kernel<RTW, CAP>), dim3(grid), dim3(512), 0, s, p);
 }
 
+template <int RTW, bool CAP>
+void launch_bf16_w8(SplitParams p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((va_split_kv_bf16_w8_kernel<RTW, CAP>), dim3(grid), dim3(512), 0, s, p);
+}
+
 struct Variant {
-    int rtw, nr;        // bf16 kernel: row tiles per wave, row groups
     launch_fn fp8, bf16, fp8_cap, bf16_cap;   // without / with the logit softcap
 };
 
-// Row tiles needed -> kernels.  Three or four row tiles use two row groups of
-// two, so a wave's O^T accumulators stay at 128 registers (three or four row
-// tiles in one wave do not fit the register file without spilling).
+// Row tiles needed -> kernels.  Both kernels use two row groups of RTW row
+// tiles: one or two row tiles take RTW = 1, three or four RTW = 2 (a wave's
+// O^T accumulators stay at 128 registers).
 const Variant kVariants[5] = {
-    {1, 1, nullptr, nullptr, nullptr, nullptr},
-    {1, 1, launch_fp8_w8<1, false>, launch_split<1, 1, kKvBf16, false>,
-     launch_fp8_w8<1, true>, launch_split<1, 1, kKvBf16, true>},
-    {2, 1, launch_fp8_w8<1, false>, launch_split<2, 1, kKvBf16, false>,
-     launch_fp8_w8<1, true>, launch_split<2, 1, kKvBf16, true>},
-    {2, 2, launch_fp8_w8<2, false>, launch_split<2, 2, kKvBf16, false>,
-     launch_fp8_w8<2, true>, launch_split<2, 2, kKvBf16, true>},
-    {2, 2, launch_fp8_w8<2, false>, launch_split<2, 2, kKvBf16, false>,
-     launch_fp8_w8<2, true>, launch_split<2, 2, kKvBf16, true>},
+    {nullptr, nullptr, nullptr, nullptr},
+    {launch_fp8_w8<1, false>, launch_bf16_w8<1, false>, launch_fp8_w8<1, true>, launch_bf16_w8<1, true>},
+    {launch_fp8_w8<1, false>, launch_bf16_w8<1, false>, launch_fp8_w8<1, true>, launch_bf16_w8<1, true>},
+    {launch_fp8_w8<2, false>, launch_bf16_w8<2, false>, launch_fp8_w8<2, true>, launch_bf16_w8<2, true>},
+    {launch_fp8_w8<2, false>, launch_bf16_w8<2, false>, launch_fp8_w8<2, true>, launch_bf16_w8<2, true>},
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1701,8 +1602,7 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     pl->log2g = G == 4 ? 2 : G == 8 ? 3 : 4;
     const int rows = G * p.max_seqlen_q;
     pl->rt = (rows + 15) / 16;
-    pl->rows_max = p.kv_dtype == VA_DT_FP8_E4M3FN ? 16 * 2 * (pl->rt <= 2 ? 1 : 2)
-                                                 : 16 * kVariants[pl->rt].rtw * kVariants[pl->rt].nr;
+    pl->rows_max = 16 * 2 * (pl->rt <= 2 ? 1 : 2);      // 2 row groups x RTW row tiles
     pl->grid = p.force_grid > 0 ? p.force_grid : cus;
     pl->min_pages = 8;
     pl->slots = (int64_t)pl->grid + bh;
