@@ -73,3 +73,67 @@ def test_device_conversion_and_attention_through_it(case):
     out = as_f64(run(p, dev=dev, force_grid=64))
     ref, _ = oracle.attn_problem(p)
     compare(out, ref, p.name)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_graph_replay_with_new_lengths_in_place(kv_dtype):
+    """Metadata conversion + attention captured once in a HIP graph, replayed
+    after the lengths, block tables and pools were rewritten in place: the
+    plan and the graph hold no lengths, so each replay follows the device
+    data (the PR #30105 page: the seq_lens addition must stay inside the
+    captured graph).  Each replay is compared with the oracle."""
+    import torch
+    import paged_gqa_attention_va_amd as va
+    from gpu_util import as_f64, compare
+    q_lens = [4, 2, 3]
+    probs = [va_inputs.custom(q_lens, [5000, 800, 64], 16, 1, kv_dtype, seed=71, extra_blocks=200,
+                              window_left=900 if kv_dtype == "bf16" else -1, name="graph-a"),
+             va_inputs.custom(q_lens, [1200, 4000, 2049], 16, 1, kv_dtype, seed=72, extra_blocks=200,
+                              window_left=900 if kv_dtype == "bf16" else -1, name="graph-b")]
+    nblk = max(p.num_blocks for p in probs)
+    mbps = max(p.block_table.shape[1] for p in probs)
+    ntok = max(int(p.seqused_k.sum()) for p in probs)
+    elt = torch.uint8 if kv_dtype == "fp8" else torch.int16
+    kpool = torch.zeros((nblk, 16, 1, 256), dtype=elt, device="cuda")
+    vpool = torch.zeros_like(kpool)
+    q = torch.empty((sum(q_lens), 16, 256), dtype=torch.bfloat16, device="cuda")
+    cu = torch.from_numpy(probs[0].cu_seqlens_q).cuda()
+    indptr = torch.zeros(len(q_lens) + 1, dtype=torch.int32, device="cuda")
+    indices = torch.zeros(ntok, dtype=torch.int32, device="cuda")
+    kd = torch.ones(1, dtype=torch.float32, device="cuda")
+    plan = va.Plan(num_seqs=3, num_q_heads=16, num_kv_heads=1, max_seqlen_q=4, max_seqlen_k=mbps * 16,
+                   max_blocks_per_seq=mbps, num_blocks=nblk, total_q=sum(q_lens), kv_dtype=kv_dtype,
+                   window_left=probs[0].window_left)
+    ws = plan.workspace()
+    out = torch.empty_like(q)
+
+    def load(p):                                   # rewrite every input in place
+        ip, idx = token_slots(p)
+        kv = lambda a: torch.from_numpy(a.view(np.int16) if kv_dtype == "bf16" else a)
+        kpool.zero_()
+        vpool.zero_()
+        kpool[:p.num_blocks].copy_(kv(p.k))
+        vpool[:p.num_blocks].copy_(kv(p.v))
+        q.copy_(torch.from_numpy(p.q.view(np.int16)).view(torch.bfloat16))
+        indptr.copy_(torch.from_numpy(ip))
+        indices[:len(idx)].copy_(torch.from_numpy(idx))
+        torch.cuda.synchronize()
+
+    kview = kpool if kv_dtype == "fp8" else kpool.view(torch.bfloat16)
+    vview = vpool if kv_dtype == "fp8" else vpool.view(torch.bfloat16)
+    load(probs[0])
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        bt, sk = va.spec_block_table(indptr, indices, mbps, stream=s)
+        plan.run(q, kview, vview, bt, cu, sk, probs[0].scale, kd, kd, out=out, workspace=ws, stream=s)
+    for rep in range(2):
+        for p in probs:
+            load(p)
+            out.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            ref, _ = oracle.attn_problem(p)
+            compare(as_f64(out), ref, f"{p.name} replay {rep}")
