@@ -36,12 +36,21 @@
  *
  * Errors.  Functions return va_status.  Host-checkable mistakes (null
  * pointers, unsupported shapes, a short workspace) return an error and enqueue
- * nothing.  Device data is not validated in va_run.  Invalid device data yields
- * an undefined result, but the kernels do not read outside their buffers:
- *   - lengths are clamped to the block-table row;
+ * nothing.  Device data (the lengths and the block table) is not validated in
+ * va_run.  Invalid device data yields an undefined result, but the kernels
+ * never access memory outside their buffers:
+ *   - a sequence whose query rows leave [0, total_q) or number more than
+ *     max_seqlen_q is treated as empty;
+ *   - key lengths are clamped to the block-table row;
  *   - page ids are clamped to [0, num_blocks).
- * Invalid device data includes q_len > seqused_k, a page id out of range, and
- * cu_seqlens_q not ascending.
+ * va_validate checks the device data explicitly (the VA_BAD_* rules below).
+ *
+ * Validate mode.  With the environment variable VA_DEBUG set (and not "0")
+ * when va_plan runs, va_plan prints the plan to stderr, and every va_run of
+ * that plan first runs va_validate on the call's metadata, waits for it, and
+ * returns VA_ERR_DEVICE_DATA (with a line on stderr) instead of running the
+ * attention if any rule fails.  That wait makes validate mode unusable under
+ * HIP graph capture; it is a debugging aid.
  */
 #ifndef VA_H
 #define VA_H
@@ -58,7 +67,8 @@ typedef enum {
     VA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent sizes */
     VA_ERR_UNSUPPORTED = 2,   /* outside the supported domain (see va_plan) */
     VA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than va_plan_workspace_bytes */
-    VA_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+    VA_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed */
+    VA_ERR_DEVICE_DATA = 5    /* validate mode (VA_DEBUG) found invalid device metadata */
 } va_status;
 
 typedef enum {
@@ -173,6 +183,38 @@ va_status va_run_ex(va_plan_t plan, int32_t stage, const void *q, const void *k_
                     float softmax_scale, const float *k_descale,
                     const float *v_descale, const float *sinks, void *out,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Check one call's device metadata against the plan (the rules below), as
+ * va_run would read it.  Every rule follows from the operation: query rows are
+ * the prefix sums cu_seqlens_q, each sequence has at most max_seqlen_q of
+ * them, its KV length bounds its causal key range, and every page it reads is
+ * a page of the pools.  Bits of result[0] (sequence b, q_len = cu[b+1] - cu[b]):
+ *   VA_BAD_CU_SEQLENS_Q  cu[0] != 0, or cu[b+1] < cu[b], or cu[b+1] > total_q
+ *   VA_BAD_Q_LEN         cu is fine for b and q_len > max_seqlen_q
+ *   VA_BAD_SEQUSED_K     seqused_k[b] < 0 or > max_seqlen_k
+ *   VA_BAD_Q_GT_K        q_len > seqused_k[b] (q_len counted 0 where cu is bad):
+ *                        a query token would sit before the first key
+ *   VA_BAD_PAGE          an entry the sequence reads is outside [0, num_blocks).
+ *                        It reads entries p with first <= p and 16 p < seqused_k,
+ *                        where first = 0, or with a window
+ *                        max(0, seqused_k - q_len - window_left) / 16.
+ *                        Entries past those (padding) are never checked.
+ * result[1] = the smallest sequence index that breaks a rule, num_seqs if none.
+ *   result   device pointer to 2 int32 (4-byte aligned), written by the call
+ *   others   as va_run
+ * Two small kernels are enqueued on `stream`; the call does not wait.  Errors:
+ * VA_ERR_INVALID_ARG (null or misaligned pointer), VA_ERR_HIP.
+ */
+enum {
+    VA_BAD_CU_SEQLENS_Q = 1,
+    VA_BAD_Q_LEN = 2,
+    VA_BAD_SEQUSED_K = 4,
+    VA_BAD_Q_GT_K = 8,
+    VA_BAD_PAGE = 16
+};
+va_status va_validate(va_plan_t plan, const int32_t *block_table, const int32_t *cu_seqlens_q,
+                      const int32_t *seqused_k, int32_t *result, void *stream);
 
 /* Release a plan (NULL is ignored). */
 void va_plan_destroy(va_plan_t plan);

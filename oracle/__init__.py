@@ -189,3 +189,59 @@ def spec_block_table(kv_indptr, kv_indices, page_size: int, max_blocks_per_seq: 
         for pg in range(-(-n // page_size)):
             bt[b, pg] = int(kv_indices[kv_indptr[b] + pg * page_size]) // page_size
     return bt, seqused
+
+
+# Rules of the call's device metadata (bits of ``validate``'s result).
+BAD_CU_SEQLENS_Q, BAD_Q_LEN, BAD_SEQUSED_K, BAD_Q_GT_K, BAD_PAGE = 1, 2, 4, 8, 16
+
+
+def validate(block_table, cu_seqlens_q, seqused_k, num_blocks: int, total_q: int,
+             max_seqlen_q: int, max_seqlen_k: int, window_left: int = -1,
+             page_size: int = 16) -> Tuple[int, int]:
+    """Check one call's metadata; returns (OR of the broken rules' bits, the
+    smallest sequence that breaks one, or num_seqs).
+
+    The rules restate what the verify call's inputs mean on the PR #36330
+    summary page ("Key source snippets": cu_seqlens_q, seqused_k and
+    block_table of the unified_attention_3d_mtp_func call, and the paged cache
+    the test builds):
+      - cu_seqlens_q holds prefix sums of the query lengths from 0, inside the
+        total_q rows of q (BAD_CU_SEQLENS_Q);
+      - no sequence has more than max_seqlen_q queries (BAD_Q_LEN);
+      - 0 <= seqused_k <= max_seqlen_k (BAD_SEQUSED_K);
+      - the query tokens are the last q_len of the seqused_k keys, so
+        q_len <= seqused_k (BAD_Q_GT_K; q_len counts 0 where cu is broken);
+      - every page holding a key some query of the sequence sees is a pool page
+        (BAD_PAGE).  The first query sits at position seqused_k - q_len and with
+        a sliding window sees keys from that position - window_left on.
+    Plain loops over sequences and pages.
+    """
+    bt = np.asarray(block_table)
+    cu = [int(x) for x in np.asarray(cu_seqlens_q).ravel()]
+    sk = [int(x) for x in np.asarray(seqused_k).ravel()]
+    B = len(sk)
+    mbps = bt.shape[1]
+    bits, first_bad = 0, B
+    for b in range(B):
+        q0, q1, lk = cu[b], cu[b + 1], sk[b]
+        bad = 0
+        cu_ok = (b > 0 or q0 == 0) and q0 <= q1 <= total_q
+        lq = q1 - q0 if cu_ok else 0
+        if not cu_ok:
+            bad |= BAD_CU_SEQLENS_Q
+        if lq > max_seqlen_q:
+            bad |= BAD_Q_LEN
+        if lk < 0 or lk > max_seqlen_k:
+            bad |= BAD_SEQUSED_K
+        if lq > lk:
+            bad |= BAD_Q_GT_K
+        if lk > 0:
+            first_key = 0 if window_left < 0 else max(0, lk - lq - window_left)
+            last_page = (lk - 1) // page_size
+            for pg in range(first_key // page_size, min(last_page + 1, mbps)):
+                if not 0 <= int(bt[b, pg]) < num_blocks:
+                    bad |= BAD_PAGE
+        if bad:
+            bits |= bad
+            first_bad = min(first_bad, b)
+    return bits, first_bad

@@ -22,12 +22,15 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libva.so")
 
-VA_OK, VA_ERR_INVALID_ARG, VA_ERR_UNSUPPORTED, VA_ERR_WORKSPACE, VA_ERR_HIP = range(5)
+VA_OK, VA_ERR_INVALID_ARG, VA_ERR_UNSUPPORTED, VA_ERR_WORKSPACE, VA_ERR_HIP, VA_ERR_DEVICE_DATA = range(6)
 VA_DT_BF16, VA_DT_FP8_E4M3FN = 1, 2
 VA_STAGE_ALL, VA_STAGE_SPLIT_KV, VA_STAGE_MERGE = 0, 1, 2
+# va_validate result bits
+VA_BAD_CU_SEQLENS_Q, VA_BAD_Q_LEN, VA_BAD_SEQUSED_K, VA_BAD_Q_GT_K, VA_BAD_PAGE = 1, 2, 4, 8, 16
 
 EXPORTED = ("va_plan", "va_plan_workspace_bytes", "va_plan_grid", "va_run", "va_run_ex",
-            "va_plan_destroy", "va_status_str", "va_fp8_to_bf16", "va_spec_block_table")
+            "va_plan_destroy", "va_status_str", "va_fp8_to_bf16", "va_spec_block_table",
+            "va_validate")
 
 _lib = None
 
@@ -78,6 +81,8 @@ def library(path: str = LIB_PATH):
     lib.va_status_str.argtypes = [ctypes.c_int]
     lib.va_spec_block_table.restype = ctypes.c_int
     lib.va_spec_block_table.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P]
+    lib.va_validate.restype = ctypes.c_int
+    lib.va_validate.argtypes = [P, P, P, P, P, P]
     lib.va_fp8_to_bf16.restype = ctypes.c_int
     lib.va_fp8_to_bf16.argtypes = [P, P, ctypes.c_int64, P]
     if path == LIB_PATH:
@@ -181,6 +186,30 @@ class Plan:
             ctypes.c_void_p(sptr))
         _check(st, "va_run")
         return out
+
+    def validate(self, block_table, cu_seqlens_q, seqused_k, result=None, stream=None):
+        """Enqueue va_validate; returns the int32 device tensor [bits, first bad
+        sequence] (read it after the stream has reached it)."""
+        import torch
+        pr = self.problem
+        meta = ((block_table, (pr.num_seqs, pr.max_blocks_per_seq)), (cu_seqlens_q, (pr.num_seqs + 1,)),
+                (seqused_k, (pr.num_seqs,)))
+        for t, shape in meta:
+            if t.dtype != torch.int32 or tuple(t.shape) != shape or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"metadata must be contiguous int32 device tensors shaped {shape}")
+        if result is None:
+            result = torch.empty(2, dtype=torch.int32, device=block_table.device)
+        if result.dtype != torch.int32 or result.numel() < 2 or not result.is_contiguous():
+            raise ValueError("result must be a contiguous int32 tensor with 2 elements")
+        if stream is None:
+            stream = torch.cuda.current_stream(block_table.device)
+        sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        _check(self._lib.va_validate(self._h, ctypes.c_void_p(block_table.data_ptr()),
+                                     ctypes.c_void_p(cu_seqlens_q.data_ptr()),
+                                     ctypes.c_void_p(seqused_k.data_ptr()),
+                                     ctypes.c_void_p(result.data_ptr()), ctypes.c_void_p(sptr)),
+               "va_validate")
+        return result
 
     def _check_tensors(self, q, k_pool, v_pool, block_table, cu, seqused, kd, vd):
         import torch

@@ -37,6 +37,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <new>
@@ -79,6 +81,7 @@ struct SplitParams {
     const float *sinks;   // [Hq] sink logits (natural-log units) or null
     int32_t window_left;  // sliding window: keys from i - window_left on (-1 = none)
     int32_t num_seqs, hq, hkv, log2g, mbps, grid_n, min_pages, rows_max;
+    int32_t total_q, max_q;   // rows of q / out, and the longest valid query block
     int64_t num_blocks;
 };
 
@@ -91,7 +94,7 @@ struct MergeParams {
     const int32_t *ws_prefix;
     const int32_t *ws_meta;
     uint16_t *out;
-    int32_t num_seqs, hq, hkv, log2g, max_q, rows_max;
+    int32_t num_seqs, hq, hkv, log2g, max_q, rows_max, total_q;
 };
 
 // ------------------------------------------------------------ primitives --
@@ -182,17 +185,24 @@ __device__ __forceinline__ int first_page(int lk, int lq, int wl)
     return wl < 0 ? 0 : max(0, lk - lq - wl) / kPage;
 }
 
+// Query length of a sequence whose rows are [q0, q1).  A range that leaves
+// [0, total_q) or is longer than max_q counts as empty, so no cu_seqlens_q
+// value can move a q read or an out write outside those buffers.
+__device__ __forceinline__ int checked_q_len(int q0, int q1, int total_q, int max_q)
+{
+    return (q0 >= 0 && q1 >= q0 && q1 <= total_q && q1 - q0 <= max_q) ? q1 - q0 : 0;
+}
+
 // Pages of (sequence, kv head) bg that the split covers: first_page .. the
 // last page holding a key below seqused_k (clamped to the block-table row).
-__device__ __forceinline__ int pages_of(const int32_t *cu, const int32_t *seqused, int hkv,
-                                        int mbps, int wl, int bg)
+__device__ __forceinline__ int pages_of(const SplitParams &p, int bg)
 {
-    const int b = bg / hkv;
-    const int lq = cu[b + 1] - cu[b];
-    const int lk = seqused[b];
+    const int b = bg / p.hkv;
+    const int lq = checked_q_len(p.cu[b], p.cu[b + 1], p.total_q, p.max_q);
+    const int lk = p.seqused[b];
     if (lq <= 0 || lk <= 0)
         return 0;
-    return max(0, min((lk + kPage - 1) / kPage, mbps) - first_page(lk, lq, wl));
+    return max(0, min((lk + kPage - 1) / kPage, p.mbps) - first_page(lk, lq, p.window_left));
 }
 
 __device__ __forceinline__ uint32_t u4get(const uint4 &u, int i)
@@ -383,7 +393,7 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
 {
     const int bh = p.num_seqs * p.hkv;
     if (bh <= 64) {                                    // one pass: one count per lane
-        const int cnt = lane < bh ? pages_of(p.cu, p.seqused, p.hkv, p.mbps, p.window_left, lane) : 0;
+        const int cnt = lane < bh ? pages_of(p, lane) : 0;
         const int incl = wave_incl_scan(cnt, lane);
         const int total = __shfl(incl, 63);
         Share sh;
@@ -413,7 +423,7 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
     int total = 0;
     for (int c0 = 0; c0 < bh; c0 += 64) {
         const int bg = c0 + lane;
-        const int cnt = bg < bh ? pages_of(p.cu, p.seqused, p.hkv, p.mbps, p.window_left, bg) : 0;
+        const int cnt = bg < bh ? pages_of(p, bg) : 0;
         total += wave_sum(cnt);
     }
     Share sh;
@@ -427,7 +437,7 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
     int base = 0;
     for (int c0 = 0; c0 < bh; c0 += 64) {
         const int bg = c0 + lane;
-        const int cnt = bg < bh ? pages_of(p.cu, p.seqused, p.hkv, p.mbps, p.window_left, bg) : 0;
+        const int cnt = bg < bh ? pages_of(p, bg) : 0;
         const int incl = wave_incl_scan(cnt, lane);
         if (write_prefix && bg < bh)
             p.ws_prefix[bg] = base + incl - cnt;
@@ -909,7 +919,7 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
         const int b = uniform(bg / p.hkv);
         const int g = bg - b * p.hkv;
         const int q0 = load_uniform(p.cu, b);
-        const int lq = load_uniform(p.cu, b + 1) - q0;
+        const int lq = checked_q_len(q0, load_uniform(p.cu, b + 1), p.total_q, p.max_q);
         const int lk = load_uniform(p.seqused, b);
         const int pb = first_page(lk, lq, p.window_left);      // the range starts at logical page pb
         const int cnt = (lq <= 0 || lk <= 0) ? 0 : max(0, min((lk + kPage - 1) / kPage, p.mbps) - pb);
@@ -1222,7 +1232,7 @@ void va_split_kv_bf16_w8_kernel(SplitParams p)
         const int b = uniform(bg / p.hkv);
         const int g = bg - b * p.hkv;
         const int q0 = load_uniform(p.cu, b);
-        const int lq = load_uniform(p.cu, b + 1) - q0;
+        const int lq = checked_q_len(q0, load_uniform(p.cu, b + 1), p.total_q, p.max_q);
         const int lk = load_uniform(p.seqused, b);
         const int pb = first_page(lk, lq, p.window_left);
         const int cnt = (lq <= 0 || lk <= 0) ? 0 : max(0, min((lk + kPage - 1) / kPage, p.mbps) - pb);
@@ -1367,7 +1377,7 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
     const int nw = load_uniform(p.ws_meta, 0);
     asm volatile("" :: "s"(q0), "s"(q1), "s"(s), "s"(e), "s"(total), "s"(nw));   // keep the loads together
     const int64_t n = nw;
-    const int lq = q1 - q0;
+    const int lq = checked_q_len(q0, q1, p.total_q, p.max_q);
     if (t >= lq || e <= s || total <= 0)
         return;
     const int w0 = (int)(((int64_t)(s + 1) * n - 1) / total);
@@ -1480,6 +1490,64 @@ __global__ __launch_bounds__(kThreads) void va_fp8_to_bf16_kernel(const uint8_t 
         out[i + k] = r[k];
 }
 
+// Validate mode: checks of one call's device metadata.  One thread per
+// block-table entry (b, page).  The page-0 thread of a sequence checks its
+// lengths; every thread checks its own entry if the sequence reads it.
+// res[0] collects the VA_BAD_* bits, res[1] the smallest offending sequence
+// (va_validate_init_kernel first sets num_seqs there).
+struct ValidateParams {
+    const int32_t *bt;
+    const int32_t *cu;
+    const int32_t *seqused;
+    int32_t *res;
+    int32_t num_seqs, mbps, max_q, max_k, window_left;
+    int64_t total_q, num_blocks;
+};
+
+__global__ __launch_bounds__(64) void va_validate_init_kernel(int32_t *res, int32_t num_seqs)
+{
+    if (threadIdx.x == 0) {
+        res[0] = 0;
+        res[1] = num_seqs;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void va_validate_kernel(ValidateParams p)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= (int64_t)p.num_seqs * p.mbps)
+        return;
+    const int b = (int)(i / p.mbps);
+    const int pg = (int)(i - (int64_t)b * p.mbps);
+    const int64_t q0 = p.cu[b], q1 = p.cu[b + 1];
+    const int64_t lk = p.seqused[b];
+    const bool cu_ok = !(b == 0 && q0 != 0) && q1 >= q0 && q1 <= p.total_q;
+    const int64_t lq = cu_ok ? q1 - q0 : 0;
+    int bad = 0;
+    if (pg == 0) {
+        if (!cu_ok)
+            bad |= VA_BAD_CU_SEQLENS_Q;
+        if (lq > p.max_q)
+            bad |= VA_BAD_Q_LEN;
+        if (lk < 0 || lk > p.max_k)
+            bad |= VA_BAD_SEQUSED_K;
+        if (lq > lk)
+            bad |= VA_BAD_Q_GT_K;
+    }
+    // entries read: the pages of keys first .. lk - 1 (first = lk - lq -
+    // window_left with a window, else 0) inside the block-table row
+    const int64_t first = p.window_left < 0 ? 0 : max((int64_t)0, lk - lq - p.window_left) / kPage;
+    if (lk > 0 && pg >= first && (int64_t)pg * kPage < lk) {
+        const int32_t page = p.bt[i];
+        if (page < 0 || page >= p.num_blocks)
+            bad |= VA_BAD_PAGE;
+    }
+    if (bad) {
+        atomicOr(p.res, bad);
+        atomicMin(p.res + 1, b);
+    }
+}
+
 // ------------------------------------------------------------------ host --
 
 typedef void (*split_fn)(SplitParams);
@@ -1527,7 +1595,40 @@ struct va_plan_s {
     int rows_max;
     int64_t slots;
     size_t off_prefix, off_lse, off_o, ws_bytes;
+    bool debug;         // VA_DEBUG set at va_plan: validate mode and a plan dump on stderr
 };
+
+namespace {
+
+bool debug_env()
+{
+    const char *e = getenv("VA_DEBUG");
+    return e && e[0] && strcmp(e, "0") != 0;
+}
+
+va_status enqueue_validate(const va_plan_s *plan, const int32_t *block_table, const int32_t *cu_seqlens_q,
+                           const int32_t *seqused_k, int32_t *result, hipStream_t s)
+{
+    const va_problem &pr = plan->prob;
+    ValidateParams vp;
+    vp.bt = block_table;
+    vp.cu = cu_seqlens_q;
+    vp.seqused = seqused_k;
+    vp.res = result;
+    vp.num_seqs = pr.num_seqs;
+    vp.mbps = pr.max_blocks_per_seq;
+    vp.max_q = pr.max_seqlen_q;
+    vp.max_k = pr.max_seqlen_k;
+    vp.window_left = pr.window_left;
+    vp.total_q = pr.total_q;
+    vp.num_blocks = pr.num_blocks;
+    const int64_t blocks = ((int64_t)pr.num_seqs * pr.max_blocks_per_seq + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(va_validate_init_kernel, dim3(1), dim3(64), 0, s, result, pr.num_seqs);
+    hipLaunchKernelGGL(va_validate_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, vp);
+    return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -1539,6 +1640,7 @@ const char *va_status_str(va_status s)
     case VA_ERR_UNSUPPORTED: return "unsupported problem (outside the supported domain)";
     case VA_ERR_WORKSPACE: return "workspace missing or too small";
     case VA_ERR_HIP: return "HIP runtime error";
+    case VA_ERR_DEVICE_DATA: return "invalid device metadata (validate mode)";
     }
     return "unknown status";
 }
@@ -1616,6 +1718,17 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     off = align_up(off + (size_t)pl->slots * pl->rows_max * kHeadDim * part_elt, 256);
 
     pl->ws_bytes = off;
+    pl->debug = debug_env();
+    if (pl->debug)
+        fprintf(stderr,
+                "va_plan: B=%d Hq=%d Hkv=%d G=%d max_q=%d max_k=%d mbps=%d blocks=%lld total_q=%lld "
+                "kv=%s window_left=%d softcap=%g -> row_tiles=%d grid=%d min_pages=%d rows_max=%d "
+                "slots=%lld workspace=%zu bytes (prefix @%zu, lse @%zu, partial O @%zu)\n",
+                p.num_seqs, p.num_q_heads, p.num_kv_heads, G, p.max_seqlen_q, p.max_seqlen_k,
+                p.max_blocks_per_seq, (long long)p.num_blocks, (long long)p.total_q,
+                p.kv_dtype == VA_DT_FP8_E4M3FN ? "fp8" : "bf16", p.window_left, (double)p.softcap, pl->rt,
+                pl->grid, pl->min_pages, pl->rows_max, (long long)pl->slots, pl->ws_bytes, pl->off_prefix,
+                pl->off_lse, pl->off_o);
     *out = pl;
     return VA_OK;
 }
@@ -1666,6 +1779,25 @@ va_status va_run_ex(va_plan_t plan, int32_t stage, const void *q, const void *k_
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     unsigned char *ws = static_cast<unsigned char *>(workspace);
 
+    if (plan->debug && (stage == VA_STAGE_ALL || stage == VA_STAGE_SPLIT_KV)) {
+        // validate mode: check the metadata first (result in workspace meta
+        // words 2 and 3, which the kernels leave alone) and wait for it
+        int32_t *res = reinterpret_cast<int32_t *>(ws) + 2;
+        const va_status vs = enqueue_validate(plan, block_table, cu_seqlens_q, seqused_k, res, s);
+        if (vs != VA_OK)
+            return vs;
+        int32_t h[2] = {0, 0};
+        if (hipMemcpyAsync(h, res, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return VA_ERR_HIP;
+        if (h[0] != 0) {
+            fprintf(stderr, "va_run: invalid device metadata, bits 0x%x (1 cu_seqlens_q, 2 q_len > max_seqlen_q, "
+                            "4 seqused_k, 8 q_len > seqused_k, 16 page id), first at sequence %d\n",
+                    (unsigned)h[0], h[1]);
+            return VA_ERR_DEVICE_DATA;
+        }
+    }
+
     if (stage == VA_STAGE_ALL || stage == VA_STAGE_SPLIT_KV) {
         SplitParams sp;
         sp.q = static_cast<const uint16_t *>(q);
@@ -1693,6 +1825,8 @@ va_status va_run_ex(va_plan_t plan, int32_t stage, const void *q, const void *k_
         sp.grid_n = plan->grid;
         sp.min_pages = plan->min_pages;
         sp.rows_max = plan->rows_max;
+        sp.total_q = (int32_t)pr.total_q;
+        sp.max_q = pr.max_seqlen_q;
         sp.num_blocks = pr.num_blocks;
         const Variant &v = kVariants[plan->rt];
         const bool cap = pr.softcap > 0.f;
@@ -1717,6 +1851,7 @@ va_status va_run_ex(va_plan_t plan, int32_t stage, const void *q, const void *k_
         mp.log2g = plan->log2g;
         mp.max_q = pr.max_seqlen_q;
         mp.rows_max = plan->rows_max;
+        mp.total_q = (int32_t)pr.total_q;
         const int64_t blocks = (int64_t)pr.num_seqs * pr.num_kv_heads * pr.max_seqlen_q *
                                ((pr.num_q_heads / pr.num_kv_heads) / 4);
         if (blocks > 0) {
@@ -1740,6 +1875,17 @@ va_status va_run(va_plan_t plan, const void *q, const void *k_pool, const void *
     return va_run_ex(plan, VA_STAGE_ALL, q, k_pool, v_pool, block_table, cu_seqlens_q,
                      seqused_k, softmax_scale, k_descale, v_descale, nullptr, out, workspace,
                      workspace_bytes, stream);
+}
+
+va_status va_validate(va_plan_t plan, const int32_t *block_table, const int32_t *cu_seqlens_q,
+                      const int32_t *seqused_k, int32_t *result, void *stream)
+{
+    if (!plan || !block_table || !cu_seqlens_q || !seqused_k || !result)
+        return VA_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(result) & 3)
+        return VA_ERR_INVALID_ARG;
+    return enqueue_validate(plan, block_table, cu_seqlens_q, seqused_k, result,
+                            reinterpret_cast<hipStream_t>(stream));
 }
 
 va_status va_spec_block_table(const int32_t *kv_indptr, const int32_t *kv_indices, int32_t num_seqs,

@@ -118,6 +118,6 @@ def test_plan_checks_window_and_softcap():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert va.status_str(s) and va.status_str(s) != "unknown status"
     assert va.status_str(99) == "unknown status"
