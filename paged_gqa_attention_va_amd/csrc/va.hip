@@ -954,8 +954,12 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
             dma_step_part(ring_addr + stage * kStageBytes, pool, rg, ya, yb, page_bytes, off);
         };
 
-        // ---- prologue: Q rows and the first two steps' pages are copied
-        // straight into LDS; the Q conversion overlaps the page copies.
+        // ---- prologue: Q rows and the first step's pages are copied
+        // straight into LDS; the Q conversion overlaps the page copies.  The
+        // second step is issued only after the conversion: at the start of
+        // the kernel every workgroup's first requests queue at once, and
+        // requests for step 1 issued with them would share the bandwidth with
+        // step 0 and delay it.
         __syncthreads();                                // previous piece's LDS reads done
         const uint32_t lds_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(lds));
         for (int i = wave; i < ((lq * G) >> 1); i += NG * 2) {        // row pairs: 1 KiB each
@@ -965,19 +969,17 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
             dma16(p.q + row0 * kHeadDim, (uint32_t)((pl >> 5) * 512 + ((slot ^ (rr & 15)) * 16)), lds_addr + r * 512);
         }
         const bool has1 = kg + NG < npairs;
-        if (kg < npairs)
+        if (kg < npairs) {
             issue(kg, 0);
-        if (has1)
-            issue(kg + NG, 1);
-        if (has1)
-            wait_vmcnt<2 * kDmaPerPart>();                  // this wave's Q copies landed
-        else if (kg < npairs)
-            wait_vmcnt<kDmaPerPart>();
-        else
+            wait_vmcnt<kDmaPerPart>();                  // this wave's Q copies landed
+        } else {
             wait_vmcnt<0>();
+        }
         __syncthreads();                                // every wave's Q copies landed
         float crow[RTW];                                       // logit multiplier of this lane's row
         stage_q_fp8<RTW>(lds, crow, c, p, lq, rg, kg, pl);
+        if (has1)
+            issue(kg + NG, 1);
 
         RowState<RTW> st;
 #pragma unroll
