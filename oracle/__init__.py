@@ -245,3 +245,73 @@ def validate(block_table, cu_seqlens_q, seqused_k, num_blocks: int, total_q: int
             bits |= bad
             first_bad = min(first_bad, b)
     return bits, first_bad
+
+
+def prefix_extend_to_paged(k_buffer, v_buffer, kv_indptr, kv_indices, k_extend, v_extend,
+                           cu_seqlens_q, page_size: int = 16):
+    """The paged cache, block table and KV lengths of a prefix + extend call.
+
+    Reading of the sglang PR #34517 summary page ("Key source snippets", the
+    shared-KV verify kernel and its entry guards): the prefix keys of sequence
+    b are the rows kv_indices[kv_indptr[b] + j], j < P_b, of the K/V buffers;
+    its q_len draft tokens' keys are rows cu[b] .. cu[b+1]-1 of k_extend /
+    v_extend and come after the prefix.  Query token t sits at position
+    P_b + t and sees the whole prefix and draft tokens 0..t, which is the
+    bottom-right causal rule of the paged call with seqused_k = P_b + q_len.
+    So the call is the paged call over a cache that holds each sequence's
+    keys in that order.  Plain loops copy them into fresh pages; buffers are
+    [rows, Hkv, D], the result is (k_pool, v_pool, block_table, seqused_k).
+    """
+    k_buffer = np.asarray(k_buffer)
+    v_buffer = np.asarray(v_buffer)
+    k_extend = np.asarray(k_extend)
+    v_extend = np.asarray(v_extend)
+    indptr = [int(x) for x in np.asarray(kv_indptr).ravel()]
+    cu = [int(x) for x in np.asarray(cu_seqlens_q).ravel()]
+    B = len(cu) - 1
+    hkv, d = k_buffer.shape[1], k_buffer.shape[2]
+    lens = [(indptr[b + 1] - indptr[b]) + (cu[b + 1] - cu[b]) for b in range(B)]
+    pages = [-(-n // page_size) for n in lens]
+    mbps = max(1, max(pages))
+    k_pool = np.zeros((max(1, sum(pages)), page_size, hkv, d), dtype=k_buffer.dtype)
+    v_pool = np.zeros_like(k_pool)
+    bt = np.zeros((B, mbps), dtype=np.int32)
+    page = 0
+    for b in range(B):
+        keys_k, keys_v = [], []
+        for j in range(indptr[b], indptr[b + 1]):
+            keys_k.append(k_buffer[int(kv_indices[j])])
+            keys_v.append(v_buffer[int(kv_indices[j])])
+        for r in range(cu[b], cu[b + 1]):
+            keys_k.append(k_extend[r])
+            keys_v.append(v_extend[r])
+        for i in range(len(keys_k)):
+            if i % page_size == 0:
+                bt[b, i // page_size] = page
+                page += 1
+            k_pool[bt[b, i // page_size], i % page_size] = keys_k[i]
+            v_pool[bt[b, i // page_size], i % page_size] = keys_v[i]
+    return k_pool, v_pool, bt, np.asarray(lens, dtype=np.int32)
+
+
+def attn_prefix_extend(q, k_buffer, v_buffer, kv_indptr, kv_indices, k_extend, v_extend,
+                       kv_dtype: str, cu_seqlens_q, num_kv_heads: int, scale: float,
+                       k_descale: float = 1.0, v_descale: float = 1.0, rows=None,
+                       threads=None, window_left: int = -1, softcap: float = 0.0,
+                       sinks=None) -> Tuple[np.ndarray, np.ndarray]:
+    """``attn`` of a prefix + extend call (see ``prefix_extend_to_paged``)."""
+    k_pool, v_pool, bt, seqused = prefix_extend_to_paged(
+        k_buffer, v_buffer, kv_indptr, kv_indices, k_extend, v_extend, cu_seqlens_q)
+    return attn(q, k_pool, v_pool, kv_dtype, bt, cu_seqlens_q, seqused, num_kv_heads, scale,
+                k_descale, v_descale, rows=rows, threads=threads, window_left=window_left,
+                softcap=softcap, sinks=sinks)
+
+
+def attn_prefix_extend_problem(p, rows=None, threads=None):
+    """``attn_prefix_extend`` on a ``va_inputs.PrefixExtendProblem``-like object."""
+    return attn_prefix_extend(
+        p.q, p.k_buffer, p.v_buffer, p.kv_indptr, p.kv_indices, p.k_extend, p.v_extend,
+        p.kv_dtype, p.cu_seqlens_q, p.num_kv_heads, p.scale, p.k_descale, p.v_descale,
+        rows=rows, threads=threads, window_left=getattr(p, "window_left", -1),
+        softcap=getattr(p, "softcap", 0.0),
+        sinks=None if getattr(p, "sinks", None) is None else p.sinks.astype(np.float64))

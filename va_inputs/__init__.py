@@ -242,3 +242,159 @@ def sample_rows(p: Problem, n: int, seed: int = 0) -> np.ndarray:
     pick.add(0)
     pick.add(total - 1)
     return np.array(sorted(pick), dtype=np.int64)
+
+
+# ------------------------------------------------- prefix + extend layout --
+
+@dataclasses.dataclass
+class PrefixExtendProblem:
+    """Host copy of one verify call in the prefix + extend layout: the prefix
+    K/V of each sequence sit in a token-row buffer addressed by per-token slots
+    (kv_indptr / kv_indices), the draft tokens' K/V in separate buffers with
+    one row per query token (the layout of the sglang PR #34517 summary page's
+    shared-KV verify kernel: prefix through kv_indices, k_extend / v_extend)."""
+    name: str
+    q: np.ndarray                # uint16 bf16 bits, [total_q, Hq, D]
+    k_buffer: np.ndarray         # uint8 fp8 bytes or uint16 bf16 bits, [num_rows, Hkv, D]
+    v_buffer: np.ndarray
+    k_extend: np.ndarray         # [total_q, Hkv, D], same dtype as the buffers
+    v_extend: np.ndarray
+    kv_dtype: str
+    kv_indptr: np.ndarray        # int32 [B+1], prefix sums of the prefix lengths
+    kv_indices: np.ndarray       # int32 [kv_indptr[B]], row of every prefix token
+    cu_seqlens_q: np.ndarray     # int32 [B+1]
+    num_q_heads: int
+    num_kv_heads: int
+    scale: float
+    k_descale: float
+    v_descale: float
+    head_dim: int = HEAD_DIM
+    window_left: int = -1
+    softcap: float = 0.0
+    sinks: Optional[np.ndarray] = None
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.cu_seqlens_q.shape[0] - 1)
+
+    @property
+    def q_lens(self) -> np.ndarray:
+        return np.diff(self.cu_seqlens_q)
+
+    @property
+    def prefix_lens(self) -> np.ndarray:
+        return np.diff(self.kv_indptr)
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_seqlens_q[-1])
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return int(self.q_lens.max()) if self.num_seqs else 0
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return int((self.prefix_lens + self.q_lens).max()) if self.num_seqs else 0
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.k_buffer.shape[0])
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+
+def prefix_extend(q_lens: Sequence[int], prefix_lens: Sequence[int], num_q_heads: int,
+                  num_kv_heads: int, kv_dtype: str = "fp8", seed: int = 0,
+                  slots: str = "tokens", extra_rows: int = 0, k_descale: float = 1.0,
+                  v_descale: float = 1.0, scale: Optional[float] = None, poison: bool = True,
+                  name: str = "prefix_extend", window_left: int = -1, softcap: float = 0.0,
+                  sinks: Optional[Sequence[float]] = None) -> PrefixExtendProblem:
+    """Build one prefix + extend problem.
+
+    slots: "tokens" -- every prefix token gets its own seeded random row (a
+                       token-granular allocator, the worst case for gathering);
+           "pages"  -- prefix tokens fill 16-row pages in order, pages in a
+                       seeded random order (a paged allocator).
+    Rows no prefix token uses are poisoned with NaN (when ``poison``).
+    """
+    assert kv_dtype in ("fp8", "bf16") and slots in ("tokens", "pages")
+    q_lens = [int(x) for x in q_lens]
+    prefix_lens = [int(x) for x in prefix_lens]
+    B = len(q_lens)
+    assert B == len(prefix_lens) and B >= 1
+    assert num_q_heads % num_kv_heads == 0
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    total_q = sum(q_lens)
+    n_prefix = sum(prefix_lens)
+    q = _randn_bf16_bits(gen, (total_q, num_q_heads, HEAD_DIM))
+    if slots == "tokens":
+        num_rows = max(1, n_prefix + extra_rows)
+        perm = torch.randperm(num_rows, generator=gen).numpy().astype(np.int64)
+        indices = perm[:n_prefix]
+    else:
+        pages = [math.ceil(n / PAGE) for n in prefix_lens]
+        num_pages = sum(pages) + math.ceil(extra_rows / PAGE)
+        num_rows = max(1, num_pages * PAGE)
+        pperm = torch.randperm(max(1, num_pages), generator=gen).numpy().astype(np.int64)
+        parts, off = [], 0
+        for n, npg in zip(prefix_lens, pages):
+            j = np.arange(n)
+            parts.append(pperm[off + j // PAGE] * PAGE + j % PAGE)
+            off += npg
+        indices = np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+    k_buf = _randn_kv_bits(gen, (num_rows, num_kv_heads, HEAD_DIM), kv_dtype)
+    v_buf = _randn_kv_bits(gen, (num_rows, num_kv_heads, HEAD_DIM), kv_dtype)
+    k_ext = _randn_kv_bits(gen, (total_q, num_kv_heads, HEAD_DIM), kv_dtype)
+    v_ext = _randn_kv_bits(gen, (total_q, num_kv_heads, HEAD_DIM), kv_dtype)
+    if poison:
+        nan = FP8_NAN if kv_dtype == "fp8" else BF16_NAN
+        used = np.zeros(num_rows, dtype=bool)
+        used[indices] = True
+        k_buf[~used] = nan
+        v_buf[~used] = nan
+    indptr = np.zeros(B + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(prefix_lens)
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    if scale is None:
+        scale = HEAD_DIM ** -0.5
+    sk_arr = None if sinks is None else np.asarray(sinks, dtype=np.float32)
+    return PrefixExtendProblem(
+        name=name, q=q, k_buffer=k_buf, v_buffer=v_buf, k_extend=k_ext, v_extend=v_ext,
+        kv_dtype=kv_dtype, kv_indptr=indptr, kv_indices=indices.astype(np.int32),
+        cu_seqlens_q=cu, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+        scale=_f32(scale), k_descale=_f32(k_descale), v_descale=_f32(v_descale),
+        window_left=int(window_left), softcap=_f32(softcap), sinks=sk_arr)
+
+
+def prefix_extend_from_paged(p: Problem, name: Optional[str] = None) -> PrefixExtendProblem:
+    """The same call as paged problem ``p`` in the prefix + extend layout: the
+    first seqused_k - q_len keys of each sequence stay in the pool (viewed as
+    token rows, slot = page * 16 + offset), its last q_len keys move to
+    k_extend / v_extend.  Pure data movement."""
+    B = p.num_seqs
+    rows_k = p.k.reshape(-1, p.num_kv_heads, p.head_dim)
+    rows_v = p.v.reshape(-1, p.num_kv_heads, p.head_dim)
+    indptr = np.zeros(B + 1, dtype=np.int32)
+    idx, ext_k, ext_v = [], [], []
+    for b in range(B):
+        lq = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
+        lk = int(p.seqused_k[b])
+        pre = lk - lq
+        j = np.arange(lk)
+        slot = p.block_table[b, j // p.page_size].astype(np.int64) * p.page_size + j % p.page_size
+        idx.append(slot[:pre])
+        ext_k.append(rows_k[slot[pre:]])
+        ext_v.append(rows_v[slot[pre:]])
+        indptr[b + 1] = indptr[b] + pre
+    return PrefixExtendProblem(
+        name=name or p.name + "-prefix-extend", q=p.q, k_buffer=rows_k.copy(), v_buffer=rows_v.copy(),
+        k_extend=np.concatenate(ext_k), v_extend=np.concatenate(ext_v), kv_dtype=p.kv_dtype,
+        kv_indptr=indptr, kv_indices=np.concatenate(idx).astype(np.int32),
+        cu_seqlens_q=p.cu_seqlens_q.copy(), num_q_heads=p.num_q_heads, num_kv_heads=p.num_kv_heads,
+        scale=p.scale, k_descale=p.k_descale, v_descale=p.v_descale, window_left=p.window_left,
+        softcap=p.softcap, sinks=p.sinks)
