@@ -76,6 +76,22 @@ typedef enum {
     VA_DT_FP8_E4M3FN = 2      /* OCP fp8 e4m3fn: bias 7, max 448, NaN = 0x7F/0xFF, no inf */
 } va_dtype;
 
+/*
+ * Where the keys live.
+ *   VA_LAYOUT_PAGED          16-token pages [num_blocks, 16, Hkv, 256] addressed by a
+ *                            block table; the verify tokens' K/V are already in
+ *                            the cache (va_run, va_run_ex).
+ *   VA_LAYOUT_PREFIX_EXTEND  the layout of the sglang PR #34517 summary page's
+ *                            shared-KV verify kernel ("Key source snippets"):
+ *                            the prefix K/V are token rows of a buffer
+ *                            [num_blocks * page_size, Hkv, 256] addressed by
+ *                            per-token slots (kv_indptr / kv_indices), the
+ *                            draft tokens' K/V sit in separate buffers with one
+ *                            row per query token (va_run_prefix_extend).
+ *                            max_blocks_per_seq is ignored.
+ */
+typedef enum { VA_LAYOUT_PAGED = 0, VA_LAYOUT_PREFIX_EXTEND = 1 } va_layout;
+
 /* Shape of one verify-attention call.  All fields are host values. */
 typedef struct {
     int32_t num_seqs;            /* B >= 1 */
@@ -100,6 +116,7 @@ typedef struct {
                                     page's verify call) */
     float softcap;               /* logit softcap: 0 = none; > 0: every scaled logit s is
                                     replaced by softcap * tanh(s / softcap) */
+    int32_t layout;              /* va_layout of the KV cache (VA_LAYOUT_PAGED = 0) */
 } va_problem;
 
 typedef struct va_plan_s *va_plan_t;
@@ -215,6 +232,36 @@ enum {
 };
 va_status va_validate(va_plan_t plan, const int32_t *block_table, const int32_t *cu_seqlens_q,
                       const int32_t *seqused_k, int32_t *result, void *stream);
+
+/*
+ * Verify attention in the prefix + extend layout (plan built with
+ * layout = VA_LAYOUT_PREFIX_EXTEND), through the same kernels as va_run_ex.
+ *   k_buffer, v_buffer [num_blocks * page_size, Hkv, 256] kv_dtype: token rows
+ *   kv_indptr    [num_seqs + 1] int32: sequence b's prefix is kv_indices
+ *                [kv_indptr[b], kv_indptr[b+1]); P_b = its length
+ *   kv_indices   [num_kv_indices] int32: the buffer row of every prefix token,
+ *                in key order (any rows: no page structure is assumed)
+ *   k_extend, v_extend  [total_q, Hkv, 256] kv_dtype: the draft tokens' K/V,
+ *                row cu_seqlens_q[b] + i = draft token i of sequence b (same
+ *                dtype and descale as the buffers, as if already cached)
+ *   others       as va_run_ex (stage, sinks, window, softcap included)
+ * Sequence b has P_b + q_len keys: the prefix, then its draft tokens; query
+ * token t sees the whole prefix and draft tokens 0..t (bottom-right causal, as
+ * in va_run with seqused_k = P_b + q_len); max_seqlen_k bounds P_b + q_len.
+ * Device data is not validated (validate mode covers the paged layout only);
+ * a prefix range outside kv_indices counts as an empty sequence and slots are
+ * clamped to the buffer rows, so no access leaves the buffers.
+ * Errors: as va_run_ex; VA_ERR_INVALID_ARG also for a paged plan, a null
+ * kv_indptr / k_extend / v_extend, num_kv_indices < 0 or > INT32_MAX - 16, or a
+ * null kv_indices with num_kv_indices > 0.  va_run / va_run_ex reject a
+ * prefix + extend plan the same way.
+ */
+va_status va_run_prefix_extend(va_plan_t plan, int32_t stage, const void *q, const void *k_buffer,
+                               const void *v_buffer, const int32_t *kv_indptr, const int32_t *kv_indices,
+                               int64_t num_kv_indices, const void *k_extend, const void *v_extend,
+                               const int32_t *cu_seqlens_q, float softmax_scale, const float *k_descale,
+                               const float *v_descale, const float *sinks, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /* Release a plan (NULL is ignored). */
 void va_plan_destroy(va_plan_t plan);

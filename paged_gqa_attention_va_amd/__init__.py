@@ -25,12 +25,13 @@ LIB_PATH = os.path.join(HERE, "libva.so")
 VA_OK, VA_ERR_INVALID_ARG, VA_ERR_UNSUPPORTED, VA_ERR_WORKSPACE, VA_ERR_HIP, VA_ERR_DEVICE_DATA = range(6)
 VA_DT_BF16, VA_DT_FP8_E4M3FN = 1, 2
 VA_STAGE_ALL, VA_STAGE_SPLIT_KV, VA_STAGE_MERGE = 0, 1, 2
+VA_LAYOUT_PAGED, VA_LAYOUT_PREFIX_EXTEND = 0, 1
 # va_validate result bits
 VA_BAD_CU_SEQLENS_Q, VA_BAD_Q_LEN, VA_BAD_SEQUSED_K, VA_BAD_Q_GT_K, VA_BAD_PAGE = 1, 2, 4, 8, 16
 
 EXPORTED = ("va_plan", "va_plan_workspace_bytes", "va_plan_grid", "va_run", "va_run_ex",
             "va_plan_destroy", "va_status_str", "va_fp8_to_bf16", "va_spec_block_table",
-            "va_validate")
+            "va_validate", "va_run_prefix_extend")
 
 _lib = None
 
@@ -51,6 +52,7 @@ class _Problem(ctypes.Structure):
         ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
         ("num_cus", ctypes.c_int32), ("force_grid", ctypes.c_int32),
         ("window_left", ctypes.c_int32), ("softcap", ctypes.c_float),
+        ("layout", ctypes.c_int32),
     ]
 
 
@@ -81,6 +83,9 @@ def library(path: str = LIB_PATH):
     lib.va_status_str.argtypes = [ctypes.c_int]
     lib.va_spec_block_table.restype = ctypes.c_int
     lib.va_spec_block_table.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P]
+    lib.va_run_prefix_extend.restype = ctypes.c_int
+    lib.va_run_prefix_extend.argtypes = [P, ctypes.c_int32, P, P, P, P, P, ctypes.c_int64, P, P, P,
+                                         ctypes.c_float, P, P, P, P, P, ctypes.c_size_t, P]
     lib.va_validate.restype = ctypes.c_int
     lib.va_validate.argtypes = [P, P, P, P, P, P]
     lib.va_fp8_to_bf16.restype = ctypes.c_int
@@ -118,14 +123,18 @@ class Plan:
                  num_blocks: int, total_q: int, kv_dtype: str = "fp8",
                  num_cus: int = 0, force_grid: int = 0, head_dim: int = 256,
                  window_left: int = -1, softcap: float = 0.0,
-                 page_size: int = 16, q_dtype: str = "bf16"):
+                 page_size: int = 16, q_dtype: str = "bf16", layout: str = "paged"):
         self._lib = library()
+        if layout not in ("paged", "prefix_extend"):
+            raise ValueError(f"unknown layout {layout!r}")
         pr = _Problem(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                       max_seqlen_q, max_seqlen_k, max_blocks_per_seq, num_blocks, total_q,
                       _dtype_code(q_dtype), _dtype_code(kv_dtype), num_cus, force_grid,
-                      int(window_left), float(softcap))
+                      int(window_left), float(softcap),
+                      VA_LAYOUT_PAGED if layout == "paged" else VA_LAYOUT_PREFIX_EXTEND)
         self.problem = pr
         self.kv_dtype = kv_dtype
+        self.layout = layout
         h = ctypes.c_void_p()
         _check(self._lib.va_plan(ctypes.byref(pr), ctypes.byref(h)), "va_plan")
         self._h = h
@@ -150,6 +159,70 @@ class Plan:
                    max_blocks_per_seq=int(p.block_table.shape[1]), num_blocks=p.num_blocks,
                    total_q=p.total_q, kv_dtype=p.kv_dtype,
                    window_left=getattr(p, "window_left", -1), softcap=getattr(p, "softcap", 0.0), **kw)
+
+    @classmethod
+    def for_prefix_extend(cls, p, **kw) -> "Plan":
+        """Plan for a ``va_inputs.PrefixExtendProblem``-like object (duck typed)."""
+        return cls(num_seqs=p.num_seqs, num_q_heads=p.num_q_heads, num_kv_heads=p.num_kv_heads,
+                   max_seqlen_q=max(1, p.max_seqlen_q), max_seqlen_k=p.max_seqlen_k,
+                   max_blocks_per_seq=1, num_blocks=p.num_rows, page_size=1,
+                   total_q=p.total_q, kv_dtype=p.kv_dtype, layout="prefix_extend",
+                   window_left=getattr(p, "window_left", -1), softcap=getattr(p, "softcap", 0.0), **kw)
+
+    def run_prefix_extend(self, q, k_buffer, v_buffer, kv_indptr, kv_indices, k_extend, v_extend,
+                          cu_seqlens_q, softmax_scale: float, k_descale=None, v_descale=None,
+                          out=None, workspace=None, stream=None, stage: int = VA_STAGE_ALL,
+                          sinks=None):
+        """Enqueue the attention of a prefix + extend call (va_run_prefix_extend).
+        k_buffer / v_buffer: [rows, Hkv, 256]; k_extend / v_extend: [total_q, Hkv, 256]."""
+        import torch
+        pr = self.problem
+        if self.layout != "prefix_extend":
+            raise ValueError("run_prefix_extend needs a plan with layout='prefix_extend'")
+        kv_ok = (torch.uint8, torch.float8_e4m3fn) if self.kv_dtype == "fp8" else (torch.bfloat16,)
+        if q.dtype != torch.bfloat16 or tuple(q.shape) != (pr.total_q, pr.num_q_heads, pr.head_dim):
+            raise ValueError(f"q must be bf16 [{pr.total_q}, {pr.num_q_heads}, {pr.head_dim}]")
+        rows = pr.num_blocks * pr.page_size
+        for name, t, shape in (("k_buffer", k_buffer, (rows, pr.num_kv_heads, pr.head_dim)),
+                               ("v_buffer", v_buffer, (rows, pr.num_kv_heads, pr.head_dim)),
+                               ("k_extend", k_extend, (pr.total_q, pr.num_kv_heads, pr.head_dim)),
+                               ("v_extend", v_extend, (pr.total_q, pr.num_kv_heads, pr.head_dim))):
+            if t.dtype not in kv_ok or tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be {self.kv_dtype} {shape}, got {t.dtype} {tuple(t.shape)}")
+        if kv_indptr.dtype != torch.int32 or tuple(kv_indptr.shape) != (pr.num_seqs + 1,):
+            raise ValueError("kv_indptr must be int32 [num_seqs + 1]")
+        if kv_indices.dtype != torch.int32 or kv_indices.dim() != 1:
+            raise ValueError("kv_indices must be a 1-D int32 tensor")
+        if cu_seqlens_q.dtype != torch.int32 or tuple(cu_seqlens_q.shape) != (pr.num_seqs + 1,):
+            raise ValueError("cu_seqlens_q must be int32 [num_seqs + 1]")
+        for name, t in (("k_descale", k_descale), ("v_descale", v_descale)):
+            if t is not None and (t.dtype != torch.float32 or t.numel() < 1):
+                raise ValueError(f"{name} must be a float32 device tensor with one element")
+        if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != pr.num_q_heads):
+            raise ValueError("sinks must be a float32 device tensor with num_q_heads elements")
+        for t in (q, k_buffer, v_buffer, kv_indptr, kv_indices, k_extend, v_extend, cu_seqlens_q,
+                  k_descale, v_descale, sinks):
+            if t is not None and (not t.is_cuda or not t.is_contiguous()):
+                raise ValueError("all tensors must be contiguous device tensors")
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.workspace(q.device)
+        if out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous():
+            raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        n_idx = kv_indices.numel()
+        st = self._lib.va_run_prefix_extend(
+            self._h, int(stage), ptr(q), ptr(k_buffer), ptr(v_buffer), ptr(kv_indptr),
+            ptr(kv_indices) if n_idx else None, n_idx, ptr(k_extend), ptr(v_extend), ptr(cu_seqlens_q),
+            ctypes.c_float(softmax_scale), ptr(k_descale), ptr(v_descale), ptr(sinks), ptr(out),
+            ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+            ctypes.c_void_p(sptr))
+        _check(st, "va_run_prefix_extend")
+        return out
 
     def workspace(self, device=None):
         import torch

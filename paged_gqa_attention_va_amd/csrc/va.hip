@@ -41,6 +41,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 
 #include "va.h"
@@ -83,6 +84,15 @@ struct SplitParams {
     int32_t num_seqs, hq, hkv, log2g, mbps, grid_n, min_pages, rows_max;
     int32_t total_q, max_q;   // rows of q / out, and the longest valid query block
     int64_t num_blocks;
+    // prefix + extend layout (kv_indptr == null: paged layout).  Key j < P of
+    // sequence b is row kv_indices[kv_indptr[b] + j] of the k / v buffers
+    // ([num_rows, Hkv, 256]); key P + i is row cu[b] + i of kext / vext.
+    const int32_t *kv_indptr;
+    const int32_t *kv_indices;
+    const uint8_t *kext;
+    const uint8_t *vext;
+    int64_t num_indices;  // elements of kv_indices
+    int64_t num_rows;     // rows of the k / v buffers
 };
 
 struct MergeParams {
@@ -193,13 +203,24 @@ __device__ __forceinline__ int checked_q_len(int q0, int q1, int total_q, int ma
     return (q0 >= 0 && q1 >= q0 && q1 <= total_q && q1 - q0 <= max_q) ? q1 - q0 : 0;
 }
 
+// Keys of a sequence from its prefix range [s0, s1) of kv_indices and its
+// (checked) query length, in the prefix + extend layout.  A prefix range
+// outside kv_indices counts as an empty sequence.
+__device__ __forceinline__ int prefix_keys(int s0, int s1, int lq, int64_t num_indices)
+{
+    return (s0 >= 0 && s1 >= s0 && s1 <= num_indices) ? (s1 - s0) + lq : 0;
+}
+
 // Pages of (sequence, kv head) bg that the split covers: first_page .. the
-// last page holding a key below seqused_k (clamped to the block-table row).
+// last page holding a key below the sequence's key count (clamped to the
+// block-table row).  In the prefix + extend layout a "page" is 16 consecutive
+// keys of the sequence.
 __device__ __forceinline__ int pages_of(const SplitParams &p, int bg)
 {
     const int b = bg / p.hkv;
     const int lq = checked_q_len(p.cu[b], p.cu[b + 1], p.total_q, p.max_q);
-    const int lk = p.seqused[b];
+    const int lk = p.kv_indptr ? prefix_keys(p.kv_indptr[b], p.kv_indptr[b + 1], lq, p.num_indices)
+                               : p.seqused[b];
     if (lq <= 0 || lk <= 0)
         return 0;
     return max(0, min((lk + kPage - 1) / kPage, p.mbps) - first_page(lk, lq, p.window_left));
@@ -478,6 +499,41 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
                  :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// The same copy from a per-lane 64-bit global address (key rows gathered one
+// by one in the prefix + extend layout).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_at(const void *addr, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(addr), "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Token-row gather, prefix + extend layout.  A "tag" names the row of one key:
+// >= 0 a row of the k / v buffers, < 0 the row ~tag of kext / vext.  Each
+// lane loads the kv_indices entry of one key of a step (unconditionally, from
+// a clamped address, so the load can stay in flight: nothing reads the value
+// until the step that issues the copies), and turns it into a tag there.
+__device__ __forceinline__ int32_t tok_load(const SplitParams &p, int b, int s0, int pre, int j)
+{
+    const int32_t *a = pre > 0 ? p.kv_indices + s0 + min(max(j, 0), pre - 1) : p.kv_indptr + b;
+    return *a;
+}
+
+__device__ __forceinline__ int32_t tok_tag(int32_t raw, int j, int pre, int lk, int q0, int64_t num_rows)
+{
+    if (j < pre)
+        return raw < 0 ? 0 : (raw >= num_rows ? (int32_t)(num_rows - 1) : raw);
+    return j < lk ? ~(q0 + (j - pre)) : 0;              // keys past lk are masked; row 0 is a safe read
+}
+
+__device__ __forceinline__ const uint8_t *tok_row(int32_t tag, const uint8_t *buf, const uint8_t *ext,
+                                                  int64_t row_bytes)
+{
+    return tag >= 0 ? buf + (int64_t)tag * row_bytes : ext + (int64_t)(~tag) * row_bytes;
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
@@ -873,7 +929,7 @@ __device__ __forceinline__ void piece_epilogue(RowState<RTW> &st, unsigned char 
 // the V pages, straight from HBM, one step ahead of the compute.  One
 // workgroup barrier per step makes a stage visible to both waves and frees the
 // stage the next copy overwrites.
-template <int RTW, bool CAP>
+template <int RTW, bool CAP, bool TOK>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void va_split_kv_fp8_w8_kernel(SplitParams p)
 {
@@ -920,7 +976,13 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
         const int g = bg - b * p.hkv;
         const int q0 = load_uniform(p.cu, b);
         const int lq = checked_q_len(q0, load_uniform(p.cu, b + 1), p.total_q, p.max_q);
-        const int lk = load_uniform(p.seqused, b);
+        int s0 = 0, lk;                                        // s0: prefix start in kv_indices
+        if constexpr (TOK) {
+            s0 = load_uniform(p.kv_indptr, b);
+            lk = prefix_keys(s0, load_uniform(p.kv_indptr, b + 1), lq, p.num_indices);
+        } else {
+            lk = load_uniform(p.seqused, b);
+        }
         const int pb = first_page(lk, lq, p.window_left);      // the range starts at logical page pb
         const int cnt = (lq <= 0 || lk <= 0) ? 0 : max(0, min((lk + kPage - 1) / kPage, p.mbps) - pb);
         if (cnt == 0) {
@@ -953,6 +1015,34 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
             const int64_t yb = pa + 1 < p1 ? phys(pa + 1) : ya;
             dma_step_part(ring_addr + stage * kStageBytes, pool, rg, ya, yb, page_bytes, off);
         };
+        // prefix + extend layout: lane l tags key 32 k' + l % 32 of step k
+        // (k' = the step's first key / 32); copy i of the wave takes key row
+        // n = 4 (i % 4) + l / 16 of page i / 4, chunk (l % 16) ^ n, as above.
+        const int pre = lk - lq;
+        const uint8_t *ext = (rg == 0 ? p.kext : p.vext) + (int64_t)g * kHeadDim;
+        const int64_t row_bytes = (int64_t)p.hkv * kHeadDim;
+        auto tload = [&](int k) { return tok_load(p, b, s0, pre, (p0 + 2 * k) * kPage + (pl & 31)); };
+        auto issue_tok = [&](int k, int stage, int32_t raw) {
+            const int32_t tag = tok_tag(raw, (p0 + 2 * k) * kPage + (pl & 31), pre, lk, q0, p.num_rows);
+            const uint32_t dst = ring_addr + stage * kStageBytes + 8192 * rg;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int n = 4 * (i & 3) + (pl >> 4);
+                const int32_t t = __shfl(tag, 16 * (i >> 2) + n);
+                dma16_at(tok_row(t, pool, ext, row_bytes) + (((pl & 15) ^ n) * 16),
+                         dst + 4096 * (i >> 2) + 1024 * (i & 3));
+            }
+        };
+        // The tags of the first two steps are read before any copy is issued;
+        // later ones one step ahead (rawN), so each is in registers when its
+        // step's copies go out.  Nothing reads a tag load's register before
+        // the wait that covers it (the empty asm statements mark those points).
+        int32_t rawA = 0, rawB = 0, rawN = 0;
+        if constexpr (TOK) {
+            rawA = tload(kg);
+            rawB = tload(kg + NG);
+            asm volatile("" : "+v"(rawA), "+v"(rawB));
+        }
 
         // ---- prologue: Q rows and the first step's pages are copied
         // straight into LDS; the Q conversion overlaps the page copies.  The
@@ -970,7 +1060,10 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
         }
         const bool has1 = kg + NG < npairs;
         if (kg < npairs) {
-            issue(kg, 0);
+            if constexpr (TOK)
+                issue_tok(kg, 0, rawA);
+            else
+                issue(kg, 0);
             wait_vmcnt<kDmaPerPart>();                  // this wave's Q copies landed
         } else {
             wait_vmcnt<0>();
@@ -978,8 +1071,14 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
         __syncthreads();                                // every wave's Q copies landed
         float crow[RTW];                                       // logit multiplier of this lane's row
         stage_q_fp8<RTW>(lds, crow, c, p, lq, rg, kg, pl);
-        if (has1)
-            issue(kg + NG, 1);
+        if (has1) {
+            if constexpr (TOK) {
+                issue_tok(kg + NG, 1, rawB);
+                rawN = tload(kg + 2 * NG);
+            } else {
+                issue(kg + NG, 1);
+            }
+        }
 
         RowState<RTW> st;
 #pragma unroll
@@ -1000,14 +1099,24 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
 
         for (int t = 0; t < nsteps; ++t) {
             const int k = kg + t * NG;
-            if (t == 0 && k + NG < npairs)
-                wait_vmcnt<kDmaPerPart>();                     // own copies of step 0 landed (step 1 may not)
+            if (t == 0 && k + NG < npairs)                     // own copies of step 0 landed (step 1 may
+                wait_vmcnt<TOK ? kDmaPerPart + 1 : kDmaPerPart>();   // not, nor step 2's tags)
             else
                 wait_vmcnt<0>();                               // own copies of step t landed
+            if constexpr (TOK) {
+                if (t >= 1)
+                    asm volatile("" : "+v"(rawN));             // step t+1's tags: loaded with step t
+            }
             __syncthreads();                                   // partner's too; stage of step t-1 is free
 
-            if (t >= 1 && k + NG < npairs)                     // steps 0 and 1 came with the prologue
-                issue(k + NG, (t + 1) & 1);
+            if (t >= 1 && k + NG < npairs) {                   // steps 0 and 1 came with the prologue
+                if constexpr (TOK) {
+                    issue_tok(k + NG, (t + 1) & 1, rawN);
+                    rawN = tload(k + 2 * NG);
+                } else {
+                    issue(k + NG, (t + 1) & 1);
+                }
+            }
             if (k < npairs && rows_live) {
                 const unsigned char *stage = ring + (t & 1) * kStageBytes;
                 floatx4_t S[2][RTW];
@@ -1189,7 +1298,7 @@ __device__ __forceinline__ void pv_lds_bf16(RowState<RTW> &st, const unsigned ch
 // waves of a key group share a 2-stage ring (one copies each step's K page,
 // the other its V page), the prologue copies the Q operands and the first two
 // steps, one barrier per step.
-template <int RTW, bool CAP>
+template <int RTW, bool CAP, bool TOK>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void va_split_kv_bf16_w8_kernel(SplitParams p)
 {
@@ -1235,7 +1344,13 @@ void va_split_kv_bf16_w8_kernel(SplitParams p)
         const int g = bg - b * p.hkv;
         const int q0 = load_uniform(p.cu, b);
         const int lq = checked_q_len(q0, load_uniform(p.cu, b + 1), p.total_q, p.max_q);
-        const int lk = load_uniform(p.seqused, b);
+        int s0 = 0, lk;                                        // s0: prefix start in kv_indices
+        if constexpr (TOK) {
+            s0 = load_uniform(p.kv_indptr, b);
+            lk = prefix_keys(s0, load_uniform(p.kv_indptr, b + 1), lq, p.num_indices);
+        } else {
+            lk = load_uniform(p.seqused, b);
+        }
         const int pb = first_page(lk, lq, p.window_left);
         const int cnt = (lq <= 0 || lk <= 0) ? 0 : max(0, min((lk + kPage - 1) / kPage, p.mbps) - pb);
         if (cnt == 0) {
@@ -1262,6 +1377,28 @@ void va_split_kv_bf16_w8_kernel(SplitParams p)
             y = y < 0 ? 0 : (y > maxpage ? maxpage : y);
             dma_page_bf16(ring_addr + stage * kStageBytes + 8192 * rg, pool, y, page_bytes, off);
         };
+        // prefix + extend layout (see the FP8 kernel): lane l tags key
+        // 16 (p0 + k) + l % 16; copy i takes key row n = 2 i + l / 32.
+        const int pre = lk - lq;
+        const uint8_t *ext = (rg == 0 ? p.kext : p.vext) + (int64_t)g * kHeadDim * 2;
+        const int64_t row_bytes = (int64_t)p.hkv * kHeadDim * 2;
+        auto tload = [&](int k) { return tok_load(p, b, s0, pre, (p0 + k) * kPage + (pl & 15)); };
+        auto issue_tok = [&](int k, int stage, int32_t raw) {
+            const int32_t tag = tok_tag(raw, (p0 + k) * kPage + (pl & 15), pre, lk, q0, p.num_rows);
+            const uint32_t dst = ring_addr + stage * kStageBytes + 8192 * rg;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int n = 2 * i + (pl >> 5);
+                const int32_t t = __shfl(tag, n);
+                dma16_at(tok_row(t, pool, ext, row_bytes) + (((pl & 31) ^ (n & 15)) * 16), dst + 1024 * i);
+            }
+        };
+        int32_t rawA = 0, rawB = 0, rawN = 0;
+        if constexpr (TOK) {
+            rawA = tload(kg);
+            rawB = tload(kg + NG);
+            asm volatile("" : "+v"(rawA), "+v"(rawB));
+        }
 
         // ---- prologue: Q operands and the first two steps' pages
         __syncthreads();                                       // previous piece's LDS reads done
@@ -1279,12 +1416,22 @@ void va_split_kv_bf16_w8_kernel(SplitParams p)
             }
         }
         const bool has1 = kg + NG < nst;
-        if (kg < nst)
-            issue(kg, 0);
+        if (kg < nst) {
+            if constexpr (TOK)
+                issue_tok(kg, 0, rawA);
+            else
+                issue(kg, 0);
+        }
+        if (has1) {
+            if constexpr (TOK) {
+                issue_tok(kg + NG, 1, rawB);
+                rawN = tload(kg + 2 * NG);
+            } else {
+                issue(kg + NG, 1);
+            }
+        }
         if (has1)
-            issue(kg + NG, 1);
-        if (has1)
-            wait_vmcnt<16>();                                  // this wave's Q copies landed
+            wait_vmcnt<TOK ? 17 : 16>();                       // this wave's Q copies landed
         else if (kg < nst)
             wait_vmcnt<8>();
         else
@@ -1309,12 +1456,22 @@ void va_split_kv_bf16_w8_kernel(SplitParams p)
         for (int t = 0; t < nsteps; ++t) {
             const int k = kg + t * NG;
             if (t == 0 && k + NG < nst)
-                wait_vmcnt<8>();                               // own copies of step 0 landed
+                wait_vmcnt<TOK ? 9 : 8>();                     // own copies of step 0 landed
             else
                 wait_vmcnt<0>();
+            if constexpr (TOK) {
+                if (t >= 1)
+                    asm volatile("" : "+v"(rawN));
+            }
             __syncthreads();                                   // partner's too (and all Q copies)
-            if (t >= 1 && k + NG < nst)
-                issue(k + NG, (t + 1) & 1);
+            if (t >= 1 && k + NG < nst) {
+                if constexpr (TOK) {
+                    issue_tok(k + NG, (t + 1) & 1, rawN);
+                    rawN = tload(k + 2 * NG);
+                } else {
+                    issue(k + NG, (t + 1) & 1);
+                }
+            }
             if (k < nst && rows_live) {
                 const unsigned char *stage = ring + (t & 1) * kStageBytes;
                 floatx4_t S[RTW];
@@ -1557,32 +1714,39 @@ typedef void (*split_fn)(SplitParams);
 
 typedef void (*launch_fn)(SplitParams, int, hipStream_t);
 
-template <int RTW, bool CAP>
+template <int RTW, bool CAP, bool TOK>
 void launch_fp8_w8(SplitParams p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((va_split_kv_fp8_w8_kernel<RTW, CAP>), dim3(grid), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((va_split_kv_fp8_w8_kernel<RTW, CAP, TOK>), dim3(grid), dim3(512), 0, s, p);
+}
+
+template <int RTW, bool CAP, bool TOK>
+void launch_bf16_w8(SplitParams p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((va_split_kv_bf16_w8_kernel<RTW, CAP, TOK>), dim3(grid), dim3(512), 0, s, p);
+}
+
+template <int RTW, bool CAP, bool TOK>
+launch_fn pick_kv(bool fp8)
+{
+    return fp8 ? launch_fp8_w8<RTW, CAP, TOK> : launch_bf16_w8<RTW, CAP, TOK>;
 }
 
 template <int RTW, bool CAP>
-void launch_bf16_w8(SplitParams p, int grid, hipStream_t s)
+launch_fn pick_layout(bool fp8, bool tok)
 {
-    hipLaunchKernelGGL((va_split_kv_bf16_w8_kernel<RTW, CAP>), dim3(grid), dim3(512), 0, s, p);
+    return tok ? pick_kv<RTW, CAP, true>(fp8) : pick_kv<RTW, CAP, false>(fp8);
 }
-
-struct Variant {
-    launch_fn fp8, bf16, fp8_cap, bf16_cap;   // without / with the logit softcap
-};
 
 // Row tiles needed -> kernels.  Both kernels use two row groups of RTW row
 // tiles: one or two row tiles take RTW = 1, three or four RTW = 2 (a wave's
-// O^T accumulators stay at 128 registers).
-const Variant kVariants[5] = {
-    {nullptr, nullptr, nullptr, nullptr},
-    {launch_fp8_w8<1, false>, launch_bf16_w8<1, false>, launch_fp8_w8<1, true>, launch_bf16_w8<1, true>},
-    {launch_fp8_w8<1, false>, launch_bf16_w8<1, false>, launch_fp8_w8<1, true>, launch_bf16_w8<1, true>},
-    {launch_fp8_w8<2, false>, launch_bf16_w8<2, false>, launch_fp8_w8<2, true>, launch_bf16_w8<2, true>},
-    {launch_fp8_w8<2, false>, launch_bf16_w8<2, false>, launch_fp8_w8<2, true>, launch_bf16_w8<2, true>},
-};
+// O^T accumulators stay at 128 registers).  Then KV dtype, softcap, layout.
+launch_fn select_launch(int row_tiles, bool fp8, bool cap, bool tok)
+{
+    if (row_tiles <= 2)
+        return cap ? pick_layout<1, true>(fp8, tok) : pick_layout<1, false>(fp8, tok);
+    return cap ? pick_layout<2, true>(fp8, tok) : pick_layout<2, false>(fp8, tok);
+}
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -1596,6 +1760,8 @@ struct va_plan_s {
     int min_pages;
     int rows_max;
     int64_t slots;
+    int32_t mbps;       // pages per sequence bound: the block-table row, or (prefix + extend)
+                        // ceil(max_seqlen_k / 16)
     size_t off_prefix, off_lse, off_o, ws_bytes;
     bool debug;         // VA_DEBUG set at va_plan: validate mode and a plan dump on stderr
 };
@@ -1654,7 +1820,8 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     *out = nullptr;
     const va_problem &p = *pr;
     if (p.num_seqs < 1 || p.num_q_heads < 1 || p.num_kv_heads < 1 || p.head_dim < 1 ||
-        p.page_size < 1 || p.max_seqlen_q < 1 || p.max_seqlen_k < 0 || p.max_blocks_per_seq < 1 ||
+        p.page_size < 1 || p.max_seqlen_q < 1 || p.max_seqlen_k < 0 ||
+        (p.layout == VA_LAYOUT_PAGED && p.max_blocks_per_seq < 1) ||
         p.num_blocks < 1 || p.total_q < 0 || p.num_cus < 0 || p.force_grid < 0)
         return VA_ERR_INVALID_ARG;
     if (p.total_q > (int64_t)p.num_seqs * p.max_seqlen_q)
@@ -1665,7 +1832,12 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
         return VA_ERR_INVALID_ARG;
     if (p.q_dtype != VA_DT_BF16)
         return VA_ERR_UNSUPPORTED;
-    if (p.head_dim != kHeadDim || p.page_size != kPage)
+    if (p.layout != VA_LAYOUT_PAGED && p.layout != VA_LAYOUT_PREFIX_EXTEND)
+        return VA_ERR_INVALID_ARG;
+    const bool tok = p.layout == VA_LAYOUT_PREFIX_EXTEND;
+    if (p.head_dim != kHeadDim || (!tok && p.page_size != kPage))
+        return VA_ERR_UNSUPPORTED;
+    if (tok && p.num_blocks * (int64_t)p.page_size > INT32_MAX)    // buffer rows are int32 slots
         return VA_ERR_UNSUPPORTED;
     if (p.num_q_heads % p.num_kv_heads != 0)
         return VA_ERR_UNSUPPORTED;
@@ -1679,9 +1851,11 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     if (p.total_q * (int64_t)p.num_q_heads >= INT32_MAX)    // q rows are indexed with 32-bit integers
         return VA_ERR_UNSUPPORTED;
     const int64_t bh = (int64_t)p.num_seqs * p.num_kv_heads;
-    if (bh > 65536 || bh * (int64_t)p.max_blocks_per_seq > INT32_MAX)
+    const int64_t mbps = tok ? std::max<int64_t>(1, ((int64_t)p.max_seqlen_k + kPage - 1) / kPage)
+                             : p.max_blocks_per_seq;
+    if (bh > 65536 || bh * mbps > INT32_MAX)
         return VA_ERR_UNSUPPORTED;
-    if ((int64_t)p.max_seqlen_k > (int64_t)p.max_blocks_per_seq * kPage)
+    if (!tok && (int64_t)p.max_seqlen_k > (int64_t)p.max_blocks_per_seq * kPage)
         return VA_ERR_INVALID_ARG;
 
     int cus = p.num_cus;
@@ -1703,6 +1877,7 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     if (!pl)
         return VA_ERR_INVALID_ARG;
     pl->prob = p;
+    pl->mbps = (int32_t)mbps;
     pl->log2g = G == 4 ? 2 : G == 8 ? 3 : 4;
     const int rows = G * p.max_seqlen_q;
     pl->rt = (rows + 15) / 16;
@@ -1756,19 +1931,40 @@ void va_plan_destroy(va_plan_t plan)
     delete plan;
 }
 
-va_status va_run_ex(va_plan_t plan, int32_t stage, const void *q, const void *k_pool,
-                    const void *v_pool, const int32_t *block_table,
-                    const int32_t *cu_seqlens_q, const int32_t *seqused_k,
-                    float softmax_scale, const float *k_descale, const float *v_descale,
-                    const float *sinks, void *out, void *workspace, size_t workspace_bytes,
-                    void *stream)
+}  // extern "C"
+
+namespace {
+
+struct TokArgs {                 // prefix + extend layout arguments
+    const int32_t *kv_indptr;
+    const int32_t *kv_indices;
+    int64_t num_kv_indices;
+    const void *k_extend;
+    const void *v_extend;
+};
+
+va_status run_impl(va_plan_t plan, int32_t stage, const void *q, const void *k_pool, const void *v_pool,
+                   const int32_t *block_table, const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                   const TokArgs *tok, float softmax_scale, const float *k_descale, const float *v_descale,
+                   const float *sinks, void *out, void *workspace, size_t workspace_bytes, void *stream)
 {
     if (!plan)
         return VA_ERR_INVALID_ARG;
     if (stage != VA_STAGE_ALL && stage != VA_STAGE_SPLIT_KV && stage != VA_STAGE_MERGE)
         return VA_ERR_INVALID_ARG;
-    if (!q || !k_pool || !v_pool || !block_table || !cu_seqlens_q || !seqused_k || !out)
+    if ((tok != nullptr) != (plan->prob.layout == VA_LAYOUT_PREFIX_EXTEND))
+        return VA_ERR_INVALID_ARG;                     // the entry point must match the plan's layout
+    if (!q || !k_pool || !v_pool || !cu_seqlens_q || !out)
         return VA_ERR_INVALID_ARG;
+    if (!tok && (!block_table || !seqused_k))
+        return VA_ERR_INVALID_ARG;
+    if (tok) {
+        if (!tok->kv_indptr || !tok->k_extend || !tok->v_extend || tok->num_kv_indices < 0 ||
+            tok->num_kv_indices > INT32_MAX - 16 || (tok->num_kv_indices > 0 && !tok->kv_indices))
+            return VA_ERR_INVALID_ARG;
+        if ((reinterpret_cast<uintptr_t>(tok->k_extend) | reinterpret_cast<uintptr_t>(tok->v_extend)) & 15)
+            return VA_ERR_INVALID_ARG;
+    }
     if (!workspace || workspace_bytes < plan->ws_bytes)
         return VA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
@@ -1781,7 +1977,7 @@ va_status va_run_ex(va_plan_t plan, int32_t stage, const void *q, const void *k_
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     unsigned char *ws = static_cast<unsigned char *>(workspace);
 
-    if (plan->debug && (stage == VA_STAGE_ALL || stage == VA_STAGE_SPLIT_KV)) {
+    if (plan->debug && !tok && (stage == VA_STAGE_ALL || stage == VA_STAGE_SPLIT_KV)) {
         // validate mode: check the metadata first (result in workspace meta
         // words 2 and 3, which the kernels leave alone) and wait for it
         int32_t *res = reinterpret_cast<int32_t *>(ws) + 2;
@@ -1823,16 +2019,20 @@ va_status va_run_ex(va_plan_t plan, int32_t stage, const void *q, const void *k_
         sp.hq = pr.num_q_heads;
         sp.hkv = pr.num_kv_heads;
         sp.log2g = plan->log2g;
-        sp.mbps = pr.max_blocks_per_seq;
+        sp.mbps = plan->mbps;
         sp.grid_n = plan->grid;
         sp.min_pages = plan->min_pages;
         sp.rows_max = plan->rows_max;
         sp.total_q = (int32_t)pr.total_q;
         sp.max_q = pr.max_seqlen_q;
         sp.num_blocks = pr.num_blocks;
-        const Variant &v = kVariants[plan->rt];
-        const bool cap = pr.softcap > 0.f;
-        launch_fn fn = pr.kv_dtype == VA_DT_FP8_E4M3FN ? (cap ? v.fp8_cap : v.fp8) : (cap ? v.bf16_cap : v.bf16);
+        sp.kv_indptr = tok ? tok->kv_indptr : nullptr;
+        sp.kv_indices = tok ? tok->kv_indices : nullptr;
+        sp.kext = tok ? static_cast<const uint8_t *>(tok->k_extend) : nullptr;
+        sp.vext = tok ? static_cast<const uint8_t *>(tok->v_extend) : nullptr;
+        sp.num_indices = tok ? tok->num_kv_indices : 0;
+        sp.num_rows = pr.num_blocks * pr.page_size;
+        launch_fn fn = select_launch(plan->rt, pr.kv_dtype == VA_DT_FP8_E4M3FN, pr.softcap > 0.f, tok != nullptr);
         fn(sp, plan->grid, s);
         if (hipGetLastError() != hipSuccess)
             return VA_ERR_HIP;
@@ -1866,6 +2066,33 @@ va_status va_run_ex(va_plan_t plan, int32_t stage, const void *q, const void *k_
         }
     }
     return VA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+va_status va_run_ex(va_plan_t plan, int32_t stage, const void *q, const void *k_pool,
+                    const void *v_pool, const int32_t *block_table,
+                    const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                    float softmax_scale, const float *k_descale, const float *v_descale,
+                    const float *sinks, void *out, void *workspace, size_t workspace_bytes,
+                    void *stream)
+{
+    return run_impl(plan, stage, q, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k, nullptr,
+                    softmax_scale, k_descale, v_descale, sinks, out, workspace, workspace_bytes, stream);
+}
+
+va_status va_run_prefix_extend(va_plan_t plan, int32_t stage, const void *q, const void *k_buffer,
+                               const void *v_buffer, const int32_t *kv_indptr, const int32_t *kv_indices,
+                               int64_t num_kv_indices, const void *k_extend, const void *v_extend,
+                               const int32_t *cu_seqlens_q, float softmax_scale, const float *k_descale,
+                               const float *v_descale, const float *sinks, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    const TokArgs tok = {kv_indptr, kv_indices, num_kv_indices, k_extend, v_extend};
+    return run_impl(plan, stage, q, k_buffer, v_buffer, nullptr, cu_seqlens_q, nullptr, &tok, softmax_scale,
+                    k_descale, v_descale, sinks, out, workspace, workspace_bytes, stream);
 }
 
 va_status va_run(va_plan_t plan, const void *q, const void *k_pool, const void *v_pool,
