@@ -62,6 +62,36 @@ def algorithmic_bytes(p, seqs=None) -> int:
     return int(kv + qo)
 
 
+def algorithmic_bytes_pe(pe, seqs=None) -> int:
+    """The same count for a prefix + extend call: every key row some query row
+    can see (prefix rows gathered by slot and draft rows, K and V, per kv head)
+    plus Q and O bytes.  There are no pages, so no partial-page rounding."""
+    elt = 1 if pe.kv_dtype == "fp8" else 2
+    idx = np.arange(pe.num_seqs) if seqs is None else np.asarray(seqs)
+    wl = getattr(pe, "window_left", -1)
+    keys = rows = 0
+    for b in idx:
+        lq = int(pe.cu_seqlens_q[b + 1] - pe.cu_seqlens_q[b])
+        lk = int(pe.kv_indptr[b + 1] - pe.kv_indptr[b]) + lq
+        if lq > 0:
+            keys += lk - (0 if wl < 0 else max(0, lk - lq - wl))
+            rows += lq
+    kv = keys * pe.num_kv_heads * pe.head_dim * elt * 2
+    qo = rows * pe.num_q_heads * pe.head_dim * 2 * 2
+    return int(kv + qo)
+
+
+def pe_head(pe, n):
+    """The first n sequences of a prefix + extend problem (slices of its metadata;
+    the row buffers are shared)."""
+    import dataclasses
+    e = int(pe.kv_indptr[n])
+    c = int(pe.cu_seqlens_q[n])
+    return dataclasses.replace(pe, q=pe.q[:c], k_extend=pe.k_extend[:c], v_extend=pe.v_extend[:c],
+                               kv_indptr=pe.kv_indptr[:n + 1].copy(), kv_indices=pe.kv_indices[:e].copy(),
+                               cu_seqlens_q=pe.cu_seqlens_q[:n + 1].copy())
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     with open(os.path.join(ROOT, "paged_gqa_attention_va_amd", "csrc", "va.hip"), "rb") as f:
@@ -82,6 +112,25 @@ def load_traffic(workload: str):
     if not e or e.get("source_hash") != source_hash():
         return None
     return e.get("bytes_per_launch")
+
+
+def cpu_baseline_pe(pe, budget_s: float = 12.0):
+    """Time the oracle on the first sequences of a prefix + extend call, one
+    more sequence per round, until about budget_s of work."""
+    import oracle
+    threads = oracle.default_threads()
+    n, secs = 0, 0.0
+    while n < pe.num_seqs and secs < budget_s:
+        n += 1
+        sub = pe_head(pe, n)
+        t0 = time.perf_counter()
+        oracle.attn_prefix_extend_problem(sub, threads=threads)
+        secs = time.perf_counter() - t0
+    nbytes = algorithmic_bytes_pe(pe, range(n))
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the first {n} of {pe.num_seqs} sequences (all their rows, re-layout included), "
+                      f"{nbytes} algorithmic bytes in {secs:.2f} s"}
 
 
 def cpu_baseline(p, budget_s: float = 12.0):
@@ -128,6 +177,10 @@ def main():
     ap.add_argument("--draft-extend", action="store_true",
                     help="draft-extend call: each step first builds the block table and seqused_k "
                          "from kv_indptr / kv_indices on the device (va_spec_block_table)")
+    ap.add_argument("--prefix-extend", choices=["tokens", "pages"], default=None,
+                    help="prefix + extend layout (va_run_prefix_extend): the same lengths with the "
+                         "prefix in a token-row buffer (slots one per token, or 16-row pages) and "
+                         "the draft tokens' K/V in separate buffers")
     ap.add_argument("--stage", choices=["all", "split", "merge"], default="all",
                     help="profiling aid: time only one kernel per step")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -175,6 +228,17 @@ def main():
         features.append("sinks")
     if args.draft_extend:
         features.append("draft-extend metadata")
+    pe = None
+    if args.prefix_extend:
+        if args.draft_extend:
+            ap.error("--prefix-extend and --draft-extend are different layouts")
+        q_lens = np.diff(p.cu_seqlens_q)
+        pe = va_inputs.prefix_extend(q_lens, p.seqused_k - q_lens, p.num_q_heads, p.num_kv_heads,
+                                     p.kv_dtype, seed=100 + args.config, slots=args.prefix_extend,
+                                     k_descale=p.k_descale, v_descale=p.v_descale,
+                                     window_left=p.window_left, softcap=p.softcap, sinks=p.sinks,
+                                     name=p.name + "-prefix-extend")
+        features.append(f"prefix + extend layout ({args.prefix_extend} slots)")
     if features:
         workload += " + " + ", ".join(features)
     log(f"bench: generated {p.name} in {time.perf_counter() - t0:.1f} s")
@@ -187,7 +251,13 @@ def main():
             t = t.view(torch.int16).view(torch.bfloat16)
         return t.to(dev)
 
-    k0, v0 = kv(p.k), kv(p.v)
+    if pe is not None:                    # rotate over copies of the row buffers instead
+        k0, v0 = kv(pe.k_buffer), kv(pe.v_buffer)
+        ke, ve = kv(pe.k_extend), kv(pe.v_extend)
+        pe_indptr = torch.from_numpy(pe.kv_indptr).to(dev)
+        pe_indices = torch.from_numpy(pe.kv_indices).to(dev)
+    else:
+        k0, v0 = kv(p.k), kv(p.v)
     ks = [k0] + [k0.clone() for _ in range(args.copies - 1)]
     vs = [v0] + [v0.clone() for _ in range(args.copies - 1)]
     bt = torch.from_numpy(p.block_table).to(dev)
@@ -206,12 +276,13 @@ def main():
             slots.append(p.block_table[b, j // p.page_size].astype(np.int64) * p.page_size + j % p.page_size)
         kv_indptr = torch.from_numpy(indptr).to(dev)
         kv_indices = torch.from_numpy(np.concatenate(slots).astype(np.int32)).to(dev)
-    plan = va.Plan.for_problem(p, force_grid=args.grid)
+    plan = (va.Plan.for_prefix_extend(pe, force_grid=args.grid) if pe is not None
+            else va.Plan.for_problem(p, force_grid=args.grid))
     ws = plan.workspace(dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
     log(f"bench: plan grid={plan.grid} workspace={plan.workspace_bytes} B, "
-        f"{args.copies} pool copies of {2 * p.k.nbytes / 2**20:.0f} MiB")
+        f"{args.copies} pool copies of {2 * k0.numel() * k0.element_size() / 2**20:.0f} MiB")
 
     stages = {"all": (va.VA_STAGE_SPLIT_KV, va.VA_STAGE_MERGE), "split": (va.VA_STAGE_SPLIT_KV,),
               "merge": (va.VA_STAGE_MERGE,)}[args.stage]
@@ -223,8 +294,12 @@ def main():
             bt_i, sk_i = va.spec_block_table(kv_indptr, kv_indices, p.block_table.shape[1],
                                              p.page_size, stream=stream)
         for s in stage_list:
-            plan.run(q, ks[c], vs[c], bt_i, cu, sk_i, p.scale, kd, vd, out=out, workspace=ws,
-                     stream=stream, stage=s, sinks=sinks)
+            if pe is not None:
+                plan.run_prefix_extend(q, ks[c], vs[c], pe_indptr, pe_indices, ke, ve, cu, p.scale, kd, vd,
+                                       out=out, workspace=ws, stream=stream, stage=s, sinks=sinks)
+            else:
+                plan.run(q, ks[c], vs[c], bt_i, cu, sk_i, p.scale, kd, vd, out=out, workspace=ws,
+                         stream=stream, stage=s, sinks=sinks)
 
     def timed(n, first, stage_list=stages):
         """Average ms per step over n back-to-back steps, HIP events on `stream`
@@ -240,8 +315,7 @@ def main():
         return a.elapsed_time(b) / n
 
     if args.stage == "merge":      # the merge reads what a split pass left in the workspace
-        plan.run(q, ks[0], vs[0], bt, cu, sk, p.scale, kd, vd, out=out, workspace=ws,
-                 stream=stream, stage=va.VA_STAGE_SPLIT_KV, sinks=sinks)
+        step(0, (va.VA_STAGE_SPLIT_KV,))
     t_w = time.perf_counter()
     n_warm = 0
     while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
@@ -253,7 +327,7 @@ def main():
     log(f"bench: {n_warm} warmup steps done in {time.perf_counter() - t_w:.1f} s")
 
     ms_step = timed(args.steps, n_warm)
-    alg = algorithmic_bytes(p)
+    alg = algorithmic_bytes_pe(pe) if pe is not None else algorithmic_bytes(p)
     value = alg / (ms_step * 1e-3) / 1e9
     log(f"bench: {args.steps} steps, {ms_step * 1e3:.2f} us/step, {value:.1f} GB/s effective")
 
@@ -273,7 +347,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(p)
+        cpu = cpu_baseline_pe(pe) if pe is not None else cpu_baseline(p)
         log(f"bench: cpu baseline {cpu}")
 
     rec = {

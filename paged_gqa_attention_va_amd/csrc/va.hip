@@ -1025,11 +1025,14 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
         auto issue_tok = [&](int k, int stage, int32_t raw) {
             const int32_t tag = tok_tag(raw, (p0 + 2 * k) * kPage + (pl & 31), pre, lk, q0, p.num_rows);
             const uint32_t dst = ring_addr + stage * kStageBytes + 8192 * rg;
+            int32_t t[8];                                      // all shuffles first: one LDS round trip
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                t[i] = __shfl(tag, 16 * (i >> 2) + 4 * (i & 3) + (pl >> 4));
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int n = 4 * (i & 3) + (pl >> 4);
-                const int32_t t = __shfl(tag, 16 * (i >> 2) + n);
-                dma16_at(tok_row(t, pool, ext, row_bytes) + (((pl & 15) ^ n) * 16),
+                dma16_at(tok_row(t[i], pool, ext, row_bytes) + (((pl & 15) ^ n) * 16),
                          dst + 4096 * (i >> 2) + 1024 * (i & 3));
             }
         };
@@ -1386,11 +1389,14 @@ void va_split_kv_bf16_w8_kernel(SplitParams p)
         auto issue_tok = [&](int k, int stage, int32_t raw) {
             const int32_t tag = tok_tag(raw, (p0 + k) * kPage + (pl & 15), pre, lk, q0, p.num_rows);
             const uint32_t dst = ring_addr + stage * kStageBytes + 8192 * rg;
+            int32_t t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                t[i] = __shfl(tag, 2 * i + (pl >> 5));
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int n = 2 * i + (pl >> 5);
-                const int32_t t = __shfl(tag, n);
-                dma16_at(tok_row(t, pool, ext, row_bytes) + (((pl & 31) ^ (n & 15)) * 16), dst + 1024 * i);
+                dma16_at(tok_row(t[i], pool, ext, row_bytes) + (((pl & 31) ^ (n & 15)) * 16), dst + 1024 * i);
             }
         };
         int32_t rawA = 0, rawB = 0, rawN = 0;
