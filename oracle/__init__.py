@@ -315,3 +315,38 @@ def attn_prefix_extend_problem(p, rows=None, threads=None):
         rows=rows, threads=threads, window_left=getattr(p, "window_left", -1),
         softcap=getattr(p, "softcap", 0.0),
         sinks=None if getattr(p, "sinks", None) is None else p.sinks.astype(np.float64))
+
+
+def attn_mla(q, kv_pool, kv_dtype: str, block_table, cu_seqlens_q, seqused_k, scale: float,
+             v_head_dim: int, k_descale: float = 1.0, v_descale: float = 1.0, rows=None,
+             threads=None, window_left: int = -1, softcap: float = 0.0,
+             sinks=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Absorbed-MLA verify attention: the PE_DIM split of the sglang PR #34517
+    summary page ("Key source snippets", verify_shared_kv_fwd: q_nope.k_nope
+    plus, when PE_DIM > 0, q_pe.k_pe; NOPE_DIM is the latent width of the
+    absorbed-MLA layout).
+
+    One kv head.  A cache row is [latent (v_head_dim) | RoPE part]; a query
+    row is [q_nope | q_pe] over the same widths.  The logit is the sum of the
+    two partial dot products, i.e. the dot product over the whole row, scaled
+    as in ``attn``.  Reading: the value of a key is its latent (the absorbed
+    layout keeps one cached vector per token; the page's output width is the
+    latent width).  So this is ``attn`` with V = the cache rows with their
+    RoPE part set to zero, keeping the first v_head_dim output dims.
+    Returns out [n_rows, v_head_dim] and the natural-log LSE, float64.
+    """
+    kv_pool = np.asarray(kv_pool)
+    v = kv_pool.copy()
+    v[..., v_head_dim:] = 0                 # +0.0 in both encodings
+    out, lse = attn(q, kv_pool, v, kv_dtype, block_table, cu_seqlens_q, seqused_k, 1, scale,
+                    k_descale, v_descale, rows=rows, threads=threads, window_left=window_left,
+                    softcap=softcap, sinks=sinks)
+    return np.ascontiguousarray(out[:, :v_head_dim]), lse
+
+
+def attn_mla_problem(p, rows=None, threads=None):
+    """``attn_mla`` on a ``va_inputs.Problem`` built by ``va_inputs.mla``."""
+    return attn_mla(p.q, p.k, p.kv_dtype, p.block_table, p.cu_seqlens_q, p.seqused_k, p.scale,
+                    p.v_head_dim, p.k_descale, p.v_descale, rows=rows, threads=threads,
+                    window_left=getattr(p, "window_left", -1), softcap=getattr(p, "softcap", 0.0),
+                    sinks=None if getattr(p, "sinks", None) is None else p.sinks.astype(np.float64))

@@ -56,6 +56,8 @@ class Problem:
     window_left: int = -1                  # sliding window: keys from i - window_left (-1 = none)
     softcap: float = 0.0                   # logit softcap (0 = none)
     sinks: Optional[np.ndarray] = None     # float32 [Hq] sink logits, or None
+    v_head_dim: Optional[int] = None       # absorbed MLA: V = the first v_head_dim dims of
+                                           # the K row (v is k); None = head_dim, separate V
 
     @property
     def num_seqs(self) -> int:
@@ -117,8 +119,13 @@ def custom(q_lens: Sequence[int], kv_lens: Sequence[int], num_q_heads: int,
            scale: Optional[float] = None, poison: bool = True,
            extra_blocks: int = 0, name: str = "custom",
            max_blocks_per_seq: Optional[int] = None, window_left: int = -1,
-           softcap: float = 0.0, sinks: Optional[Sequence[float]] = None) -> Problem:
+           softcap: float = 0.0, sinks: Optional[Sequence[float]] = None,
+           head_dim: int = HEAD_DIM, v_head_dim: Optional[int] = None) -> Problem:
     """Build one problem.
+
+    head_dim / v_head_dim: with v_head_dim < head_dim the call is absorbed MLA
+    (one kv head; a key's value is the first v_head_dim dims of its K row, and
+    the problem's v is the same array as k).
 
     table: "perm"     -- pages of all sequences are a seeded random permutation
                          of a pool that holds exactly the pages in use (+extra);
@@ -142,9 +149,11 @@ def custom(q_lens: Sequence[int], kv_lens: Sequence[int], num_q_heads: int,
         num_blocks = sum(pages) + extra_blocks
     num_blocks = max(num_blocks, 1)
     total_q = sum(q_lens)
-    q = _randn_bf16_bits(gen, (total_q, num_q_heads, HEAD_DIM))
-    k = _randn_kv_bits(gen, (num_blocks, PAGE, num_kv_heads, HEAD_DIM), kv_dtype)
-    v = _randn_kv_bits(gen, (num_blocks, PAGE, num_kv_heads, HEAD_DIM), kv_dtype)
+    mla = v_head_dim is not None and v_head_dim < head_dim
+    assert not mla or num_kv_heads == 1
+    q = _randn_bf16_bits(gen, (total_q, num_q_heads, head_dim))
+    k = _randn_kv_bits(gen, (num_blocks, PAGE, num_kv_heads, head_dim), kv_dtype)
+    v = k if mla else _randn_kv_bits(gen, (num_blocks, PAGE, num_kv_heads, head_dim), kv_dtype)
 
     bt = np.zeros((B, mbps), dtype=np.int32)
     if table == "identity":
@@ -168,18 +177,19 @@ def custom(q_lens: Sequence[int], kv_lens: Sequence[int], num_q_heads: int,
             if pages[b] and tail:
                 last = bt[b, pages[b] - 1]
                 k[last, tail:] = nan
-                v[last, tail:] = nan
+                v[last, tail:] = nan                 # no-op when v is k
             # entries past the last page point outside the pool
             bt[b, pages[b]:] = num_blocks + np.arange(mbps - pages[b], dtype=np.int32)
         k[~used] = nan
         v[~used] = nan
 
     if scale is None:
-        scale = HEAD_DIM ** -0.5
+        scale = head_dim ** -0.5
     sk_arr = None if sinks is None else np.asarray(sinks, dtype=np.float32)
     if sk_arr is not None:
         assert sk_arr.shape == (num_q_heads,)
-    return Problem(name=name, q=q, k=k, v=v, kv_dtype=kv_dtype, block_table=bt,
+    return Problem(name=name, q=q, k=k, v=v, kv_dtype=kv_dtype, block_table=bt, head_dim=head_dim,
+                   v_head_dim=v_head_dim if mla else None,
                    cu_seqlens_q=cu, seqused_k=seqused, num_q_heads=num_q_heads,
                    num_kv_heads=num_kv_heads, scale=_f32(scale),
                    k_descale=_f32(k_descale), v_descale=_f32(v_descale),
@@ -229,6 +239,24 @@ def config(i: int, variant: int = 0, poison: bool = True,
         return custom(ql, [131072] * 8, g, 1, dt, seed=s, poison=poison,
                       name=f"config4-g{g}-{dt}")
     raise ValueError(f"unknown config {i}")
+
+
+# Absorbed-MLA shape of the PR #34517 page's Kimi-K3 path: a 512-wide latent
+# plus a 64-wide RoPE part per key row, one kv head.
+MLA_LATENT = 512
+MLA_ROPE = 64
+
+
+def mla(q_lens: Sequence[int], kv_lens: Sequence[int], num_q_heads: int, kv_dtype: str = "fp8",
+        seed: int = 0, **kw) -> Problem:
+    """An absorbed-MLA verify problem: Q rows [q_nope (512) | q_pe (64)], one kv
+    head whose cache row is [latent (512) | k_pe (64)], V = the latent.  The
+    scale defaults to 192**-0.5 (a 128-wide no-RoPE head plus the 64-wide RoPE
+    part before absorption)."""
+    kw.setdefault("scale", (128 + MLA_ROPE) ** -0.5)
+    kw.setdefault("name", "mla")
+    return custom(q_lens, kv_lens, num_q_heads, 1, kv_dtype, seed=seed,
+                  head_dim=MLA_LATENT + MLA_ROPE, v_head_dim=MLA_LATENT, **kw)
 
 
 def sample_rows(p: Problem, n: int, seed: int = 0) -> np.ndarray:
