@@ -117,6 +117,8 @@ typedef struct {
     float softcap;               /* logit softcap: 0 = none; > 0: every scaled logit s is
                                     replaced by softcap * tanh(s / softcap) */
     int32_t layout;              /* va_layout of the KV cache (VA_LAYOUT_PAGED = 0) */
+    int32_t v_head_dim;          /* value / output width; 0 = head_dim.  head_dim 576 with
+                                    v_head_dim 512 is absorbed MLA (see below) */
 } va_problem;
 
 typedef struct va_plan_s *va_plan_t;
@@ -124,7 +126,7 @@ typedef struct va_plan_s *va_plan_t;
 /*
  * Check the problem and build a plan.
  * Supported domain (VA_ERR_UNSUPPORTED otherwise):
- *   - D = 256 and page 16;
+ *   - D = 256 and page 16; or absorbed MLA (below);
  *   - Q and out bf16; KV fp8 e4m3fn or bf16;
  *   - G = Hq/Hkv in {4, 8, 16}; 1 <= max_seqlen_q <= 4;
  *   - num_seqs * num_kv_heads <= 65536;
@@ -139,6 +141,18 @@ typedef struct va_plan_s *va_plan_t;
  * On success *out holds a new plan; release it with va_plan_destroy.
  */
 va_status va_plan(const va_problem *problem, va_plan_t *out);
+
+/*
+ * Absorbed MLA: the PE_DIM split of the sglang PR #34517 summary page's
+ * shared-KV verify kernel ("Key source snippets": q_nope.k_nope plus q_pe.k_pe,
+ * with the latent width as NOPE_DIM in its absorbed-MLA layout).
+ * head_dim = 576, v_head_dim = 512, num_kv_heads = 1, paged layout, no window
+ * or softcap.  A cache row [num_blocks, 16, 1, 576] is [latent (512) | RoPE
+ * part (64)]; q rows [total_q, Hq, 576] are [q_nope | q_pe]; the logit is the
+ * dot product over the whole row times softmax_scale * k_descale; the value
+ * of a key is its latent, so out is [total_q, Hq, 512] and va_run_ex must get
+ * v_pool == k_pool (VA_ERR_INVALID_ARG otherwise) and no sinks.
+ */
 
 /* Bytes of device workspace va_run needs for this plan. */
 va_status va_plan_workspace_bytes(va_plan_t plan, size_t *bytes);

@@ -52,7 +52,7 @@ class _Problem(ctypes.Structure):
         ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
         ("num_cus", ctypes.c_int32), ("force_grid", ctypes.c_int32),
         ("window_left", ctypes.c_int32), ("softcap", ctypes.c_float),
-        ("layout", ctypes.c_int32),
+        ("layout", ctypes.c_int32), ("v_head_dim", ctypes.c_int32),
     ]
 
 
@@ -123,7 +123,8 @@ class Plan:
                  num_blocks: int, total_q: int, kv_dtype: str = "fp8",
                  num_cus: int = 0, force_grid: int = 0, head_dim: int = 256,
                  window_left: int = -1, softcap: float = 0.0,
-                 page_size: int = 16, q_dtype: str = "bf16", layout: str = "paged"):
+                 page_size: int = 16, q_dtype: str = "bf16", layout: str = "paged",
+                 v_head_dim: int = 0):
         self._lib = library()
         if layout not in ("paged", "prefix_extend"):
             raise ValueError(f"unknown layout {layout!r}")
@@ -131,8 +132,9 @@ class Plan:
                       max_seqlen_q, max_seqlen_k, max_blocks_per_seq, num_blocks, total_q,
                       _dtype_code(q_dtype), _dtype_code(kv_dtype), num_cus, force_grid,
                       int(window_left), float(softcap),
-                      VA_LAYOUT_PAGED if layout == "paged" else VA_LAYOUT_PREFIX_EXTEND)
+                      VA_LAYOUT_PAGED if layout == "paged" else VA_LAYOUT_PREFIX_EXTEND, int(v_head_dim))
         self.problem = pr
+        self.v_head_dim = int(v_head_dim) or int(head_dim)
         self.kv_dtype = kv_dtype
         self.layout = layout
         h = ctypes.c_void_p()
@@ -157,7 +159,8 @@ class Plan:
         return cls(num_seqs=p.num_seqs, num_q_heads=p.num_q_heads, num_kv_heads=p.num_kv_heads,
                    max_seqlen_q=max(1, p.max_seqlen_q), max_seqlen_k=p.max_seqlen_k,
                    max_blocks_per_seq=int(p.block_table.shape[1]), num_blocks=p.num_blocks,
-                   total_q=p.total_q, kv_dtype=p.kv_dtype,
+                   total_q=p.total_q, kv_dtype=p.kv_dtype, head_dim=getattr(p, "head_dim", 256),
+                   v_head_dim=getattr(p, "v_head_dim", None) or 0,
                    window_left=getattr(p, "window_left", -1), softcap=getattr(p, "softcap", 0.0), **kw)
 
     @classmethod
@@ -239,12 +242,13 @@ class Plan:
         if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != self.problem.num_q_heads
                                   or not sinks.is_cuda or not sinks.is_contiguous()):
             raise ValueError("sinks must be a contiguous float32 device tensor with num_q_heads elements")
+        oshape = (q.shape[0], q.shape[1], self.v_head_dim)
         if out is None:
-            out = torch.empty_like(q)
+            out = torch.empty(oshape, dtype=torch.bfloat16, device=q.device)
         if workspace is None:
             workspace = self.workspace(q.device)
-        if out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous():
-            raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+        if out.dtype != torch.bfloat16 or tuple(out.shape) != oshape or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous bf16 tensor of shape {oshape}")
         if workspace.numel() * workspace.element_size() < self.workspace_bytes:
             raise ValueError("workspace smaller than plan.workspace_bytes")
         if stream is None:

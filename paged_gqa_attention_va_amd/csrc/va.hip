@@ -1506,9 +1506,545 @@ void va_split_kv_bf16_w8_kernel(SplitParams p)
     }
 }
 
-// Segment reduce.  One workgroup = 4 consecutive heads of one query token;
-// 64 threads per row, 4 dims each.  The partials of a row are read in chunks of
-// 8 slots with all loads of a chunk issued before any is used.
+// ------------------------------------------------ absorbed MLA (PE_DIM split) --
+//
+// One kv head whose cache row is [latent (512) | RoPE part (64)]: 576 values,
+// 576 bytes (FP8) or 1152 bytes (bf16) per key.  The logit of a query row
+// [q_nope | q_pe] is the dot product over the whole row (q_nope.k_nope +
+// q_pe.k_pe); the value of a key is its latent.  Each key row is copied into
+// LDS once and serves both contractions.
+//
+// Workgroup: 8 waves = 2 key groups x 4 row tiles of the packed rows
+// r = t G + h (up to 64).  Key group kg takes pages kg, kg + 2, ... of the
+// piece; its 4 waves share a 2-stage LDS ring of one page per stage.  Each wave
+// computes, for its own row tile, S^T = K Q^T over the 576 dims, its own
+// online softmax and O^T += V^T P^T over the 512 latent dims (32 O^T tiles,
+// 128 registers).  The two key groups merge in the epilogue.
+//
+// Ring rows: row n of a page sits at n * row bytes, its 16-byte chunk c at slot
+// c ^ swz(n), swz = (n >> 2) & 3 (FP8, 36 chunks a row) or (n >> 1) & 7 (bf16,
+// 72 chunks a row), so the 16 rows one lane group reads hit 16 distinct bank
+// quads.  A page copy is 9 (FP8) or 18 (bf16) 1-KiB copies; wave (kg, rt)
+// issues copies rt, rt + 4, ... of its key group's page.
+
+constexpr int kMlaDim = 576;                   // cache row and query row width
+constexpr int kMlaDv = 512;                    // latent = value width
+constexpr int kMlaRows = 64;                   // packed rows: up to 16 heads x 4 tokens
+constexpr int kMlaObufBytes = 2 * kMlaRows * kMlaDv * 2;   // epilogue: [kg][row][512] x 2 B
+
+template <int KVT> struct MlaCfg;
+template <> struct MlaCfg<kKvFp8> {
+    static constexpr int kRowBytes = kMlaDim;
+    static constexpr int kChunks = 36;
+    static constexpr int kCopies = 9;
+    static constexpr int kMaxCopies = 3;                   // wave rt = 0; the others 2
+    static constexpr int kQBytes = 4 * 5 * 2 * 64 * 32;     // [rt][c][hi, lo][lane] x 32 B
+    __device__ static int swz(int n) { return (n >> 2) & 3; }
+};
+template <> struct MlaCfg<kKvBf16> {
+    static constexpr int kRowBytes = 2 * kMlaDim;
+    static constexpr int kChunks = 72;
+    static constexpr int kCopies = 18;
+    static constexpr int kMaxCopies = 5;                   // waves rt = 0, 1; the others 4
+    static constexpr int kQBytes = 4 * 18 * 64 * 16;        // [rt][s][lane] x 16 B
+    __device__ static int swz(int n) { return (n >> 1) & 7; }
+};
+
+template <int KVT>
+constexpr int mla_lds_bytes()
+{
+    return (MlaCfg<KVT>::kQBytes + 4 * 16 * MlaCfg<KVT>::kRowBytes) > (kMlaObufBytes + 1024)
+               ? (MlaCfg<KVT>::kQBytes + 4 * 16 * MlaCfg<KVT>::kRowBytes)
+               : (kMlaObufBytes + 1024);
+}
+
+struct MlaState {
+    floatx4_t o[32];     // O^T tiles of the wave's row tile (dim mapping in mla_dim)
+    float m;             // running max (log2-scaled logits) of the lane's row
+    float l;             // the lane's partial sum of 2^(x - m)
+};
+
+// Dim of O^T tile T, element i, for lane group j (lane l holds row l%16):
+// FP8 cache: 16 (16 (T / 16) + 4 j + i) + T % 16; bf16: 8 (16 (T / 8) + 4 j + i) + T % 8.
+template <int KVT>
+__device__ __forceinline__ int mla_dim(int T, int j, int i)
+{
+    if constexpr (KVT == kKvFp8)
+        return 16 * (16 * (T >> 4) + 4 * j + i) + (T & 15);
+    else
+        return 8 * (16 * (T >> 3) + 4 * j + i) + (T & 7);
+}
+
+// S^T (16 keys x 16 rows of row tile rt) of one page, FP8: 5 chunks of 128
+// dims (the last one half empty: dims 576..639 are zero in Q and skipped in K),
+// Q as the exact hi + lo pair.
+__device__ __forceinline__ floatx4_t mla_qk_f8(const unsigned char *stage, const unsigned char *qlds, int rt,
+                                               int lane)
+{
+    const int n = lane & 15, j = lane >> 4;
+    const int sw = MlaCfg<kKvFp8>::swz(n);
+    floatx4_t S = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 5; ++c) {
+        const int c0 = 8 * c + 2 * j;
+        uint4 a = *reinterpret_cast<const uint4 *>(stage + kMlaDim * n + 16 * (c0 ^ sw));
+        uint4 b = *reinterpret_cast<const uint4 *>(stage + kMlaDim * n + 16 * ((c0 + 1) ^ sw));
+        if (c == 4 && j >= 2) {                        // dims 576.. do not exist
+            a = make_uint4(0, 0, 0, 0);
+            b = make_uint4(0, 0, 0, 0);
+        }
+        const intx8_t kop = intx8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+            const uint4 *qp = reinterpret_cast<const uint4 *>(qlds + ((size_t)((rt * 5 + c) * 2 + part) * 64 + lane) * 32);
+            const uint4 q0 = qp[0], q1 = qp[1];
+            const intx8_t qop = intx8_t{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w,
+                                        (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+            S = mfma16_f8(kop, qop, S);
+        }
+        asm volatile("" ::: "memory");                 // one chunk's operands live at a time
+    }
+    return S;
+}
+
+// The same for a bf16 cache: 18 slices of 32 dims on v_mfma_f32_16x16x32_bf16.
+__device__ __forceinline__ floatx4_t mla_qk_bf16(const unsigned char *stage, const unsigned char *qlds, int rt,
+                                                 int lane)
+{
+    const int n = lane & 15, j = lane >> 4;
+    const int sw = MlaCfg<kKvBf16>::swz(n);
+    floatx4_t S = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 18; ++s) {
+        const bf16x8_t kop = *reinterpret_cast<const bf16x8_t *>(stage + 2 * kMlaDim * n + 16 * ((4 * s + j) ^ sw));
+        const bf16x8_t qop = *reinterpret_cast<const bf16x8_t *>(qlds + ((size_t)(rt * 18 + s) * 64 + lane) * 16);
+        S = mfma16(kop, qop, S);
+    }
+    return S;
+}
+
+// Online softmax of one page for the wave's row tile (lane: row l%16, keys
+// key0 + 4 (l/16) + e); same rules as softmax_step1.  Returns the P^T operand.
+__device__ __forceinline__ shortx4_t mla_softmax(MlaState &st, const floatx4_t &S, int limit, int key0, float c,
+                                                 int lane, bool masked)
+{
+    const int j = lane >> 4;
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float v = S[e] * c;
+        x[e] = (masked && key0 + 4 * j + e > limit) ? -INFINITY : v;
+    }
+    const float lmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__any(lmax > st.m + kTau)) {
+        float t = fmaxf(lmax, __shfl_xor(lmax, 16));
+        t = fmaxf(t, __shfl_xor(t, 32));
+        const bool need = t > st.m + kTau;
+        const float alpha = need ? exp2_fast(st.m - t) : 1.0f;
+        st.m = need ? t : st.m;
+        st.l *= alpha;
+#pragma unroll
+        for (int T = 0; T < 32; ++T)
+            st.o[T] *= alpha;
+    }
+    const float mref = st.m == -INFINITY ? 0.0f : st.m;
+    float pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        pv[e] = exp2_fast(x[e] - mref);
+    st.l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+    return __builtin_bit_cast(shortx4_t, make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])));
+}
+
+// O^T += V^T P^T over the latent of one page, FP8: lane (m, j) reads chunk
+// 16 h + m (16 dims) of key rows 4 j .. 4 j + 3, transposes the 4 x 16 bytes in
+// registers and converts them exactly to bf16 (K = 16 keys per MFMA).
+// zmask: key rows 4 j + e at or past the sequence's end read as zero.
+__device__ __forceinline__ void mla_pv_f8(MlaState &st, const unsigned char *stage, const shortx4_t &pop,
+                                          uint32_t zmask, int lane)
+{
+    const int m = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint4 w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int n = 4 * j + e;                             // swz(n) = j
+            w[e] = *reinterpret_cast<const uint4 *>(stage + kMlaDim * n + 16 * ((16 * h + m) ^ j));
+            if (zmask & (1u << e))
+                w[e] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t w0 = u4get(w[0], d), w1 = u4get(w[1], d), w2 = u4get(w[2], d), w3 = u4get(w[3], d);
+            const uint32_t a = byte_perm(w1, w0, 0x05010400u);   // w0.0 w1.0 w0.1 w1.1
+            const uint32_t b = byte_perm(w1, w0, 0x07030602u);   // w0.2 w1.2 w0.3 w1.3
+            const uint32_t cc = byte_perm(w3, w2, 0x05010400u);
+            const uint32_t dd = byte_perm(w3, w2, 0x07030602u);
+            const uint32_t tr[4] = {byte_perm(cc, a, 0x05040100u), byte_perm(cc, a, 0x07060302u),
+                                    byte_perm(dd, b, 0x05040100u), byte_perm(dd, b, 0x07060302u)};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {                        // dim 4 d + x of the chunk, keys 0..3
+                const shortx4_t av = __builtin_bit_cast(
+                    shortx4_t, make_uint2(fp8x2_lo_to_bf16x2(tr[x]), fp8x2_hi_to_bf16x2(tr[x])));
+                const int T = 16 * h + 4 * d + x;
+                st.o[T] = mfma16k16(av, pop, st.o[T]);
+            }
+        }
+        asm volatile("" ::: "memory");                 // one pass's rows live at a time
+    }
+}
+
+// The same for a bf16 cache: chunk 16 h + m (8 dims) of key rows 4 j .. 4 j + 3.
+__device__ __forceinline__ void mla_pv_bf16(MlaState &st, const unsigned char *stage, const shortx4_t &pop,
+                                            uint32_t zmask, int lane)
+{
+    const int m = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        uint4 w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int n = 4 * j + e;
+            w[e] = *reinterpret_cast<const uint4 *>(stage + 2 * kMlaDim * n +
+                                                    16 * ((16 * h + m) ^ MlaCfg<kKvBf16>::swz(n)));
+            if (zmask & (1u << e))
+                w[e] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t w01 = byte_perm(u4get(w[1], x >> 1), u4get(w[0], x >> 1), sel);
+            const uint32_t w23 = byte_perm(u4get(w[3], x >> 1), u4get(w[2], x >> 1), sel);
+            const int T = 8 * h + x;
+            st.o[T] = mfma16k16(__builtin_bit_cast(shortx4_t, make_uint2(w01, w23)), pop, st.o[T]);
+        }
+    }
+}
+
+// Split-KV main kernel for absorbed MLA.  Same work split (stream-K over the
+// pages of all sequences), partials and whole-piece output rules as the GQA
+// kernels, with 512-wide rows of O.
+template <int KVT>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void va_mla_split_kernel(SplitParams p)
+{
+    using C = MlaCfg<KVT>;
+    constexpr int kPageBytes = 16 * C::kRowBytes;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[mla_lds_bytes<KVT>()];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const int rt = wave & 3;                           // row tile
+    const int kg = wave >> 2;                          // key group
+    const int w = blockIdx.x;
+    const int G = 1 << p.log2g;
+
+    Share sh = locate(p, w, lane, w == 0 && wave == 0);
+    sh.n_eff = uniform(sh.n_eff);
+    sh.s = uniform(sh.s);
+    sh.e = uniform(sh.e);
+    sh.bg = uniform(sh.bg);
+    sh.base = uniform(sh.base);
+    if (w >= sh.n_eff)
+        return;                                        // uniform over the workgroup
+
+    const float kd = p.kdesc ? p.kdesc[0] : 1.0f;
+    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
+    const float c = p.scale_log2 * kd;
+    unsigned char *qlds = lds;
+    unsigned char *ring = lds + C::kQBytes + kg * 2 * kPageBytes;
+    const uint32_t ring_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(ring));
+    const uint32_t lds_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(lds));
+    const int64_t page_bytes = (int64_t)kPage * C::kRowBytes;
+    const int ncp = uniform((C::kCopies - rt + 3) / 4);     // copies this wave issues per page
+
+    const int bh = p.num_seqs;                             // one kv head
+    int s = sh.s, bg = sh.bg, base = sh.base;
+    while (s < sh.e && bg < bh) {
+        int pl = lane;                                 // opaque per piece (see the FP8 GQA kernel)
+        asm volatile("" : "+v"(pl));
+        const int b = bg;
+        const int q0 = load_uniform(p.cu, b);
+        const int lq = checked_q_len(q0, load_uniform(p.cu, b + 1), p.total_q, p.max_q);
+        const int lk = load_uniform(p.seqused, b);
+        const int cnt = (lq <= 0 || lk <= 0) ? 0 : max(0, min((lk + kPage - 1) / kPage, p.mbps));
+        if (cnt == 0) {
+            ++bg;
+            continue;
+        }
+        const int ctx = lk - lq;
+        const int r0 = s - base;
+        const int r1 = min(sh.e, base + cnt) - base;
+        const bool whole = (r0 == 0 && r1 == cnt);
+        const int p0 = r0;
+        const int npg = r1 - r0;                           // pages of the piece
+        const int nsteps = (npg + 1) >> 1;                 // steps of key group 0 (uniform)
+        const int slot = w + bg;
+        const int R = lq * G;
+        const bool rows_live = 16 * rt < R;
+        const int32_t *btrow = p.bt + (int64_t)b * p.mbps;
+        const int64_t maxpage = p.num_blocks - 1;
+        auto issue = [&](int k, int stage) {               // this wave's copies of page k of the piece
+            int64_t y = load_uniform(btrow, uniform(p0 + k));
+            y = y < 0 ? 0 : (y > maxpage ? maxpage : y);
+            const uint8_t *a = p.k + y * page_bytes;
+            const uint32_t dst = ring_addr + stage * kPageBytes;
+            int ln = lane;                                 // lane offsets rederived per copy (no
+            asm volatile("" : "+v"(ln));                   // registers held across the page loop)
+#pragma unroll
+            for (int i = 0; i < C::kMaxCopies; ++i)
+                if (i < ncp) {
+                    const int sl = 64 * (rt + 4 * i) + ln;     // LDS slot of this lane's 16 bytes
+                    const int n = sl / C::kChunks;             // key row
+                    const uint32_t off = (uint32_t)(n * C::kRowBytes + 16 * ((sl - n * C::kChunks) ^ C::swz(n)));
+                    dma16(a, off, dst + 1024 * (rt + 4 * i));
+                }
+        };
+        auto wait_own = [&]() {                            // this wave's copies of the older page landed
+            if (ncp == C::kMaxCopies)
+                wait_vmcnt<C::kMaxCopies>();
+            else
+                wait_vmcnt<C::kMaxCopies - 1>();
+        };
+
+        // ---- prologue: the first page of each key group; Q operands; the second
+        __syncthreads();                                   // previous piece's LDS reads done
+        float crow = c;                                    // logit multiplier of this lane's row
+        if constexpr (KVT == kKvFp8) {
+            if (kg < npg)
+                issue(kg, 0);
+            // this wave's row tile, lane (row n, j): dims 128 cc + 32 j .. +32
+            const int n = pl & 15, j = pl >> 4;
+            const int r = 16 * rt + n;
+            const int t = r >> p.log2g;
+            const bool live = r < R;
+            const uint16_t *qrow = p.q + ((int64_t)(q0 + (live ? t : 0)) * p.hq + (r & (G - 1))) * kMlaDim;
+            uint32_t raw[5][16];
+#pragma unroll
+            for (int cc = 0; cc < 5; ++cc) {
+                const bool have = live && (cc < 4 || j < 2);   // dims 576.. do not exist
+                const int jj = cc < 4 ? j : (j & 1);           // in-row address for every lane
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint4 v = *reinterpret_cast<const uint4 *>(qrow + 128 * cc + 32 * jj + 8 * i);
+                    if (!have)
+                        v = make_uint4(0, 0, 0, 0);
+                    raw[cc][4 * i] = v.x;
+                    raw[cc][4 * i + 1] = v.y;
+                    raw[cc][4 * i + 2] = v.z;
+                    raw[cc][4 * i + 3] = v.w;
+                }
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < 5; ++cc)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, raw[cc][i] << 16)),
+                                             fabsf(__builtin_bit_cast(float, raw[cc][i] & 0xFFFF0000u))));
+            amax = fmaxf(amax, __shfl_xor(amax, 16));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));          // row max (4 lanes)
+            int kx = 0;
+            if (amax > 0.f) {
+                int e;
+                frexpf(amax, &e);
+                kx = min(8 - e, 127);
+            }
+            crow = ldexpf(c, -kx);
+            // key group 0 converts chunks 0..2, key group 1 chunks 3..4
+#pragma unroll
+            for (int cc = 0; cc < 5; ++cc)
+                if ((cc < 3) == (kg == 0))
+                    convert_q_block<1>(qlds, raw[cc], kx, rt * 5 + cc, pl);
+            __syncthreads();                               // Q operands visible
+            if (kg + 2 < npg)
+                issue(kg + 2, 1);
+        } else {
+            // Q operands copied straight in operand order: copy i = rt' * 18 + sl,
+            // lane l gets dims 32 sl + 8 (l/16) .. +8 of packed row 16 rt' + l%16
+            const uint16_t *qbase = p.q + (int64_t)q0 * p.hq * kMlaDim;
+            for (int i = wave; i < 4 * 18; i += 8) {
+                const int rr = i / 18, sl = i - rr * 18;
+                const int r = 16 * rr + (pl & 15);
+                int t = r >> p.log2g;
+                t = r < R ? t : 0;
+                const uint32_t voff = (uint32_t)(((t * p.hq + (r & (G - 1))) * kMlaDim + 32 * sl + 8 * (pl >> 4)) * 2);
+                dma16(qbase, voff, lds_addr + i * 1024);
+            }
+            if (kg < npg)
+                issue(kg, 0);
+            if (kg + 2 < npg)
+                issue(kg + 2, 1);
+            wait_vmcnt<0>();                               // (the loop's barrier publishes Q)
+        }
+
+        // O starts at zero only here: an opaque zero keeps the 128 accumulator
+        // registers from being set (and held) across the Q conversion above
+        float z = 0.f;
+        asm volatile("" : "+v"(z));
+        MlaState st;
+        st.m = -INFINITY;
+        st.l = 0.f;
+#pragma unroll
+        for (int T = 0; T < 32; ++T)
+            st.o[T] = floatx4_t{z, z, z, z};
+        int limit;
+        {
+            const int r = 16 * rt + (pl & 15);
+            limit = min(ctx + (r >> p.log2g), lk - 1);
+        }
+
+        for (int t = 0; t < nsteps; ++t) {
+            const int k = kg + 2 * t;                      // page of the piece
+            if (KVT == kKvFp8 && t == 0 && k + 2 < npg)
+                wait_own();                                // page k landed (page k + 2 may not)
+            else
+                wait_vmcnt<0>();
+            __syncthreads();                               // the group's copies too; stage t-1 free
+            if (t >= 1 && k + 2 < npg)
+                issue(k + 2, (t + 1) & 1);
+            if (k < npg && rows_live) {
+                // lane-derived LDS addresses are rederived each step from an
+                // opaque lane index: hoisted out of the loop they would hold
+                // some 30 registers next to the 128 accumulators
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const unsigned char *stage = ring + (t & 1) * kPageBytes;
+                const int key0 = (p0 + k) * kPage;
+                const bool masked = key0 + 15 > ctx;
+                floatx4_t S;
+                if constexpr (KVT == kKvFp8)
+                    S = mla_qk_f8(stage, qlds, rt, ln);
+                else
+                    S = mla_qk_bf16(stage, qlds, rt, ln);
+                const shortx4_t pop = mla_softmax(st, S, limit, key0, crow, ln, masked);
+                uint32_t zmask = 0;
+                if (key0 + 15 >= lk) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (key0 + 4 * (ln >> 4) + e >= lk)
+                            zmask |= 1u << e;
+                }
+                if constexpr (KVT == kKvFp8)
+                    mla_pv_f8(st, stage, pop, zmask, ln);
+                else
+                    mla_pv_bf16(st, stage, pop, zmask, ln);
+            }
+        }
+        wait_vmcnt<0>();
+
+        // ---- epilogue: merge the two key groups, then the final rows or a partial
+        st.l += __shfl_xor(st.l, 16);
+        st.l += __shfl_xor(st.l, 32);
+        __syncthreads();                                   // every wave is past its loop
+        float *ml = reinterpret_cast<float *>(lds + kMlaObufBytes);
+        unsigned char *obuf = lds;
+        {
+            const int n = pl & 15, j = pl >> 4;
+            const int row = 16 * rt + n;
+            if (j == 0) {
+                ml[(kg * kMlaRows + row) * 2] = st.m;
+                ml[(kg * kMlaRows + row) * 2 + 1] = st.l;
+            }
+            const float inv = st.l > 0.f ? 1.0f / st.l : 0.f;
+            unsigned char *orow = obuf + (size_t)(kg * kMlaRows + row) * 1024;
+            if constexpr (KVT == kKvFp8) {                 // 16-dim chunks 16 h + 4 j + i
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int q = 16 * h + 4 * j + i;
+                        uint32_t v[8];
+#pragma unroll
+                        for (int x = 0; x < 8; ++x)
+                            v[x] = pack_f16x2(st.o[16 * h + 2 * x][i] * inv, st.o[16 * h + 2 * x + 1][i] * inv);
+                        *reinterpret_cast<uint4 *>(orow + 16 * ((2 * q) ^ n)) = make_uint4(v[0], v[1], v[2], v[3]);
+                        *reinterpret_cast<uint4 *>(orow + 16 * ((2 * q + 1) ^ n)) = make_uint4(v[4], v[5], v[6], v[7]);
+                    }
+            } else {                                       // 8-dim chunks 16 h + 4 j + i
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int q = 16 * h + 4 * j + i;
+                        uint32_t v[4];
+#pragma unroll
+                        for (int x = 0; x < 4; ++x)
+                            v[x] = pack_bf16x2(st.o[8 * h + 2 * x][i] * inv, st.o[8 * h + 2 * x + 1][i] * inv);
+                        *reinterpret_cast<uint4 *>(orow + 16 * (q ^ n)) = make_uint4(v[0], v[1], v[2], v[3]);
+                    }
+            }
+        }
+        __syncthreads();
+        const int tid = opaque_tid();
+        const int nrows = min(R, kMlaRows);
+        for (int it = tid; it < nrows * 64; it += 512) {
+            const int r = it >> 6, u = it & 63;            // row, 8-dim unit
+            float M = -INFINITY;
+            float mk[2], lkk[2];
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                mk[k2] = ml[(k2 * kMlaRows + r) * 2];
+                lkk[k2] = ml[(k2 * kMlaRows + r) * 2 + 1];
+                M = fmaxf(M, lkk[k2] > 0.f ? mk[k2] : -INFINITY);
+            }
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            float W = 0.f;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const float wk = lkk[k2] > 0.f ? lkk[k2] * exp2_fast(mk[k2] - M) : 0.f;
+                W += wk;
+                const uint4 v = *reinterpret_cast<const uint4 *>(obuf + (size_t)(k2 * kMlaRows + r) * 1024 +
+                                                                 16 * (u ^ (r & 15)));
+                acc[0] += wk * xlo<KVT>(v.x);
+                acc[1] += wk * xhi<KVT>(v.x);
+                acc[2] += wk * xlo<KVT>(v.y);
+                acc[3] += wk * xhi<KVT>(v.y);
+                acc[4] += wk * xlo<KVT>(v.z);
+                acc[5] += wk * xhi<KVT>(v.z);
+                acc[6] += wk * xlo<KVT>(v.w);
+                acc[7] += wk * xhi<KVT>(v.w);
+            }
+            const int t = r >> p.log2g, hh = r & (G - 1);
+            if (whole) {
+                const float sc = W > 0.f ? vd / W : 0.f;
+                uint4 o;
+                o.x = pack_bf16x2(acc[0] * sc, acc[1] * sc);
+                o.y = pack_bf16x2(acc[2] * sc, acc[3] * sc);
+                o.z = pack_bf16x2(acc[4] * sc, acc[5] * sc);
+                o.w = pack_bf16x2(acc[6] * sc, acc[7] * sc);
+                *reinterpret_cast<uint4 *>(p.out + ((int64_t)(q0 + t) * p.hq + hh) * kMlaDv + 8 * u) = o;
+            } else {
+                const float sc = W > 0.f ? 1.0f / W : 0.f;
+                const int64_t sr = ((int64_t)slot * kMlaRows + r) * kMlaDv + 8 * u;
+                if constexpr (KVT == kKvFp8) {
+                    uint4 o;
+                    o.x = pack_f16x2(acc[0] * sc, acc[1] * sc);
+                    o.y = pack_f16x2(acc[2] * sc, acc[3] * sc);
+                    o.z = pack_f16x2(acc[4] * sc, acc[5] * sc);
+                    o.w = pack_f16x2(acc[6] * sc, acc[7] * sc);
+                    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.ws_o) + sr) = o;
+                } else {
+                    float4 *dst = reinterpret_cast<float4 *>(static_cast<float *>(p.ws_o) + sr);
+                    dst[0] = make_float4(acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc);
+                    dst[1] = make_float4(acc[4] * sc, acc[5] * sc, acc[6] * sc, acc[7] * sc);
+                }
+                if (u == 0)
+                    p.ws_lse[(int64_t)slot * kMlaRows + r] = W > 0.f ? M + __log2f(W) : -INFINITY;
+            }
+        }
+
+        s = base + r1;
+        base += cnt;
+        ++bg;
+    }
+}
+
+// Segment reduce.  One workgroup = 256 / (DV / 4) consecutive heads of one
+// query token (4 for 256-wide rows, 2 for the 512-wide MLA rows); DV / 4
+// threads per row, 4 dims each.  The partials of a row are read in chunks of
+// 16 slots with all loads of a chunk issued before any is used.
 template <bool kHalf>
 __device__ __forceinline__ float4 load_partial4(const void *base, int64_t idx)
 {
@@ -1520,11 +2056,13 @@ __device__ __forceinline__ float4 load_partial4(const void *base, int64_t idx)
     }
 }
 
-template <bool kHalf>
+template <bool kHalf, int DV>
 __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
 {
     constexpr int kChunk = 16;
-    const int gq = (1 << p.log2g) >> 2;               // head quads per group
+    constexpr int kTpr = DV / 4;                        // threads per row
+    constexpr int kHpb = kThreads / kTpr;               // heads per workgroup
+    const int gq = (1 << p.log2g) / kHpb;               // workgroups per (token, group)
     int idx = blockIdx.x;
     const int hq4 = idx % gq;
     idx /= gq;
@@ -1549,13 +2087,13 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
     const int w1 = (int)(((int64_t)e * n - 1) / total);
     if (w0 == w1)
         return;                                        // written by the main kernel
-    const int h = hq4 * 4 + (threadIdx.x >> 6);
+    const int h = hq4 * kHpb + threadIdx.x / kTpr;
     const int row = (t << p.log2g) + h;
-    const int d = (threadIdx.x & 63) * 4;
+    const int d = (threadIdx.x % kTpr) * 4;
     const float *lse = p.ws_lse + (int64_t)(w0 + bg) * p.rows_max + row;
-    const int64_t o0 = ((int64_t)(w0 + bg) * p.rows_max + row) * kHeadDim + d;
+    const int64_t o0 = ((int64_t)(w0 + bg) * p.rows_max + row) * DV + d;
     const int64_t lstride = p.rows_max;
-    const int64_t ostride = (int64_t)p.rows_max * kHeadDim;
+    const int64_t ostride = (int64_t)p.rows_max * DV;
     const int ns = w1 - w0 + 1;
 
     // One pass over the slots, kChunk at a time with every load of a chunk in
@@ -1615,7 +2153,7 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
     pk.x = pack_bf16x2(acc.x * inv, acc.y * inv);
     pk.y = pack_bf16x2(acc.z * inv, acc.w * inv);
     const int G = 1 << p.log2g;
-    *reinterpret_cast<uint2 *>(p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + d) = pk;
+    *reinterpret_cast<uint2 *>(p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * DV + d) = pk;
 }
 
 // Draft-extend metadata: one thread per block-table entry (b, page).  Page pg
@@ -1768,6 +2306,7 @@ struct va_plan_s {
     int64_t slots;
     int32_t mbps;       // pages per sequence bound: the block-table row, or (prefix + extend)
                         // ceil(max_seqlen_k / 16)
+    bool mla;           // absorbed MLA: 576-wide rows, 512-wide values (va_mla_split_kernel)
     size_t off_prefix, off_lse, off_o, ws_bytes;
     bool debug;         // VA_DEBUG set at va_plan: validate mode and a plan dump on stderr
 };
@@ -1841,8 +2380,17 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     if (p.layout != VA_LAYOUT_PAGED && p.layout != VA_LAYOUT_PREFIX_EXTEND)
         return VA_ERR_INVALID_ARG;
     const bool tok = p.layout == VA_LAYOUT_PREFIX_EXTEND;
-    if (p.head_dim != kHeadDim || (!tok && p.page_size != kPage))
+    const int dv = p.v_head_dim == 0 ? p.head_dim : p.v_head_dim;
+    if (p.v_head_dim < 0)
+        return VA_ERR_INVALID_ARG;
+    const bool mla = p.head_dim == kMlaDim;
+    if (mla) {                                         // absorbed MLA: one kv head, paged, causal only
+        if (dv != kMlaDv || p.num_kv_heads != 1 || tok || p.page_size != kPage || p.window_left != -1 ||
+            p.softcap != 0.f)
+            return VA_ERR_UNSUPPORTED;
+    } else if (p.head_dim != kHeadDim || dv != kHeadDim || (!tok && p.page_size != kPage)) {
         return VA_ERR_UNSUPPORTED;
+    }
     if (tok && p.num_blocks * (int64_t)p.page_size > INT32_MAX)    // buffer rows are int32 slots
         return VA_ERR_UNSUPPORTED;
     if (p.num_q_heads % p.num_kv_heads != 0)
@@ -1887,7 +2435,8 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     pl->log2g = G == 4 ? 2 : G == 8 ? 3 : 4;
     const int rows = G * p.max_seqlen_q;
     pl->rt = (rows + 15) / 16;
-    pl->rows_max = 16 * 2 * (pl->rt <= 2 ? 1 : 2);      // 2 row groups x RTW row tiles
+    pl->mla = mla;
+    pl->rows_max = mla ? kMlaRows : 16 * 2 * (pl->rt <= 2 ? 1 : 2);   // 2 row groups x RTW row tiles
     pl->grid = p.force_grid > 0 ? p.force_grid : cus;
     pl->min_pages = 8;
     pl->slots = (int64_t)pl->grid + bh;
@@ -1898,7 +2447,7 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     off = align_up(off + (size_t)pl->slots * pl->rows_max * 4, 256);
     pl->off_o = off;
     const size_t part_elt = p.kv_dtype == VA_DT_FP8_E4M3FN ? 2 : 4;   // fp16 or fp32 partial O
-    off = align_up(off + (size_t)pl->slots * pl->rows_max * kHeadDim * part_elt, 256);
+    off = align_up(off + (size_t)pl->slots * pl->rows_max * (mla ? kMlaDv : kHeadDim) * part_elt, 256);
 
     pl->ws_bytes = off;
     pl->debug = debug_env();
@@ -1963,6 +2512,8 @@ va_status run_impl(va_plan_t plan, int32_t stage, const void *q, const void *k_p
     if (!q || !k_pool || !v_pool || !cu_seqlens_q || !out)
         return VA_ERR_INVALID_ARG;
     if (!tok && (!block_table || !seqused_k))
+        return VA_ERR_INVALID_ARG;
+    if (plan->mla && (k_pool != v_pool || sinks))      // V is the latent part of the K rows
         return VA_ERR_INVALID_ARG;
     if (tok) {
         if (!tok->kv_indptr || !tok->k_extend || !tok->v_extend || tok->num_kv_indices < 0 ||
@@ -2038,8 +2589,16 @@ va_status run_impl(va_plan_t plan, int32_t stage, const void *q, const void *k_p
         sp.vext = tok ? static_cast<const uint8_t *>(tok->v_extend) : nullptr;
         sp.num_indices = tok ? tok->num_kv_indices : 0;
         sp.num_rows = pr.num_blocks * pr.page_size;
-        launch_fn fn = select_launch(plan->rt, pr.kv_dtype == VA_DT_FP8_E4M3FN, pr.softcap > 0.f, tok != nullptr);
-        fn(sp, plan->grid, s);
+        if (plan->mla) {
+            if (pr.kv_dtype == VA_DT_FP8_E4M3FN)
+                hipLaunchKernelGGL(va_mla_split_kernel<kKvFp8>, dim3(plan->grid), dim3(512), 0, s, sp);
+            else
+                hipLaunchKernelGGL(va_mla_split_kernel<kKvBf16>, dim3(plan->grid), dim3(512), 0, s, sp);
+        } else {
+            launch_fn fn = select_launch(plan->rt, pr.kv_dtype == VA_DT_FP8_E4M3FN, pr.softcap > 0.f,
+                                         tok != nullptr);
+            fn(sp, plan->grid, s);
+        }
         if (hipGetLastError() != hipSuccess)
             return VA_ERR_HIP;
     }
@@ -2060,13 +2619,15 @@ va_status run_impl(va_plan_t plan, int32_t stage, const void *q, const void *k_p
         mp.max_q = pr.max_seqlen_q;
         mp.rows_max = plan->rows_max;
         mp.total_q = (int32_t)pr.total_q;
+        const int hpb = plan->mla ? 2 : 4;                 // heads per merge workgroup
         const int64_t blocks = (int64_t)pr.num_seqs * pr.num_kv_heads * pr.max_seqlen_q *
-                               ((pr.num_q_heads / pr.num_kv_heads) / 4);
+                               ((pr.num_q_heads / pr.num_kv_heads) / hpb);
         if (blocks > 0) {
-            if (pr.kv_dtype == VA_DT_FP8_E4M3FN)
-                hipLaunchKernelGGL(va_merge_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s, mp);
-            else
-                hipLaunchKernelGGL(va_merge_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, s, mp);
+            const bool half = pr.kv_dtype == VA_DT_FP8_E4M3FN;
+            void (*merge)(MergeParams) =
+                plan->mla ? (half ? va_merge_kernel<true, kMlaDv> : va_merge_kernel<false, kMlaDv>)
+                          : (half ? va_merge_kernel<true, kHeadDim> : va_merge_kernel<false, kHeadDim>);
+            hipLaunchKernelGGL(merge, dim3((unsigned)blocks), dim3(kThreads), 0, s, mp);
             if (hipGetLastError() != hipSuccess)
                 return VA_ERR_HIP;
         }

@@ -121,3 +121,23 @@ def test_status_strings():
     for s in range(6):
         assert va.status_str(s) and va.status_str(s) != "unknown status"
     assert va.status_str(99) == "unknown status"
+
+
+def test_plan_checks_the_mla_domain():
+    mla = dict(num_seqs=4, num_q_heads=16, num_kv_heads=1, max_seqlen_q=4, max_seqlen_k=4096,
+               max_blocks_per_seq=256, num_blocks=1024, total_q=16, num_cus=256, head_dim=576)
+    assert va.Plan(**mla, v_head_dim=512).v_head_dim == 512
+    for kw, status in ((dict(v_head_dim=576), va.VA_ERR_UNSUPPORTED),
+                       (dict(v_head_dim=512, num_kv_heads=2, num_q_heads=32), va.VA_ERR_UNSUPPORTED),
+                       (dict(v_head_dim=512, window_left=10), va.VA_ERR_UNSUPPORTED),
+                       (dict(v_head_dim=512, softcap=5.0), va.VA_ERR_UNSUPPORTED),
+                       (dict(v_head_dim=512, layout="prefix_extend", page_size=1), va.VA_ERR_UNSUPPORTED),
+                       (dict(v_head_dim=-1), va.VA_ERR_INVALID_ARG)):
+        d = dict(mla)
+        d.update(kw)
+        with pytest.raises(va.VaError) as e:
+            va.Plan(**d)
+        assert e.value.status == status, kw
+    with pytest.raises(va.VaError) as e:           # 256-wide heads with another value width
+        va.Plan(**base_problem(), v_head_dim=128)
+    assert e.value.status == va.VA_ERR_UNSUPPORTED
