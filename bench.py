@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0
 MAIN_KERNEL = {"fp8": "va_split_kv_fp8_w8_kernel", "bf16": "va_split_kv_bf16_w8_kernel"}
+MLA_KERNEL = "va_mla_split_kernel"
 # Arithmetic of the path: FP8 KV runs QK^T on fp8 MFMA (Q as an exact hi/lo fp8
 # pair) and PV on bf16 MFMA; bf16 KV runs both on bf16 MFMA; fp32 accumulation.
 COMPUTE_DTYPE = {"fp8": "fp8/bf16", "bf16": "bf16"}
@@ -48,6 +49,7 @@ def algorithmic_bytes(p, seqs=None) -> int:
     elt = 1 if p.kv_dtype == "fp8" else 2
     idx = np.arange(p.num_seqs) if seqs is None else np.asarray(seqs)
     wl = getattr(p, "window_left", -1)
+    dv = getattr(p, "v_head_dim", None)
     pages = 0
     rows = 0
     for b in idx:
@@ -57,6 +59,10 @@ def algorithmic_bytes(p, seqs=None) -> int:
             first = 0 if wl < 0 else max(0, lk - lq - wl) // p.page_size
             pages += -(-lk // p.page_size) - first
             rows += lq
+    if dv:                                 # absorbed MLA: one cache row serves K and V
+        kv = pages * p.page_size * p.head_dim * elt
+        qo = rows * p.num_q_heads * (p.head_dim + dv) * 2
+        return int(kv + qo)
     kv = pages * p.num_kv_heads * p.page_size * p.head_dim * elt * 2
     qo = rows * p.num_q_heads * p.head_dim * 2 * 2
     return int(kv + qo)
@@ -145,7 +151,8 @@ def cpu_baseline(p, budget_s: float = 12.0):
         if len(rows) == 0:
             continue
         t0 = time.perf_counter()
-        oracle.attn_problem(p, rows=rows, threads=threads)
+        run = oracle.attn_mla_problem if getattr(p, "v_head_dim", None) else oracle.attn_problem
+        run(p, rows=rows, threads=threads)
         secs += time.perf_counter() - t0
         done_seqs.append(b)
         if secs >= budget_s:
@@ -181,6 +188,9 @@ def main():
                     help="prefix + extend layout (va_run_prefix_extend): the same lengths with the "
                          "prefix in a token-row buffer (slots one per token, or 16-row pages) and "
                          "the draft tokens' K/V in separate buffers")
+    ap.add_argument("--mla", choices=["fp8", "bf16"], default=None,
+                    help="absorbed-MLA call of the same batch shape: 576-wide cache rows "
+                         "(512 latent + 64 RoPE), one kv head, the workload's query heads")
     ap.add_argument("--stage", choices=["all", "split", "merge"], default="all",
                     help="profiling aid: time only one kernel per step")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -216,6 +226,13 @@ def main():
     t0 = time.perf_counter()
     p = va_inputs.config(args.config, args.variant)
     workload = va_inputs.CONFIG_NAMES[args.config] if args.config != 4 else p.name
+    if args.mla:
+        q_lens = np.diff(p.cu_seqlens_q)
+        p = va_inputs.mla(q_lens, p.seqused_k, p.num_q_heads // p.num_kv_heads, args.mla,
+                          seed=200 + args.config, k_descale=p.k_descale, v_descale=p.v_descale,
+                          name=p.name + "-mla")
+        workload = (f"absorbed MLA {p.num_seqs} seqs q{int(p.max_seqlen_q)} kv{int(p.max_seqlen_k)} "
+                    f"{p.num_q_heads}q/1kv 512+64 {args.mla}")
     features = []
     if args.window > 0:
         p.window_left = args.window - 1
@@ -229,6 +246,8 @@ def main():
     if args.draft_extend:
         features.append("draft-extend metadata")
     pe = None
+    if args.mla and (args.prefix_extend or args.draft_extend or features):
+        ap.error("--mla runs the paged causal call without window, softcap, sinks or other layouts")
     if args.prefix_extend:
         if args.draft_extend:
             ap.error("--prefix-extend and --draft-extend are different layouts")
@@ -259,7 +278,7 @@ def main():
     else:
         k0, v0 = kv(p.k), kv(p.v)
     ks = [k0] + [k0.clone() for _ in range(args.copies - 1)]
-    vs = [v0] + [v0.clone() for _ in range(args.copies - 1)]
+    vs = ks if getattr(p, "v_head_dim", None) else [v0] + [v0.clone() for _ in range(args.copies - 1)]
     bt = torch.from_numpy(p.block_table).to(dev)
     cu = torch.from_numpy(p.cu_seqlens_q).to(dev)
     sk = torch.from_numpy(p.seqused_k).to(dev)
@@ -279,7 +298,7 @@ def main():
     plan = (va.Plan.for_prefix_extend(pe, force_grid=args.grid) if pe is not None
             else va.Plan.for_problem(p, force_grid=args.grid))
     ws = plan.workspace(dev)
-    out = torch.empty_like(q)
+    out = torch.empty((q.shape[0], q.shape[1], plan.v_head_dim), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
     log(f"bench: plan grid={plan.grid} workspace={plan.workspace_bytes} B, "
         f"{args.copies} pool copies of {2 * k0.numel() * k0.element_size() / 2**20:.0f} MiB")
@@ -342,7 +361,8 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                     "traffic": load_traffic(workload),
-                    "kernel": MAIN_KERNEL[p.kv_dtype], "us_per_launch": round(main_ms * 1e3, 3)}
+                    "kernel": MLA_KERNEL if args.mla else MAIN_KERNEL[p.kv_dtype],
+                    "us_per_launch": round(main_ms * 1e3, 3)}
         log(f"bench: main kernel {main_ms * 1e3:.2f} us/launch, {achieved:.1f} GB/s")
 
     cpu = None

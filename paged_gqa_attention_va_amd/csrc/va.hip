@@ -1583,15 +1583,19 @@ __device__ __forceinline__ floatx4_t mla_qk_f8(const unsigned char *stage, const
 {
     const int n = lane & 15, j = lane >> 4;
     const int sw = MlaCfg<kKvFp8>::swz(n);
-    floatx4_t S = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    floatx4_t Sp[2][2];                                // [chunk parity][hi, lo]: 4 independent chains
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+        Sp[a][0] = Sp[a][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 5; ++c) {
         const int c0 = 8 * c + 2 * j;
         uint4 a = *reinterpret_cast<const uint4 *>(stage + kMlaDim * n + 16 * (c0 ^ sw));
         uint4 b = *reinterpret_cast<const uint4 *>(stage + kMlaDim * n + 16 * ((c0 + 1) ^ sw));
-        if (c == 4 && j >= 2) {                        // dims 576.. do not exist
-            a = make_uint4(0, 0, 0, 0);
-            b = make_uint4(0, 0, 0, 0);
+        if (c == 4) {                                  // dims 576.. do not exist: lanes j >= 2
+            const uint32_t keep = (uint32_t)((j >> 1) - 1);    // all ones for j < 2, else 0
+            a.x &= keep; a.y &= keep; a.z &= keep; a.w &= keep;
+            b.x &= keep; b.y &= keep; b.z &= keep; b.w &= keep;
         }
         const intx8_t kop = intx8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 #pragma unroll
@@ -1600,11 +1604,11 @@ __device__ __forceinline__ floatx4_t mla_qk_f8(const unsigned char *stage, const
             const uint4 q0 = qp[0], q1 = qp[1];
             const intx8_t qop = intx8_t{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w,
                                         (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
-            S = mfma16_f8(kop, qop, S);
+            Sp[c & 1][part] = mfma16_f8(kop, qop, Sp[c & 1][part]);
         }
         asm volatile("" ::: "memory");                 // one chunk's operands live at a time
     }
-    return S;
+    return (Sp[0][0] + Sp[1][0]) + (Sp[0][1] + Sp[1][1]);
 }
 
 // The same for a bf16 cache: 18 slices of 32 dims on v_mfma_f32_16x16x32_bf16.
@@ -1613,14 +1617,17 @@ __device__ __forceinline__ floatx4_t mla_qk_bf16(const unsigned char *stage, con
 {
     const int n = lane & 15, j = lane >> 4;
     const int sw = MlaCfg<kKvBf16>::swz(n);
-    floatx4_t S = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    floatx4_t Sp[3];                                   // 3 independent chains
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+        Sp[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 18; ++s) {
         const bf16x8_t kop = *reinterpret_cast<const bf16x8_t *>(stage + 2 * kMlaDim * n + 16 * ((4 * s + j) ^ sw));
         const bf16x8_t qop = *reinterpret_cast<const bf16x8_t *>(qlds + ((size_t)(rt * 18 + s) * 64 + lane) * 16);
-        S = mfma16(kop, qop, S);
+        Sp[s % 3] = mfma16(kop, qop, Sp[s % 3]);
     }
-    return S;
+    return (Sp[0] + Sp[1]) + Sp[2];
 }
 
 // Online softmax of one page for the wave's row tile (lane: row l%16, keys
@@ -1659,9 +1666,10 @@ __device__ __forceinline__ shortx4_t mla_softmax(MlaState &st, const floatx4_t &
 // O^T += V^T P^T over the latent of one page, FP8: lane (m, j) reads chunk
 // 16 h + m (16 dims) of key rows 4 j .. 4 j + 3, transposes the 4 x 16 bytes in
 // registers and converts them exactly to bf16 (K = 16 keys per MFMA).
-// zmask: key rows 4 j + e at or past the sequence's end read as zero.
+// tail (uniform): the page reaches the sequence's end; then the key rows
+// 4 j + e flagged in zmask (at or past the end) read as zero.
 __device__ __forceinline__ void mla_pv_f8(MlaState &st, const unsigned char *stage, const shortx4_t &pop,
-                                          uint32_t zmask, int lane)
+                                          bool tail, uint32_t zmask, int lane)
 {
     const int m = lane & 15, j = lane >> 4;
 #pragma unroll
@@ -1671,8 +1679,13 @@ __device__ __forceinline__ void mla_pv_f8(MlaState &st, const unsigned char *sta
         for (int e = 0; e < 4; ++e) {
             const int n = 4 * j + e;                             // swz(n) = j
             w[e] = *reinterpret_cast<const uint4 *>(stage + kMlaDim * n + 16 * ((16 * h + m) ^ j));
-            if (zmask & (1u << e))
-                w[e] = make_uint4(0, 0, 0, 0);
+        }
+        if (tail) {                                              // uniform: the sequence's last page
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t keep = ((zmask >> e) & 1u) - 1u;    // 0 for a zeroed row
+                w[e].x &= keep; w[e].y &= keep; w[e].z &= keep; w[e].w &= keep;
+            }
         }
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -1697,7 +1710,7 @@ __device__ __forceinline__ void mla_pv_f8(MlaState &st, const unsigned char *sta
 
 // The same for a bf16 cache: chunk 16 h + m (8 dims) of key rows 4 j .. 4 j + 3.
 __device__ __forceinline__ void mla_pv_bf16(MlaState &st, const unsigned char *stage, const shortx4_t &pop,
-                                            uint32_t zmask, int lane)
+                                            bool tail, uint32_t zmask, int lane)
 {
     const int m = lane & 15, j = lane >> 4;
 #pragma unroll
@@ -1708,8 +1721,13 @@ __device__ __forceinline__ void mla_pv_bf16(MlaState &st, const unsigned char *s
             const int n = 4 * j + e;
             w[e] = *reinterpret_cast<const uint4 *>(stage + 2 * kMlaDim * n +
                                                     16 * ((16 * h + m) ^ MlaCfg<kKvBf16>::swz(n)));
-            if (zmask & (1u << e))
-                w[e] = make_uint4(0, 0, 0, 0);
+        }
+        if (tail) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t keep = ((zmask >> e) & 1u) - 1u;
+                w[e].x &= keep; w[e].y &= keep; w[e].z &= keep; w[e].w &= keep;
+            }
         }
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
@@ -1919,17 +1937,16 @@ void va_mla_split_kernel(SplitParams p)
                 else
                     S = mla_qk_bf16(stage, qlds, rt, ln);
                 const shortx4_t pop = mla_softmax(st, S, limit, key0, crow, ln, masked);
+                const bool tail = key0 + 15 >= lk;                 // uniform
                 uint32_t zmask = 0;
-                if (key0 + 15 >= lk) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (key0 + 4 * (ln >> 4) + e >= lk)
-                            zmask |= 1u << e;
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (key0 + 4 * (ln >> 4) + e >= lk)
+                        zmask |= 1u << e;
                 if constexpr (KVT == kKvFp8)
-                    mla_pv_f8(st, stage, pop, zmask, ln);
+                    mla_pv_f8(st, stage, pop, tail, zmask, ln);
                 else
-                    mla_pv_bf16(st, stage, pop, zmask, ln);
+                    mla_pv_bf16(st, stage, pop, tail, zmask, ln);
             }
         }
         wait_vmcnt<0>();
