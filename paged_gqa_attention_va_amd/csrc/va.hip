@@ -73,8 +73,10 @@ struct SplitParams {
     const float *kdesc;
     const float *vdesc;
     uint16_t *out;
-    void *ws_o;           // [slots][rows_max][256]: fp16 (FP8 cache) or fp32 (bf16 cache)
-    float *ws_lse;        // [slots][rows_max]   log2-domain LSE of the scaled logits
+    void *ws_o;           // [2 grid][rows_max][256]: fp16 (FP8 cache) or fp32 (bf16 cache);
+                          // slot 2 w = workgroup w's first piece, 2 w + 1 its last (only
+                          // those two pieces of a workgroup can be split)
+    float *ws_lse;        // [2 grid][rows_max]   log2-domain LSE of the scaled logits
     int32_t *ws_prefix;   // [BH + 1] exclusive prefix of page counts, [BH] = total
     int32_t *ws_meta;     // [0] = workgroups in use
     float scale_log2;     // softmax_scale * log2(e)
@@ -994,7 +996,7 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
         const int r1 = min(sh.e, base + cnt) - base;
         const bool whole = (r0 == 0 && r1 == cnt);
         const int p0 = pb + r0, p1 = pb + r1;
-        const int slot = w + bg;
+        const int slot = 2 * w + (s != sh.s);           // first or last piece of this workgroup
         const int lo_max = p.window_left < 0 ? INT_MIN : ctx + lq - 1 - p.window_left;
         const uint32_t wlim = p.window_left < 0 ? 0x7FFFFFFFu : (uint32_t)p.window_left;
 
@@ -1365,7 +1367,7 @@ void va_split_kv_bf16_w8_kernel(SplitParams p)
         const int r1 = min(sh.e, base + cnt) - base;
         const bool whole = (r0 == 0 && r1 == cnt);
         const int p0 = pb + r0;
-        const int slot = w + bg;
+        const int slot = 2 * w + (s != sh.s);           // first or last piece of this workgroup
         const int lo_max = p.window_left < 0 ? INT_MIN : ctx + lq - 1 - p.window_left;
         const uint32_t wlim = p.window_left < 0 ? 0x7FFFFFFFu : (uint32_t)p.window_left;
 
@@ -1798,7 +1800,7 @@ void va_mla_split_kernel(SplitParams p)
         const int p0 = r0;
         const int npg = r1 - r0;                           // pages of the piece
         const int nsteps = (npg + 1) >> 1;                 // steps of key group 0 (uniform)
-        const int slot = w + bg;
+        const int slot = 2 * w + (s != sh.s);           // first or last piece of this workgroup
         const int R = lq * G;
         const bool rows_live = 16 * rt < R;
         const int32_t *btrow = p.bt + (int64_t)b * p.mbps;
@@ -2107,11 +2109,12 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
     const int h = hq4 * kHpb + threadIdx.x / kTpr;
     const int row = (t << p.log2g) + h;
     const int d = (threadIdx.x % kTpr) * 4;
-    const float *lse = p.ws_lse + (int64_t)(w0 + bg) * p.rows_max + row;
-    const int64_t o0 = ((int64_t)(w0 + bg) * p.rows_max + row) * DV + d;
-    const int64_t lstride = p.rows_max;
-    const int64_t ostride = (int64_t)p.rows_max * DV;
+    // Slots of the pieces: workgroup w0 holds this pair as its first piece
+    // (slot 2 w0) if the pair starts where w0's range starts, else as its last
+    // (2 w0 + 1); every later workgroup w holds it as its first piece (2 w).
+    const int first0 = s > (int)(((int64_t)w0 * total) / n) ? 1 : 0;
     const int ns = w1 - w0 + 1;
+    auto slot_of = [&](int si) -> int64_t { return si == 0 ? 2 * w0 + first0 : 2 * (w0 + si); };
 
     // One pass over the slots, kChunk at a time with every load of a chunk in
     // flight; the running max moves per chunk (the sum is rescaled then).
@@ -2123,9 +2126,9 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
         float4 v[kChunk];
 #pragma unroll
         for (int i = 0; i < kChunk; ++i) {                 // unconditional loads (a slot past the
-            const int si = min(c0 + i, ns - 1);             // end re-reads the last one), then masked
-            l[i] = lse[si * lstride];
-            v[i] = load_partial4<kHalf>(p.ws_o, o0 + si * ostride);
+            const int64_t sl = slot_of(min(c0 + i, ns - 1));  // end re-reads the last one), then masked
+            l[i] = p.ws_lse[sl * p.rows_max + row];
+            v[i] = load_partial4<kHalf>(p.ws_o, (sl * p.rows_max + row) * DV + d);
         }
 #pragma unroll
         for (int i = 0; i < kChunk; ++i)
@@ -2456,7 +2459,7 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     pl->rows_max = mla ? kMlaRows : 16 * 2 * (pl->rt <= 2 ? 1 : 2);   // 2 row groups x RTW row tiles
     pl->grid = p.force_grid > 0 ? p.force_grid : cus;
     pl->min_pages = 8;
-    pl->slots = (int64_t)pl->grid + bh;
+    pl->slots = 2 * (int64_t)pl->grid;                 // a first and a last piece per workgroup
     size_t off = 256;                                   // meta
     pl->off_prefix = off;
     off = align_up(off + (size_t)(bh + 1) * 4, 256);

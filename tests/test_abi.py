@@ -141,3 +141,13 @@ def test_plan_checks_the_mla_domain():
     with pytest.raises(va.VaError) as e:           # 256-wide heads with another value width
         va.Plan(**base_problem(), v_head_dim=128)
     assert e.value.status == va.VA_ERR_UNSUPPORTED
+
+
+def test_workspace_is_bounded_by_the_grid_not_the_pairs():
+    small = va.Plan(**base_problem())                                  # 16 pairs
+    big = va.Plan(**base_problem(num_seqs=16384, num_kv_heads=4, num_q_heads=16, max_seqlen_q=1,
+                                 max_seqlen_k=32, max_blocks_per_seq=2, total_q=16384))   # 65536 pairs
+    assert big.grid == small.grid == 256
+    # two partial slots per workgroup, plus the page prefix over the pairs
+    assert big.workspace_bytes < small.workspace_bytes + 65537 * 4 + 4096
+    assert big.workspace_bytes < 16 << 20
