@@ -9,10 +9,16 @@
 //      K/V page once, straight from HBM into an LDS ring, and reuses it for all
 //      G*q_len packed query rows (GQA packing); MFMA QK^T and PV with an online
 //      softmax; then either the final rows or a partial (o, lse) per piece.
+//      A template flag selects the paged layout (block table) or the prefix +
+//      extend layout (keys gathered row by row through kv_indices, draft keys
+//      from separate buffers).
+//  va_mla_split_kernel  The same split for absorbed MLA: 576-wide cache rows
+//                       (latent + RoPE part), values = the 512-wide latent.
 //  va_merge_kernel      Segment reduce: log-sum-exp merge of the partials of
 //                       every (sequence, kv head) that was split over
-//                       workgroups.
-//  va_spec_block_table_kernel, va_fp8_to_bf16_kernel   metadata and test helpers.
+//                       workgroups (256- or 512-wide rows).
+//  va_spec_block_table_kernel, va_validate_kernel, va_fp8_to_bf16_kernel
+//                       draft-extend metadata, validate mode, test helper.
 //
 // The method comes from the sglang PR #36330 summary page ("Implementation
 // breakdown", item 1: pack the G query heads and speculative tokens of a group
@@ -31,9 +37,8 @@
 // Stream-K partition: WG w of N handles flat pages [floor(w*P/N),
 // floor((w+1)*P/N)) where P is the total page count, computed on the device from
 // seqused_k / cu_seqlens_q.  Any length mix therefore balances over the CUs
-// with no host-side lengths (graph-safe).  A piece (w, bg) writes its partial to
-// workspace slot w + bg, which is unique (a later WG cannot meet an earlier
-// sequence).
+// with no host-side lengths (graph-safe).  Only a WG's first and last piece can
+// be split: they write their partials to workspace slots 2w and 2w + 1.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -1561,21 +1566,10 @@ constexpr int mla_lds_bytes()
 }
 
 struct MlaState {
-    floatx4_t o[32];     // O^T tiles of the wave's row tile (dim mapping in mla_dim)
+    floatx4_t o[32];     // O^T tiles of the wave's row tile (dim mapping: see the epilogue)
     float m;             // running max (log2-scaled logits) of the lane's row
     float l;             // the lane's partial sum of 2^(x - m)
 };
-
-// Dim of O^T tile T, element i, for lane group j (lane l holds row l%16):
-// FP8 cache: 16 (16 (T / 16) + 4 j + i) + T % 16; bf16: 8 (16 (T / 8) + 4 j + i) + T % 8.
-template <int KVT>
-__device__ __forceinline__ int mla_dim(int T, int j, int i)
-{
-    if constexpr (KVT == kKvFp8)
-        return 16 * (16 * (T >> 4) + 4 * j + i) + (T & 15);
-    else
-        return 8 * (16 * (T >> 3) + 4 * j + i) + (T & 7);
-}
 
 // S^T (16 keys x 16 rows of row tile rt) of one page, FP8: 5 chunks of 128
 // dims (the last one half empty: dims 576..639 are zero in Q and skipped in K),
@@ -2272,9 +2266,6 @@ __global__ __launch_bounds__(kThreads) void va_validate_kernel(ValidateParams p)
 }
 
 // ------------------------------------------------------------------ host --
-
-typedef void (*split_fn)(SplitParams);
-
 
 typedef void (*launch_fn)(SplitParams, int, hipStream_t);
 
