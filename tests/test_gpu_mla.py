@@ -96,3 +96,13 @@ def test_mla_long_context_sampled(dt):
     got = as_f64(run_mla(p))
     ref, _ = oracle.attn_mla_problem(p, rows=rows)
     compare(got[rows], ref, p.name)
+
+
+@pytest.mark.parametrize("dt", ["fp8", "bf16"])
+def test_mla_long_pieces(dt):
+    """Two sequences of 9000 keys on a 3-workgroup split: each piece spans
+    several hundred pages (the kernel reads its block-table entries in chunks
+    of 256 pages)."""
+    p = vi.mla([4, 3], [9000, 8190], 16, dt, seed=29, name=f"mla-long-pieces-{dt}")
+    ref, _ = oracle.attn_mla_problem(p)
+    compare(as_f64(run_mla(p, force_grid=3)), ref, p.name)
