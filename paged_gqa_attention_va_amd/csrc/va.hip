@@ -597,9 +597,11 @@ __device__ __forceinline__ void dma_step_part(uint32_t stage, const uint8_t *poo
 // S = K.hi + K.lo carries the same information as the bf16 product, and the
 // logit multiplier of row r absorbs 2^-k_r.
 //
-// LDS layout of the Q operands: [rt][kc][part][lane] x 32 bytes, where kc
-// selects dims [128 kc, 128 kc + 128), part 0 = hi, 1 = lo, and lane l holds
-// row 16 rt + l%16, dims 128 kc + 32 (l/16) .. +32.
+// LDS layout of the Q operands: [rt][kc][part][half][lane] x 16 bytes, where
+// kc selects dims [128 kc, 128 kc + 128), part 0 = hi, 1 = lo, and lane l
+// holds row 16 rt + l%16, dims 128 kc + 32 (l/16) + 16 half .. +16.  Keeping a
+// lane's two halves 1 KiB apart makes each 16-byte operand read of a wave one
+// contiguous 1 KiB (a 32-byte lane stride costs a two-way bank conflict).
 constexpr int kQf8Bytes = 4 * 2 * 2 * 64 * 32;              // up to 4 row tiles: 32 KiB
 
 // The piece's packed Q rows arrive in the Q area as bf16, 512 B per row
@@ -634,12 +636,12 @@ __device__ __forceinline__ void convert_q_block(unsigned char *qlds, const uint3
         lo[i] = (uint32_t)lw;
     }
     // block blk = rt * 2 + kc of the whole tile set; parts 0 (hi) and 1 (lo)
-    uint4 *dh = reinterpret_cast<uint4 *>(qlds + ((size_t)(blk * 2) * 64 + lane) * 32);
-    uint4 *dl = reinterpret_cast<uint4 *>(qlds + ((size_t)(blk * 2 + 1) * 64 + lane) * 32);
+    uint4 *dh = reinterpret_cast<uint4 *>(qlds + (size_t)(blk * 2) * 2048 + lane * 16);
+    uint4 *dl = reinterpret_cast<uint4 *>(qlds + (size_t)(blk * 2 + 1) * 2048 + lane * 16);
     dh[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    dh[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+    dh[64] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
     dl[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    dl[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+    dl[64] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
 }
 
 template <int RTW>
@@ -735,8 +737,8 @@ __device__ __forceinline__ void qk_lds_f8(floatx4_t (&S)[2][RTW], const unsigned
 #pragma unroll
             for (int part = 0; part < 2; ++part) {
                 const uint4 *qp = reinterpret_cast<const uint4 *>(
-                    qw + ((size_t)((rt * 2 + kc) * 2 + part) * 64 + lane) * 32);
-                const uint4 b0 = qp[0], b1 = qp[1];
+                    qw + (size_t)((rt * 2 + kc) * 2 + part) * 2048 + lane * 16);
+                const uint4 b0 = qp[0], b1 = qp[64];
                 const intx8_t qop = intx8_t{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
                                             (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
 #pragma unroll
@@ -1529,9 +1531,11 @@ void va_split_kv_bf16_w8_kernel(SplitParams p)
 // 128 registers).  The two key groups merge in the epilogue.
 //
 // Ring rows: row n of a page sits at n * row bytes, its 16-byte chunk c at slot
-// c ^ swz(n), swz = (n >> 2) & 3 (FP8, 36 chunks a row) or (n >> 1) & 7 (bf16,
-// 72 chunks a row), so the 16 rows one lane group reads hit 16 distinct bank
-// quads.  A page copy is 9 (FP8) or 18 (bf16) 1-KiB copies; wave (kg, rt)
+// c ^ swz(n), swz = ((n >> 2) ^ (n >> 3)) & 3 (FP8, 36 chunks a row) or
+// (n >> 1) & 7 (bf16, 72 chunks a row).  Both were chosen by measuring LDS bank
+// conflicts (SQ_LDS_BANK_CONFLICT) of the two read patterns on gfx950 (QK:
+// one chunk of 16 rows; PV: 16 chunks of one row): neither conflicts.  The
+// FP8 swizzle (n >> 2) & 3 costs a two-way conflict on the QK reads.  A page copy is 9 (FP8) or 18 (bf16) 1-KiB copies; wave (kg, rt)
 // issues copies rt, rt + 4, ... of its key group's page.
 
 constexpr int kMlaDim = 576;                   // cache row and query row width
@@ -1545,8 +1549,8 @@ template <> struct MlaCfg<kKvFp8> {
     static constexpr int kChunks = 36;
     static constexpr int kCopies = 9;
     static constexpr int kMaxCopies = 3;                   // wave rt = 0; the others 2
-    static constexpr int kQBytes = 4 * 5 * 2 * 64 * 32;     // [rt][c][hi, lo][lane] x 32 B
-    __device__ static int swz(int n) { return (n >> 2) & 3; }
+    static constexpr int kQBytes = 4 * 5 * 2 * 64 * 32;     // [rt][c][hi, lo][half][lane] x 16 B
+    __device__ static int swz(int n) { return ((n >> 2) ^ (n >> 3)) & 3; }
 };
 template <> struct MlaCfg<kKvBf16> {
     static constexpr int kRowBytes = 2 * kMlaDim;
@@ -1574,21 +1578,58 @@ struct MlaState {
 // S^T (16 keys x 16 rows of row tile rt) of one page, FP8: 5 chunks of 128
 // dims (the last one half empty: dims 576..639 are zero in Q and skipped in K),
 // Q as the exact hi + lo pair.
-__device__ __forceinline__ floatx4_t mla_qk_f8(const unsigned char *stage, const unsigned char *qlds, int rt,
-                                               int lane)
+// Per-lane LDS byte offsets of one piece's page loop, so the loop adds only
+// immediates to them.  FP8: K operand rows k0 / k1 (the two 16-byte halves of
+// chunk 0 of lane (n, j); chunk c adds 128 c because the swizzle only touches
+// the low two slot bits), Q operands q (block (rt, c, part) adds
+// (2 c + part) 2048), V rows v (key row 4 j of lane (m, j); row 4 j + e and
+// pass h add 576 e + 256 h).  bf16: K slices of even / odd index k0 / k1
+// (slice s adds 64 s), Q q (slice s adds 1024 s), V rows v0 / v1 for keys
+// 4 j + e with e < 2 / e >= 2 (row and pass add 1152 e + 256 h).
+struct MlaLane {
+    uint32_t k0, k1, q, v0, v1;
+};
+
+template <int KVT>
+__device__ __forceinline__ MlaLane mla_lane(int rt, int lane)
 {
-    const int n = lane & 15, j = lane >> 4;
-    const int sw = MlaCfg<kKvFp8>::swz(n);
+    const int n = lane & 15, j = lane >> 4, m = lane & 15;
+    const int sw = MlaCfg<KVT>::swz(n);
+    MlaLane a;
+    if constexpr (KVT == kKvFp8) {
+        const int g = MlaCfg<kKvFp8>::swz(4 * j);          // = swz(4 j + e) for e = 0..3
+        a.k0 = (uint32_t)(kMlaDim * n + 16 * ((2 * j) ^ sw));
+        a.k1 = (uint32_t)(kMlaDim * n + 16 * ((2 * j + 1) ^ sw));
+        a.q = (uint32_t)(rt * 5 * 2 * 2048 + lane * 16);
+        a.v0 = (uint32_t)(kMlaDim * 4 * j + 16 * (m ^ g));
+        a.v1 = a.v0;
+    } else {
+        const int lo = (j ^ sw) & 3, hi = sw & 4;          // slot 4 s + j -> 4 s +- hi + lo
+        a.k0 = (uint32_t)(2 * kMlaDim * n + 16 * (hi + lo));
+        a.k1 = (uint32_t)(2 * kMlaDim * n + 16 * (lo - hi));
+        a.q = (uint32_t)(rt * 18 * 1024 + lane * 16);
+        a.v0 = (uint32_t)(2 * kMlaDim * 4 * j + 16 * (m ^ ((2 * j) & 7)));
+        a.v1 = (uint32_t)(2 * kMlaDim * 4 * j + 16 * (m ^ ((2 * j + 1) & 7)));
+    }
+    return a;
+}
+
+__device__ __forceinline__ floatx4_t mla_qk_f8(const unsigned char *stage, const unsigned char *qlds,
+                                               const MlaLane &ad, int lane)
+{
+    const int j = lane >> 4;
     floatx4_t Sp[2][2];                                // [chunk parity][hi, lo]: 4 independent chains
 #pragma unroll
     for (int a = 0; a < 2; ++a)
         Sp[a][0] = Sp[a][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 5; ++c) {
-        const int c0 = 8 * c + 2 * j;
-        uint4 a = *reinterpret_cast<const uint4 *>(stage + kMlaDim * n + 16 * (c0 ^ sw));
-        uint4 b = *reinterpret_cast<const uint4 *>(stage + kMlaDim * n + 16 * ((c0 + 1) ^ sw));
-        if (c == 4) {                                  // dims 576.. do not exist: lanes j >= 2
+        // chunk 4 of lanes j >= 2 would be dims 576..: they read chunk 4 of
+        // lane j - 2 (inside the row) and zero it
+        const uint32_t fix = c == 4 ? (uint32_t)((j >> 1) << 6) : 0u;
+        uint4 a = *reinterpret_cast<const uint4 *>(stage + ad.k0 - fix + 128 * c);
+        uint4 b = *reinterpret_cast<const uint4 *>(stage + ad.k1 - fix + 128 * c);
+        if (c == 4) {
             const uint32_t keep = (uint32_t)((j >> 1) - 1);    // all ones for j < 2, else 0
             a.x &= keep; a.y &= keep; a.z &= keep; a.w &= keep;
             b.x &= keep; b.y &= keep; b.z &= keep; b.w &= keep;
@@ -1596,8 +1637,8 @@ __device__ __forceinline__ floatx4_t mla_qk_f8(const unsigned char *stage, const
         const intx8_t kop = intx8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
-            const uint4 *qp = reinterpret_cast<const uint4 *>(qlds + ((size_t)((rt * 5 + c) * 2 + part) * 64 + lane) * 32);
-            const uint4 q0 = qp[0], q1 = qp[1];
+            const uint4 *qp = reinterpret_cast<const uint4 *>(qlds + ad.q + (2 * c + part) * 2048);
+            const uint4 q0 = qp[0], q1 = qp[64];
             const intx8_t qop = intx8_t{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w,
                                         (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
             Sp[c & 1][part] = mfma16_f8(kop, qop, Sp[c & 1][part]);
@@ -1608,19 +1649,17 @@ __device__ __forceinline__ floatx4_t mla_qk_f8(const unsigned char *stage, const
 }
 
 // The same for a bf16 cache: 18 slices of 32 dims on v_mfma_f32_16x16x32_bf16.
-__device__ __forceinline__ floatx4_t mla_qk_bf16(const unsigned char *stage, const unsigned char *qlds, int rt,
-                                                 int lane)
+__device__ __forceinline__ floatx4_t mla_qk_bf16(const unsigned char *stage, const unsigned char *qlds,
+                                                 const MlaLane &ad)
 {
-    const int n = lane & 15, j = lane >> 4;
-    const int sw = MlaCfg<kKvBf16>::swz(n);
     floatx4_t Sp[3];                                   // 3 independent chains
 #pragma unroll
     for (int a = 0; a < 3; ++a)
         Sp[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 18; ++s) {
-        const bf16x8_t kop = *reinterpret_cast<const bf16x8_t *>(stage + 2 * kMlaDim * n + 16 * ((4 * s + j) ^ sw));
-        const bf16x8_t qop = *reinterpret_cast<const bf16x8_t *>(qlds + ((size_t)(rt * 18 + s) * 64 + lane) * 16);
+        const bf16x8_t kop = *reinterpret_cast<const bf16x8_t *>(stage + ((s & 1) ? ad.k1 : ad.k0) + 64 * s);
+        const bf16x8_t qop = *reinterpret_cast<const bf16x8_t *>(qlds + ad.q + 1024 * s);
         Sp[s % 3] = mfma16(kop, qop, Sp[s % 3]);
     }
     return (Sp[0] + Sp[1]) + Sp[2];
@@ -1665,17 +1704,14 @@ __device__ __forceinline__ shortx4_t mla_softmax(MlaState &st, const floatx4_t &
 // tail (uniform): the page reaches the sequence's end; then the key rows
 // 4 j + e flagged in zmask (at or past the end) read as zero.
 __device__ __forceinline__ void mla_pv_f8(MlaState &st, const unsigned char *stage, const shortx4_t &pop,
-                                          bool tail, uint32_t zmask, int lane)
+                                          bool tail, uint32_t zmask, const MlaLane &ad)
 {
-    const int m = lane & 15, j = lane >> 4;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         uint4 w[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int n = 4 * j + e;                             // swz(n) = j
-            w[e] = *reinterpret_cast<const uint4 *>(stage + kMlaDim * n + 16 * ((16 * h + m) ^ j));
-        }
+        for (int e = 0; e < 4; ++e)
+            w[e] = *reinterpret_cast<const uint4 *>(stage + ad.v0 + kMlaDim * e + 256 * h);
         if (tail) {                                              // uniform: the sequence's last page
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1706,18 +1742,14 @@ __device__ __forceinline__ void mla_pv_f8(MlaState &st, const unsigned char *sta
 
 // The same for a bf16 cache: chunk 16 h + m (8 dims) of key rows 4 j .. 4 j + 3.
 __device__ __forceinline__ void mla_pv_bf16(MlaState &st, const unsigned char *stage, const shortx4_t &pop,
-                                            bool tail, uint32_t zmask, int lane)
+                                            bool tail, uint32_t zmask, const MlaLane &ad)
 {
-    const int m = lane & 15, j = lane >> 4;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
         uint4 w[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int n = 4 * j + e;
-            w[e] = *reinterpret_cast<const uint4 *>(stage + 2 * kMlaDim * n +
-                                                    16 * ((16 * h + m) ^ MlaCfg<kKvBf16>::swz(n)));
-        }
+        for (int e = 0; e < 4; ++e)
+            w[e] = *reinterpret_cast<const uint4 *>(stage + (e < 2 ? ad.v0 : ad.v1) + 2 * kMlaDim * e + 256 * h);
         if (tail) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1909,6 +1941,7 @@ void va_mla_split_kernel(SplitParams p)
             limit = min(ctx + (r >> p.log2g), lk - 1);
         }
 
+        const MlaLane ad = mla_lane<KVT>(rt, pl);          // the loop's LDS offsets: 5 registers
         for (int t = 0; t < nsteps; ++t) {
             const int k = kg + 2 * t;                      // page of the piece
             if (KVT == kKvFp8 && t == 0 && k + 2 < npg)
@@ -1919,9 +1952,9 @@ void va_mla_split_kernel(SplitParams p)
             if (t >= 1 && k + 2 < npg)
                 issue(k + 2, (t + 1) & 1);
             if (k < npg && rows_live) {
-                // lane-derived LDS addresses are rederived each step from an
+                // other lane-derived values are rederived each step from an
                 // opaque lane index: hoisted out of the loop they would hold
-                // some 30 registers next to the 128 accumulators
+                // registers next to the 128 accumulators
                 int ln = lane;
                 asm volatile("" : "+v"(ln));
                 const unsigned char *stage = ring + (t & 1) * kPageBytes;
@@ -1929,9 +1962,9 @@ void va_mla_split_kernel(SplitParams p)
                 const bool masked = key0 + 15 > ctx;
                 floatx4_t S;
                 if constexpr (KVT == kKvFp8)
-                    S = mla_qk_f8(stage, qlds, rt, ln);
+                    S = mla_qk_f8(stage, qlds, ad, ln);
                 else
-                    S = mla_qk_bf16(stage, qlds, rt, ln);
+                    S = mla_qk_bf16(stage, qlds, ad);
                 const shortx4_t pop = mla_softmax(st, S, limit, key0, crow, ln, masked);
                 const bool tail = key0 + 15 >= lk;                 // uniform
                 uint32_t zmask = 0;
@@ -1940,9 +1973,9 @@ void va_mla_split_kernel(SplitParams p)
                     if (key0 + 4 * (ln >> 4) + e >= lk)
                         zmask |= 1u << e;
                 if constexpr (KVT == kKvFp8)
-                    mla_pv_f8(st, stage, pop, tail, zmask, ln);
+                    mla_pv_f8(st, stage, pop, tail, zmask, ad);
                 else
-                    mla_pv_bf16(st, stage, pop, tail, zmask, ln);
+                    mla_pv_bf16(st, stage, pop, tail, zmask, ad);
             }
         }
         wait_vmcnt<0>();
