@@ -1531,11 +1531,13 @@ void va_split_kv_bf16_w8_kernel(SplitParams p)
 // 128 registers).  The two key groups merge in the epilogue.
 //
 // Ring rows: row n of a page sits at n * row bytes, its 16-byte chunk c at slot
-// c ^ swz(n), swz = ((n >> 2) ^ (n >> 3)) & 3 (FP8, 36 chunks a row) or
-// (n >> 1) & 7 (bf16, 72 chunks a row).  Both were chosen by measuring LDS bank
-// conflicts (SQ_LDS_BANK_CONFLICT) of the two read patterns on gfx950 (QK:
-// one chunk of 16 rows; PV: 16 chunks of one row): neither conflicts.  The
-// FP8 swizzle (n >> 2) & 3 costs a two-way conflict on the QK reads.  A page copy is 9 (FP8) or 18 (bf16) 1-KiB copies; wave (kg, rt)
+// c ^ swz(n), swz = ((n >> 2) ^ (n >> 3)) & 1 | ((n >> 2) & 1) << 1 (FP8, 36
+// chunks a row) or n & 7 (bf16, 72 chunks a row).  Both were chosen by
+// measuring LDS bank conflicts (SQ_LDS_BANK_CONFLICT) of the kernel's read
+// patterns on gfx950: QK reads one chunk of 16 rows, PV reads transposed
+// (mla_pv_f8, mla_pv_bf16); none of them conflicts.  (n >> 2) & 3 costs a
+// two-way conflict on the FP8 QK reads, ((n >> 2) ^ (n >> 3)) & 3 one on the
+// FP8 transposed reads, (n >> 1) & 7 one on the bf16 transposed reads.  A page copy is 9 (FP8) or 18 (bf16) 1-KiB copies; wave (kg, rt)
 // issues copies rt, rt + 4, ... of its key group's page.
 
 constexpr int kMlaDim = 576;                   // cache row and query row width
@@ -1550,7 +1552,7 @@ template <> struct MlaCfg<kKvFp8> {
     static constexpr int kCopies = 9;
     static constexpr int kMaxCopies = 3;                   // wave rt = 0; the others 2
     static constexpr int kQBytes = 4 * 5 * 2 * 64 * 32;     // [rt][c][hi, lo][half][lane] x 16 B
-    __device__ static int swz(int n) { return ((n >> 2) ^ (n >> 3)) & 3; }
+    __device__ static int swz(int n) { return (((n >> 2) ^ (n >> 3)) & 1) | (((n >> 2) & 1) << 1); }
 };
 template <> struct MlaCfg<kKvBf16> {
     static constexpr int kRowBytes = 2 * kMlaDim;
@@ -1558,7 +1560,7 @@ template <> struct MlaCfg<kKvBf16> {
     static constexpr int kCopies = 18;
     static constexpr int kMaxCopies = 5;                   // waves rt = 0, 1; the others 4
     static constexpr int kQBytes = 4 * 18 * 64 * 16;        // [rt][s][lane] x 16 B
-    __device__ static int swz(int n) { return (n >> 1) & 7; }
+    __device__ static int swz(int n) { return n & 7; }
 };
 
 template <int KVT>
@@ -1575,45 +1577,57 @@ struct MlaState {
     float l;             // the lane's partial sum of 2^(x - m)
 };
 
-// S^T (16 keys x 16 rows of row tile rt) of one page, FP8: 5 chunks of 128
-// dims (the last one half empty: dims 576..639 are zero in Q and skipped in K),
-// Q as the exact hi + lo pair.
 // Per-lane LDS byte offsets of one piece's page loop, so the loop adds only
 // immediates to them.  FP8: K operand rows k0 / k1 (the two 16-byte halves of
 // chunk 0 of lane (n, j); chunk c adds 128 c because the swizzle only touches
 // the low two slot bits), Q operands q (block (rt, c, part) adds
-// (2 c + part) 2048), V rows v (key row 4 j of lane (m, j); row 4 j + e and
-// pass h add 576 e + 256 h).  bf16: K slices of even / odd index k0 / k1
-// (slice s adds 64 s), Q q (slice s adds 1024 s), V rows v0 / v1 for keys
-// 4 j + e with e < 2 / e >= 2 (row and pass add 1152 e + 256 h).
+// (2 c + part) 2048), V reads v0 / v1 (transposed reads of even / odd index
+// p, see mla_pv_f8; read p adds 64 (p >> 1)).  bf16: K slices of even / odd
+// index k0 / k1 (slice s adds 64 s), Q q (slice s adds 1024 s), V reads
+// v0 .. v3 (transposed reads of tiles T with T % 4 = 0 .. 3, see mla_pv_bf16;
+// tile T adds 128 (T >> 2)).
 struct MlaLane {
-    uint32_t k0, k1, q, v0, v1;
+    uint32_t k0, k1, q, v0, v1, v2, v3;
 };
 
 template <int KVT>
 __device__ __forceinline__ MlaLane mla_lane(int rt, int lane)
 {
-    const int n = lane & 15, j = lane >> 4, m = lane & 15;
+    const int n = lane & 15, j = lane >> 4;
     const int sw = MlaCfg<KVT>::swz(n);
     MlaLane a;
     if constexpr (KVT == kKvFp8) {
-        const int g = MlaCfg<kKvFp8>::swz(4 * j);          // = swz(4 j + e) for e = 0..3
         a.k0 = (uint32_t)(kMlaDim * n + 16 * ((2 * j) ^ sw));
         a.k1 = (uint32_t)(kMlaDim * n + 16 * ((2 * j + 1) ^ sw));
         a.q = (uint32_t)(rt * 5 * 2 * 2048 + lane * 16);
-        a.v0 = (uint32_t)(kMlaDim * 4 * j + 16 * (m ^ g));
-        a.v1 = a.v0;
+        // transposed V reads (see mla_pv_f8): lane l addresses key row
+        // 4 (l >> 4) + ((l >> 1) & 3), tile 2 p + ((l >> 3) & 1), half l & 1
+        const int tn = 4 * j + ((lane >> 1) & 3), ts = (lane >> 3) & 1, th = lane & 1;
+        const int tw = MlaCfg<kKvFp8>::swz(tn);
+        a.v0 = (uint32_t)(kMlaDim * tn + 16 * (ts ^ tw) + 8 * th);          // even p
+        a.v1 = (uint32_t)(kMlaDim * tn + 16 * ((2 + ts) ^ tw) + 8 * th);    // odd p
+        a.v2 = a.v3 = 0;
     } else {
         const int lo = (j ^ sw) & 3, hi = sw & 4;          // slot 4 s + j -> 4 s +- hi + lo
         a.k0 = (uint32_t)(2 * kMlaDim * n + 16 * (hi + lo));
         a.k1 = (uint32_t)(2 * kMlaDim * n + 16 * (lo - hi));
         a.q = (uint32_t)(rt * 18 * 1024 + lane * 16);
-        a.v0 = (uint32_t)(2 * kMlaDim * 4 * j + 16 * (m ^ ((2 * j) & 7)));
-        a.v1 = (uint32_t)(2 * kMlaDim * 4 * j + 16 * (m ^ ((2 * j + 1) & 7)));
+        // transposed V reads (see mla_pv_bf16): lane l addresses key row
+        // 4 (l >> 4) + ((l >> 2) & 3), dims 16 T + 4 (l & 3) .. + 3
+        const int tn = 4 * j + ((lane >> 2) & 3), ta = lane & 3;
+        const int tw = MlaCfg<kKvBf16>::swz(tn);
+        const uint32_t row = (uint32_t)(2 * kMlaDim * tn + 8 * (ta & 1));
+        a.v0 = row + 16 * ((0 + (ta >> 1)) ^ tw);                         // T % 4 = 0
+        a.v1 = row + 16 * ((2 + (ta >> 1)) ^ tw);                         // T % 4 = 1
+        a.v2 = row + 16 * ((4 + (ta >> 1)) ^ tw);                         // T % 4 = 2
+        a.v3 = row + 16 * ((6 + (ta >> 1)) ^ tw);                         // T % 4 = 3
     }
     return a;
 }
 
+// S^T (16 keys x 16 rows of row tile rt) of one page, FP8: 5 chunks of 128
+// dims (the last one half empty: dims 576..639 are zero in Q and skipped in K),
+// Q as the exact hi + lo pair.
 __device__ __forceinline__ floatx4_t mla_qk_f8(const unsigned char *stage, const unsigned char *qlds,
                                                const MlaLane &ad, int lane)
 {
@@ -1698,73 +1712,81 @@ __device__ __forceinline__ shortx4_t mla_softmax(MlaState &st, const floatx4_t &
     return __builtin_bit_cast(shortx4_t, make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])));
 }
 
-// O^T += V^T P^T over the latent of one page, FP8: lane (m, j) reads chunk
-// 16 h + m (16 dims) of key rows 4 j .. 4 j + 3, transposes the 4 x 16 bytes in
-// registers and converts them exactly to bf16 (K = 16 keys per MFMA).
-// tail (uniform): the page reaches the sequence's end; then the key rows
-// 4 j + e flagged in zmask (at or past the end) read as zero.
+// LDS transposed read (ds_read_b64_tr_b8).  Measured lane rule on gfx950:
+// within each group of 16 lanes, output lane 16 g + 8 h + b receives as its
+// byte i byte b of the 8 bytes addressed by input lane 16 g + 2 i + h.
+__device__ __forceinline__ uint2 lds_read_tr8(const unsigned char *p)
+{
+    typedef int v2i_t __attribute__((ext_vector_type(2)));
+    const v2i_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i_t *)p);
+    return make_uint2((uint32_t)r.x, (uint32_t)r.y);
+}
+
+// O^T += V^T P^T over the latent of one page, FP8.  Read p (0..15) is one
+// transposed read: input lane l addresses the 8 dims 16 T + 8 (l & 1) .. + 7 of
+// key row 4 (l >> 4) + ((l >> 1) & 3), with T = 2 p + ((l >> 3) & 1).  Output
+// lane (n, j) then holds dim 16 T + n of keys 4 j .. 4 j + 3 for T = 2 p (bytes
+// 0..3) and T = 2 p + 1 (bytes 4..7): the A operands of tiles 2 p and 2 p + 1,
+// converted exactly to bf16 (K = 16 keys per MFMA), with no byte shuffles.
+// tail (uniform): the page reaches the sequence's end; then the keys 4 j + e
+// flagged in zmask (at or past the end, poisoned) read as zero.
 __device__ __forceinline__ void mla_pv_f8(MlaState &st, const unsigned char *stage, const shortx4_t &pop,
                                           bool tail, uint32_t zmask, const MlaLane &ad)
 {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint4 w[4];
+    // Byte mask of the lane's four keys 4 (l >> 4) + e: ones for a live key.
+    uint32_t km = 0xFFFFFFFFu;
+    if (tail) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            w[e] = *reinterpret_cast<const uint4 *>(stage + ad.v0 + kMlaDim * e + 256 * h);
-        if (tail) {                                              // uniform: the sequence's last page
+            if (zmask & (1u << e))
+                km &= ~(0xFFu << (8 * e));
+    }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t keep = ((zmask >> e) & 1u) - 1u;    // 0 for a zeroed row
-                w[e].x &= keep; w[e].y &= keep; w[e].z &= keep; w[e].w &= keep;
-            }
-        }
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint32_t w0 = u4get(w[0], d), w1 = u4get(w[1], d), w2 = u4get(w[2], d), w3 = u4get(w[3], d);
-            const uint32_t a = byte_perm(w1, w0, 0x05010400u);   // w0.0 w1.0 w0.1 w1.1
-            const uint32_t b = byte_perm(w1, w0, 0x07030602u);   // w0.2 w1.2 w0.3 w1.3
-            const uint32_t cc = byte_perm(w3, w2, 0x05010400u);
-            const uint32_t dd = byte_perm(w3, w2, 0x07030602u);
-            const uint32_t tr[4] = {byte_perm(cc, a, 0x05040100u), byte_perm(cc, a, 0x07060302u),
-                                    byte_perm(dd, b, 0x05040100u), byte_perm(dd, b, 0x07060302u)};
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {                        // dim 4 d + x of the chunk, keys 0..3
-                const shortx4_t av = __builtin_bit_cast(
-                    shortx4_t, make_uint2(fp8x2_lo_to_bf16x2(tr[x]), fp8x2_hi_to_bf16x2(tr[x])));
-                const int T = 16 * h + 4 * d + x;
-                st.o[T] = mfma16k16(av, pop, st.o[T]);
-            }
-        }
-        asm volatile("" ::: "memory");                 // one pass's rows live at a time
+    for (int p = 0; p < 16; ++p) {
+        uint2 r = lds_read_tr8(stage + ((p & 1) ? ad.v1 : ad.v0) + 64 * (p >> 1));
+        r.x &= km;
+        r.y &= km;
+        const shortx4_t a0 = __builtin_bit_cast(shortx4_t, make_uint2(fp8x2_lo_to_bf16x2(r.x), fp8x2_hi_to_bf16x2(r.x)));
+        const shortx4_t a1 = __builtin_bit_cast(shortx4_t, make_uint2(fp8x2_lo_to_bf16x2(r.y), fp8x2_hi_to_bf16x2(r.y)));
+        st.o[2 * p] = mfma16k16(a0, pop, st.o[2 * p]);
+        st.o[2 * p + 1] = mfma16k16(a1, pop, st.o[2 * p + 1]);
     }
 }
 
-// The same for a bf16 cache: chunk 16 h + m (8 dims) of key rows 4 j .. 4 j + 3.
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char *p)
+{
+    typedef short v4s_t __attribute__((ext_vector_type(4)));
+    const v4s_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t *)p);
+    return __builtin_bit_cast(uint2, r);
+}
+
+// The same for a bf16 cache, with ds_read_b64_tr_b16 (measured lane rule:
+// within each group of 16 lanes, output lane 16 g + 4 a + b receives as its
+// element i element b of the 4 addressed by input lane 16 g + 4 i + a).
+// Input lane l addresses dims 16 T + 4 (l & 3) .. + 3 of key row
+// 4 (l >> 4) + ((l >> 2) & 3), so output lane (n, j) holds dim 16 T + n of
+// keys 4 j .. 4 j + 3: the A operand of tile T as read, one read per tile.
 __device__ __forceinline__ void mla_pv_bf16(MlaState &st, const unsigned char *stage, const shortx4_t &pop,
                                             bool tail, uint32_t zmask, const MlaLane &ad)
 {
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        uint4 w[4];
+    uint32_t km0 = 0xFFFFFFFFu, km1 = 0xFFFFFFFFu;         // 16-bit masks of keys 4 j + e
+    if (tail) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            w[e] = *reinterpret_cast<const uint4 *>(stage + (e < 2 ? ad.v0 : ad.v1) + 2 * kMlaDim * e + 256 * h);
-        if (tail) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t keep = ((zmask >> e) & 1u) - 1u;
-                w[e].x &= keep; w[e].y &= keep; w[e].z &= keep; w[e].w &= keep;
+            if (zmask & (1u << e)) {
+                if (e < 2)
+                    km0 &= ~(0xFFFFu << (16 * e));
+                else
+                    km1 &= ~(0xFFFFu << (16 * (e - 2)));
             }
-        }
+    }
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
-            const uint32_t w01 = byte_perm(u4get(w[1], x >> 1), u4get(w[0], x >> 1), sel);
-            const uint32_t w23 = byte_perm(u4get(w[3], x >> 1), u4get(w[2], x >> 1), sel);
-            const int T = 8 * h + x;
-            st.o[T] = mfma16k16(__builtin_bit_cast(shortx4_t, make_uint2(w01, w23)), pop, st.o[T]);
-        }
+    for (int T = 0; T < 32; ++T) {
+        const uint32_t b = (T & 3) == 0 ? ad.v0 : (T & 3) == 1 ? ad.v1 : (T & 3) == 2 ? ad.v2 : ad.v3;
+        uint2 r = lds_read_tr16(stage + b + 128 * (T >> 2));
+        r.x &= km0;
+        r.y &= km1;
+        st.o[T] = mfma16k16(__builtin_bit_cast(shortx4_t, r), pop, st.o[T]);
     }
 }
 
@@ -1995,31 +2017,22 @@ void va_mla_split_kernel(SplitParams p)
             }
             const float inv = st.l > 0.f ? 1.0f / st.l : 0.f;
             unsigned char *orow = obuf + (size_t)(kg * kMlaRows + row) * 1024;
-            if constexpr (KVT == kKvFp8) {                 // 16-dim chunks 16 h + 4 j + i
+            if constexpr (KVT == kKvFp8) {                 // tile T: dims 16 T + 4 j .. + 3
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                for (int T = 0; T < 32; ++T) {
+                    const int u = 2 * T + (j >> 1);             // 8-dim unit of the row
+                    *reinterpret_cast<uint2 *>(orow + 16 * (u ^ n) + 8 * (j & 1)) =
+                        make_uint2(pack_f16x2(st.o[T][0] * inv, st.o[T][1] * inv),
+                                   pack_f16x2(st.o[T][2] * inv, st.o[T][3] * inv));
+                }
+            } else {                                       // the same mapping, bf16 units
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int q = 16 * h + 4 * j + i;
-                        uint32_t v[8];
-#pragma unroll
-                        for (int x = 0; x < 8; ++x)
-                            v[x] = pack_f16x2(st.o[16 * h + 2 * x][i] * inv, st.o[16 * h + 2 * x + 1][i] * inv);
-                        *reinterpret_cast<uint4 *>(orow + 16 * ((2 * q) ^ n)) = make_uint4(v[0], v[1], v[2], v[3]);
-                        *reinterpret_cast<uint4 *>(orow + 16 * ((2 * q + 1) ^ n)) = make_uint4(v[4], v[5], v[6], v[7]);
-                    }
-            } else {                                       // 8-dim chunks 16 h + 4 j + i
-#pragma unroll
-                for (int h = 0; h < 4; ++h)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int q = 16 * h + 4 * j + i;
-                        uint32_t v[4];
-#pragma unroll
-                        for (int x = 0; x < 4; ++x)
-                            v[x] = pack_bf16x2(st.o[8 * h + 2 * x][i] * inv, st.o[8 * h + 2 * x + 1][i] * inv);
-                        *reinterpret_cast<uint4 *>(orow + 16 * (q ^ n)) = make_uint4(v[0], v[1], v[2], v[3]);
-                    }
+                for (int T = 0; T < 32; ++T) {
+                    const int u = 2 * T + (j >> 1);
+                    *reinterpret_cast<uint2 *>(orow + 16 * (u ^ n) + 8 * (j & 1)) =
+                        make_uint2(pack_bf16x2(st.o[T][0] * inv, st.o[T][1] * inv),
+                                   pack_bf16x2(st.o[T][2] * inv, st.o[T][3] * inv));
+                }
             }
         }
         __syncthreads();
