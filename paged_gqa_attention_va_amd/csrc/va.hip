@@ -1639,15 +1639,12 @@ __device__ __forceinline__ floatx4_t mla_qk_f8(const unsigned char *stage, const
 #pragma unroll
     for (int c = 0; c < 5; ++c) {
         // chunk 4 of lanes j >= 2 would be dims 576..: they read chunk 4 of
-        // lane j - 2 (inside the row) and zero it
+        // lane j - 2 (inside the row).  Their Q operand is zero, so a key
+        // adds nothing there unless its row holds a NaN, and then the lanes
+        // j - 2 that own those dims make the same logit NaN anyway.
         const uint32_t fix = c == 4 ? (uint32_t)((j >> 1) << 6) : 0u;
-        uint4 a = *reinterpret_cast<const uint4 *>(stage + ad.k0 - fix + 128 * c);
-        uint4 b = *reinterpret_cast<const uint4 *>(stage + ad.k1 - fix + 128 * c);
-        if (c == 4) {
-            const uint32_t keep = (uint32_t)((j >> 1) - 1);    // all ones for j < 2, else 0
-            a.x &= keep; a.y &= keep; a.z &= keep; a.w &= keep;
-            b.x &= keep; b.y &= keep; b.z &= keep; b.w &= keep;
-        }
+        const uint4 a = *reinterpret_cast<const uint4 *>(stage + ad.k0 - fix + 128 * c);
+        const uint4 b = *reinterpret_cast<const uint4 *>(stage + ad.k1 - fix + 128 * c);
         const intx8_t kop = intx8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
