@@ -107,9 +107,10 @@ typedef struct {
     int32_t q_dtype;             /* va_dtype; must be VA_DT_BF16 (out is bf16 too) */
     int32_t kv_dtype;            /* va_dtype of both pools */
     int32_t num_cus;             /* compute units to plan for; 0 = query the current device */
-    int32_t force_grid;          /* 0 = automatic; > 0 = number of split-KV workgroups
-                                    (a testing hook: every value gives the same result
-                                    up to floating-point merge order) */
+    int32_t force_grid;          /* 0 = automatic; 1 .. 65536 = number of split-KV
+                                    workgroups (a testing hook: every value gives the same
+                                    result up to floating-point merge order; larger values
+                                    are VA_ERR_INVALID_ARG) */
     int32_t window_left;         /* sliding window: -1 = none; >= 0: the query at absolute
                                     position i also needs key j >= i - window_left (the
                                     window_size = (sliding_window - 1, 0) of the PR #30105

@@ -2421,7 +2421,7 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     if (p.num_seqs < 1 || p.num_q_heads < 1 || p.num_kv_heads < 1 || p.head_dim < 1 ||
         p.page_size < 1 || p.max_seqlen_q < 1 || p.max_seqlen_k < 0 ||
         (p.layout == VA_LAYOUT_PAGED && p.max_blocks_per_seq < 1) ||
-        p.num_blocks < 1 || p.total_q < 0 || p.num_cus < 0 || p.force_grid < 0)
+        p.num_blocks < 1 || p.total_q < 0 || p.num_cus < 0 || p.force_grid < 0 || p.force_grid > 65536)
         return VA_ERR_INVALID_ARG;
     if (p.total_q > (int64_t)p.num_seqs * p.max_seqlen_q)
         return VA_ERR_INVALID_ARG;

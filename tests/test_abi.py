@@ -60,6 +60,8 @@ def test_plan_accepts_the_workloads():
     (dict(num_blocks=0), va.VA_ERR_INVALID_ARG),
     (dict(max_seqlen_k=32769), va.VA_ERR_INVALID_ARG),
     (dict(num_cus=-1), va.VA_ERR_INVALID_ARG),
+    (dict(force_grid=-1), va.VA_ERR_INVALID_ARG),
+    (dict(force_grid=65537), va.VA_ERR_INVALID_ARG),
 ])
 def test_plan_rejects(kw, status):
     with pytest.raises(va.VaError) as e:
