@@ -107,6 +107,14 @@ def _check(status: int, where: str) -> None:
         raise VaError(status, where)
 
 
+def _same_device(device, *tensors) -> None:
+    """Every tensor must live on ``device``: the kernels are launched there and
+    dereference the pointers as that device's memory."""
+    for t in tensors:
+        if t is not None and t.device != device:
+            raise ValueError(f"all tensors must be on {device}, got one on {t.device}")
+
+
 def _dtype_code(name: str) -> int:
     if name in ("fp8", "fp8_e4m3fn", "float8_e4m3fn"):
         return VA_DT_FP8_E4M3FN
@@ -213,6 +221,8 @@ class Plan:
             workspace = self.workspace(q.device)
         if out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous():
             raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+        _same_device(q.device, k_buffer, v_buffer, kv_indptr, kv_indices, k_extend, v_extend, cu_seqlens_q,
+                     k_descale, v_descale, sinks, out, workspace)
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -251,6 +261,8 @@ class Plan:
             raise ValueError(f"out must be a contiguous bf16 tensor of shape {oshape}")
         if workspace.numel() * workspace.element_size() < self.workspace_bytes:
             raise ValueError("workspace smaller than plan.workspace_bytes")
+        _same_device(q.device, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k, k_descale, v_descale,
+                     sinks, out, workspace)
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -278,6 +290,7 @@ class Plan:
             result = torch.empty(2, dtype=torch.int32, device=block_table.device)
         if result.dtype != torch.int32 or result.numel() < 2 or not result.is_contiguous():
             raise ValueError("result must be a contiguous int32 tensor with 2 elements")
+        _same_device(block_table.device, cu_seqlens_q, seqused_k, result)
         if stream is None:
             stream = torch.cuda.current_stream(block_table.device)
         sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -343,6 +356,7 @@ def spec_block_table(kv_indptr, kv_indices, max_blocks_per_seq: int, page_size: 
     for t in (kv_indptr, kv_indices):
         if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("kv_indptr and kv_indices must be contiguous int32 device tensors")
+    _same_device(kv_indptr.device, kv_indices)
     bt = torch.empty((B, max_blocks_per_seq), dtype=torch.int32, device=kv_indptr.device)
     sk = torch.empty((B,), dtype=torch.int32, device=kv_indptr.device)
     if stream is None:

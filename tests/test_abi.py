@@ -153,3 +153,10 @@ def test_workspace_is_bounded_by_the_grid_not_the_pairs():
     # two partial slots per workgroup, plus the page prefix over the pairs
     assert big.workspace_bytes < small.workspace_bytes + 65537 * 4 + 4096
     assert big.workspace_bytes < 16 << 20
+
+
+def test_binding_rejects_tensors_on_another_device():
+    import torch
+    va._same_device(torch.device("cpu"), torch.zeros(1), None)
+    with pytest.raises(ValueError):
+        va._same_device(torch.device("cpu"), torch.zeros(1), torch.empty(1, device="meta"))
