@@ -1551,6 +1551,7 @@ template <> struct MlaCfg<kKvFp8> {
     static constexpr int kChunks = 36;
     static constexpr int kCopies = 9;
     static constexpr int kMaxCopies = 3;                   // wave rt = 0; the others 2
+    static constexpr int kPages = 2;                       // pages per key-group step
     static constexpr int kQBytes = 4 * 5 * 2 * 64 * 32;     // [rt][c][hi, lo][half][lane] x 16 B
     __device__ static int swz(int n) { return (((n >> 2) ^ (n >> 3)) & 1) | (((n >> 2) & 1) << 1); }
 };
@@ -1559,6 +1560,7 @@ template <> struct MlaCfg<kKvBf16> {
     static constexpr int kChunks = 72;
     static constexpr int kCopies = 18;
     static constexpr int kMaxCopies = 5;                   // waves rt = 0, 1; the others 4
+    static constexpr int kPages = 1;
     static constexpr int kQBytes = 4 * 18 * 64 * 16;        // [rt][s][lane] x 16 B
     __device__ static int swz(int n) { return n & 7; }
 };
@@ -1566,8 +1568,8 @@ template <> struct MlaCfg<kKvBf16> {
 template <int KVT>
 constexpr int mla_lds_bytes()
 {
-    return (MlaCfg<KVT>::kQBytes + 4 * 16 * MlaCfg<KVT>::kRowBytes) > (kMlaObufBytes + 1024)
-               ? (MlaCfg<KVT>::kQBytes + 4 * 16 * MlaCfg<KVT>::kRowBytes)
+    return (MlaCfg<KVT>::kQBytes + 4 * MlaCfg<KVT>::kPages * 16 * MlaCfg<KVT>::kRowBytes) > (kMlaObufBytes + 1024)
+               ? (MlaCfg<KVT>::kQBytes + 4 * MlaCfg<KVT>::kPages * 16 * MlaCfg<KVT>::kRowBytes)
                : (kMlaObufBytes + 1024);
 }
 
@@ -1587,7 +1589,7 @@ struct MlaState {
 // v0 .. v3 (transposed reads of tiles T with T % 4 = 0 .. 3, see mla_pv_bf16;
 // tile T adds 128 (T >> 2)).
 struct MlaLane {
-    uint32_t k0, k1, q, v0, v1, v2, v3;
+    uint32_t k0, k1, k0b, k1b, q, v0, v1, v2, v3;
 };
 
 template <int KVT>
@@ -1597,20 +1599,27 @@ __device__ __forceinline__ MlaLane mla_lane(int rt, int lane)
     const int sw = MlaCfg<KVT>::swz(n);
     MlaLane a;
     if constexpr (KVT == kKvFp8) {
+        // the second page of a step is stored with the swizzle swz(n) ^ 2
         a.k0 = (uint32_t)(kMlaDim * n + 16 * ((2 * j) ^ sw));
         a.k1 = (uint32_t)(kMlaDim * n + 16 * ((2 * j + 1) ^ sw));
+        a.k0b = (uint32_t)(kMlaDim * n + 16 * ((2 * j) ^ sw ^ 2));
+        a.k1b = (uint32_t)(kMlaDim * n + 16 * ((2 * j + 1) ^ sw ^ 2));
         a.q = (uint32_t)(rt * 5 * 2 * 2048 + lane * 16);
         // transposed V reads (see mla_pv_f8): lane l addresses key row
-        // 4 (l >> 4) + ((l >> 1) & 3), tile 2 p + ((l >> 3) & 1), half l & 1
-        const int tn = 4 * j + ((lane >> 1) & 3), ts = (lane >> 3) & 1, th = lane & 1;
-        const int tw = MlaCfg<kKvFp8>::swz(tn);
-        a.v0 = (uint32_t)(kMlaDim * tn + 16 * (ts ^ tw) + 8 * th);          // even p
-        a.v1 = (uint32_t)(kMlaDim * tn + 16 * ((2 + ts) ^ tw) + 8 * th);    // odd p
-        a.v2 = a.v3 = 0;
+        // 4 (l >> 4) + ((l >> 1) & 3) of page (l >> 3) & 1 of the step, dims
+        // 16 T + 8 (l & 1) .. + 7
+        const int tn = 4 * j + ((lane >> 1) & 3), tp = (lane >> 3) & 1, th = lane & 1;
+        const int tw = MlaCfg<kKvFp8>::swz(tn) ^ (2 * tp);
+        const uint32_t row = (uint32_t)(tp * 16 * kMlaDim + kMlaDim * tn + 8 * th);
+        a.v0 = row + 16 * (0 ^ tw);                                          // T % 4 = 0
+        a.v1 = row + 16 * (1 ^ tw);
+        a.v2 = row + 16 * (2 ^ tw);
+        a.v3 = row + 16 * (3 ^ tw);
     } else {
         const int lo = (j ^ sw) & 3, hi = sw & 4;          // slot 4 s + j -> 4 s +- hi + lo
         a.k0 = (uint32_t)(2 * kMlaDim * n + 16 * (hi + lo));
         a.k1 = (uint32_t)(2 * kMlaDim * n + 16 * (lo - hi));
+        a.k0b = a.k1b = 0;
         a.q = (uint32_t)(rt * 18 * 1024 + lane * 16);
         // transposed V reads (see mla_pv_bf16): lane l addresses key row
         // 4 (l >> 4) + ((l >> 2) & 3), dims 16 T + 4 (l & 3) .. + 3
@@ -1625,14 +1634,15 @@ __device__ __forceinline__ MlaLane mla_lane(int rt, int lane)
     return a;
 }
 
-// S^T (16 keys x 16 rows of row tile rt) of one page, FP8: 5 chunks of 128
-// dims (the last one half empty: dims 576..639 are zero in Q and skipped in K),
-// Q as the exact hi + lo pair.
-__device__ __forceinline__ floatx4_t mla_qk_f8(const unsigned char *stage, const unsigned char *qlds,
-                                               const MlaLane &ad, int lane)
+// S^T (16 keys x 16 rows of row tile rt) of the two pages of a step, FP8: 5
+// chunks of 128 dims (the last one half empty: dims 576..639 are zero in Q),
+// Q as the exact hi + lo pair, each Q operand read once for both pages.
+__device__ __forceinline__ void mla_qk_f8(floatx4_t (&S)[2], const unsigned char *stage, const unsigned char *qlds,
+                                          const MlaLane &ad, int lane)
 {
+    constexpr int kPageBytes = 16 * kMlaDim;
     const int j = lane >> 4;
-    floatx4_t Sp[2][2];                                // [chunk parity][hi, lo]: 4 independent chains
+    floatx4_t Sp[2][2];                                // [page][hi, lo]: 4 independent chains
 #pragma unroll
     for (int a = 0; a < 2; ++a)
         Sp[a][0] = Sp[a][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -1643,20 +1653,27 @@ __device__ __forceinline__ floatx4_t mla_qk_f8(const unsigned char *stage, const
         // adds nothing there unless its row holds a NaN, and then the lanes
         // j - 2 that own those dims make the same logit NaN anyway.
         const uint32_t fix = c == 4 ? (uint32_t)((j >> 1) << 6) : 0u;
-        const uint4 a = *reinterpret_cast<const uint4 *>(stage + ad.k0 - fix + 128 * c);
-        const uint4 b = *reinterpret_cast<const uint4 *>(stage + ad.k1 - fix + 128 * c);
-        const intx8_t kop = intx8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+        intx8_t kop[2];
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg) {
+            const unsigned char *base = stage + pg * kPageBytes - fix + 128 * c;
+            const uint4 a = *reinterpret_cast<const uint4 *>(base + (pg ? ad.k0b : ad.k0));
+            const uint4 b = *reinterpret_cast<const uint4 *>(base + (pg ? ad.k1b : ad.k1));
+            kop[pg] = intx8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+        }
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
             const uint4 *qp = reinterpret_cast<const uint4 *>(qlds + ad.q + (2 * c + part) * 2048);
             const uint4 q0 = qp[0], q1 = qp[64];
             const intx8_t qop = intx8_t{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w,
                                         (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
-            Sp[c & 1][part] = mfma16_f8(kop, qop, Sp[c & 1][part]);
+            Sp[0][part] = mfma16_f8(kop[0], qop, Sp[0][part]);
+            Sp[1][part] = mfma16_f8(kop[1], qop, Sp[1][part]);
         }
         asm volatile("" ::: "memory");                 // one chunk's operands live at a time
     }
-    return (Sp[0][0] + Sp[1][0]) + (Sp[0][1] + Sp[1][1]);
+    S[0] = Sp[0][0] + Sp[0][1];
+    S[1] = Sp[1][0] + Sp[1][1];
 }
 
 // The same for a bf16 cache: 18 slices of 32 dims on v_mfma_f32_16x16x32_bf16.
@@ -1709,6 +1726,53 @@ __device__ __forceinline__ shortx4_t mla_softmax(MlaState &st, const floatx4_t &
     return __builtin_bit_cast(shortx4_t, make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])));
 }
 
+// Online softmax of the two pages of an FP8 step (lane: row l%16, keys
+// key0 + 4 (l/16) + e of page 0 and key0 + 16 + 4 (l/16) + e of page 1; the
+// second page is absent when !hasb).  Returns the B operand of the 32-key PV
+// MFMA: K position 8 j + e is key 4 j + e of page 0, 8 j + 4 + e the same key
+// of page 1 (the V operands use the same order).
+__device__ __forceinline__ bf16x8_t mla_softmax2(MlaState &st, const floatx4_t (&S)[2], int limit, int key0,
+                                                 float c, int lane, bool masked, bool hasb)
+{
+    const int j = lane >> 4;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[e] = S[0][e] * c;
+        x[4 + e] = S[1][e] * c;
+    }
+    if (masked) {                                      // uniform
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = key0 + 4 * j + e > limit ? -INFINITY : x[e];
+            x[4 + e] = (!hasb || key0 + 16 + 4 * j + e > limit) ? -INFINITY : x[4 + e];
+        }
+    }
+    float lmax = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e)
+        lmax = fmaxf(lmax, x[e]);
+    if (__any(lmax > st.m + kTau)) {
+        float t = fmaxf(lmax, __shfl_xor(lmax, 16));
+        t = fmaxf(t, __shfl_xor(t, 32));
+        const bool need = t > st.m + kTau;
+        const float alpha = need ? exp2_fast(st.m - t) : 1.0f;
+        st.m = need ? t : st.m;
+        st.l *= alpha;
+#pragma unroll
+        for (int T = 0; T < 32; ++T)
+            st.o[T] *= alpha;
+    }
+    const float mref = st.m == -INFINITY ? 0.0f : st.m;
+    float pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        pv[e] = exp2_fast(x[e] - mref);
+    st.l += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+    return __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                                   pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])));
+}
+
 // LDS transposed read (ds_read_b64_tr_b8).  Measured lane rule on gfx950:
 // within each group of 16 lanes, output lane 16 g + 8 h + b receives as its
 // byte i byte b of the 8 bytes addressed by input lane 16 g + 2 i + h.
@@ -1719,34 +1783,26 @@ __device__ __forceinline__ uint2 lds_read_tr8(const unsigned char *p)
     return make_uint2((uint32_t)r.x, (uint32_t)r.y);
 }
 
-// O^T += V^T P^T over the latent of one page, FP8.  Read p (0..15) is one
-// transposed read: input lane l addresses the 8 dims 16 T + 8 (l & 1) .. + 7 of
-// key row 4 (l >> 4) + ((l >> 1) & 3), with T = 2 p + ((l >> 3) & 1).  Output
-// lane (n, j) then holds dim 16 T + n of keys 4 j .. 4 j + 3 for T = 2 p (bytes
-// 0..3) and T = 2 p + 1 (bytes 4..7): the A operands of tiles 2 p and 2 p + 1,
-// converted exactly to bf16 (K = 16 keys per MFMA), with no byte shuffles.
-// tail (uniform): the page reaches the sequence's end; then the keys 4 j + e
-// flagged in zmask (at or past the end, poisoned) read as zero.
-__device__ __forceinline__ void mla_pv_f8(MlaState &st, const unsigned char *stage, const shortx4_t &pop,
-                                          bool tail, uint32_t zmask, const MlaLane &ad)
+// O^T += V^T P^T over the latent of the two pages of an FP8 step, on the
+// 32-key bf16 MFMA.  Read T (0..31) is one transposed read: input lane l
+// addresses the 8 dims 16 T + 8 (l & 1) .. + 7 of key row 4 (l >> 4) +
+// ((l >> 1) & 3) of page (l >> 3) & 1.  Output lane (n, j) then holds dim
+// 16 T + n of keys 4 j .. 4 j + 3 of page 0 (bytes 0..3) and page 1 (bytes
+// 4..7): the A operand of tile T in the K order of mla_softmax2, converted
+// exactly to bf16, with no byte shuffles.
+// Key rows at or past the end of the sequence or of the piece (poisoned or
+// stale) have been zeroed in the stage (mla_zero_rows), so their zero weights
+// meet zero values.
+__device__ __forceinline__ void mla_pv_f8(MlaState &st, const unsigned char *stage, const bf16x8_t &pop,
+                                          const MlaLane &ad)
 {
-    // Byte mask of the lane's four keys 4 (l >> 4) + e: ones for a live key.
-    uint32_t km = 0xFFFFFFFFu;
-    if (tail) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (zmask & (1u << e))
-                km &= ~(0xFFu << (8 * e));
-    }
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-        uint2 r = lds_read_tr8(stage + ((p & 1) ? ad.v1 : ad.v0) + 64 * (p >> 1));
-        r.x &= km;
-        r.y &= km;
-        const shortx4_t a0 = __builtin_bit_cast(shortx4_t, make_uint2(fp8x2_lo_to_bf16x2(r.x), fp8x2_hi_to_bf16x2(r.x)));
-        const shortx4_t a1 = __builtin_bit_cast(shortx4_t, make_uint2(fp8x2_lo_to_bf16x2(r.y), fp8x2_hi_to_bf16x2(r.y)));
-        st.o[2 * p] = mfma16k16(a0, pop, st.o[2 * p]);
-        st.o[2 * p + 1] = mfma16k16(a1, pop, st.o[2 * p + 1]);
+    for (int T = 0; T < 32; ++T) {
+        const uint32_t b = (T & 3) == 0 ? ad.v0 : (T & 3) == 1 ? ad.v1 : (T & 3) == 2 ? ad.v2 : ad.v3;
+        const uint2 r = lds_read_tr8(stage + b + 64 * (T >> 2));
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(fp8x2_lo_to_bf16x2(r.x), fp8x2_hi_to_bf16x2(r.x),
+                                                                  fp8x2_lo_to_bf16x2(r.y), fp8x2_hi_to_bf16x2(r.y)));
+        st.o[T] = mfma16(a, pop, st.o[T]);
     }
 }
 
@@ -1763,27 +1819,31 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char *p)
 // Input lane l addresses dims 16 T + 4 (l & 3) .. + 3 of key row
 // 4 (l >> 4) + ((l >> 2) & 3), so output lane (n, j) holds dim 16 T + n of
 // keys 4 j .. 4 j + 3: the A operand of tile T as read, one read per tile.
+// Key rows past the end have been zeroed in the stage, as for FP8.
 __device__ __forceinline__ void mla_pv_bf16(MlaState &st, const unsigned char *stage, const shortx4_t &pop,
-                                            bool tail, uint32_t zmask, const MlaLane &ad)
+                                            const MlaLane &ad)
 {
-    uint32_t km0 = 0xFFFFFFFFu, km1 = 0xFFFFFFFFu;         // 16-bit masks of keys 4 j + e
-    if (tail) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (zmask & (1u << e)) {
-                if (e < 2)
-                    km0 &= ~(0xFFFFu << (16 * e));
-                else
-                    km1 &= ~(0xFFFFu << (16 * (e - 2)));
-            }
-    }
 #pragma unroll
     for (int T = 0; T < 32; ++T) {
         const uint32_t b = (T & 3) == 0 ? ad.v0 : (T & 3) == 1 ? ad.v1 : (T & 3) == 2 ? ad.v2 : ad.v3;
-        uint2 r = lds_read_tr16(stage + b + 128 * (T >> 2));
-        r.x &= km0;
-        r.y &= km1;
+        const uint2 r = lds_read_tr16(stage + b + 128 * (T >> 2));
         st.o[T] = mfma16k16(__builtin_bit_cast(shortx4_t, r), pop, st.o[T]);
+    }
+}
+
+// Zeroes, in a ring stage of np pages of 16 rows, the rows n >= nv[pg] of page
+// pg (whole rows, every slot).  Each wave that reads the stage does this itself
+// on its own schedule: every write is a zero, so no order between the waves
+// matters, and a wave's own writes precede its reads.
+template <int ROW>
+__device__ __forceinline__ void mla_zero_rows(unsigned char *stage, int np, int nv0, int nv1, int lane)
+{
+    constexpr int kSlots = ROW / 16;                   // 16-byte slots per row
+    for (int i = lane; i < np * 16 * kSlots; i += 64) {
+        const int pg = i / (16 * kSlots), rem = i - pg * 16 * kSlots;
+        const int n = rem / kSlots;
+        if (n >= (pg ? nv1 : nv0))
+            *reinterpret_cast<uint4 *>(stage + pg * 16 * ROW + rem * 16) = make_uint4(0, 0, 0, 0);
     }
 }
 
@@ -1818,7 +1878,8 @@ void va_mla_split_kernel(SplitParams p)
     const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
     const float c = p.scale_log2 * kd;
     unsigned char *qlds = lds;
-    unsigned char *ring = lds + C::kQBytes + kg * 2 * kPageBytes;
+    constexpr int PP = C::kPages;                      // pages per step of a key group
+    unsigned char *ring = lds + C::kQBytes + kg * 2 * PP * kPageBytes;
     const uint32_t ring_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(ring));
     const uint32_t lds_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(lds));
     const int64_t page_bytes = (int64_t)kPage * C::kRowBytes;
@@ -1844,40 +1905,57 @@ void va_mla_split_kernel(SplitParams p)
         const bool whole = (r0 == 0 && r1 == cnt);
         const int p0 = r0;
         const int npg = r1 - r0;                           // pages of the piece
-        const int nsteps = (npg + 1) >> 1;                 // steps of key group 0 (uniform)
+        const int nblk = (npg + PP - 1) / PP;              // steps of PP pages; key group kg
+        const int nsteps = (nblk + 1) >> 1;                // takes blocks kg, kg + 2, ... (uniform)
         const int slot = 2 * w + (s != sh.s);           // first or last piece of this workgroup
         const int R = lq * G;
         const bool rows_live = 16 * rt < R;
         const int32_t *btrow = p.bt + (int64_t)b * p.mbps;
         const int64_t maxpage = p.num_blocks - 1;
-        auto issue = [&](int k, int stage) {               // this wave's copies of page k of the piece
-            int64_t y = load_uniform(btrow, uniform(p0 + k));
-            y = y < 0 ? 0 : (y > maxpage ? maxpage : y);
-            const uint8_t *a = p.k + y * page_bytes;
-            const uint32_t dst = ring_addr + stage * kPageBytes;
-            int ln = lane;                                 // lane offsets rederived per copy (no
-            asm volatile("" : "+v"(ln));                   // registers held across the page loop)
+        auto pages_in = [&](int u) { return max(0, min(PP, npg - PP * u)); };   // pages of block u
+        auto issue = [&](int u, int stage) {               // this wave's copies of block u of the piece
 #pragma unroll
-            for (int i = 0; i < C::kMaxCopies; ++i)
-                if (i < ncp) {
-                    const int sl = 64 * (rt + 4 * i) + ln;     // LDS slot of this lane's 16 bytes
-                    const int n = sl / C::kChunks;             // key row
-                    const uint32_t off = (uint32_t)(n * C::kRowBytes + 16 * ((sl - n * C::kChunks) ^ C::swz(n)));
-                    dma16(a, off, dst + 1024 * (rt + 4 * i));
-                }
+            for (int pg = 0; pg < PP; ++pg) {
+                if (PP * u + pg >= npg)
+                    break;                                 // uniform
+                int64_t y = load_uniform(btrow, uniform(p0 + PP * u + pg));
+                y = y < 0 ? 0 : (y > maxpage ? maxpage : y);
+                const uint8_t *a = p.k + y * page_bytes;
+                const uint32_t dst = ring_addr + (stage * PP + pg) * kPageBytes;
+                int ln = lane;                             // lane offsets rederived per copy (no
+                asm volatile("" : "+v"(ln));               // registers held across the page loop)
+#pragma unroll
+                for (int i = 0; i < C::kMaxCopies; ++i)
+                    if (i < ncp) {
+                        const int sl = 64 * (rt + 4 * i) + ln; // LDS slot of this lane's 16 bytes
+                        const int n = sl / C::kChunks;         // key row; page pg of a step uses swz ^ 2 pg
+                        const uint32_t off =
+                            (uint32_t)(n * C::kRowBytes + 16 * ((sl - n * C::kChunks) ^ C::swz(n) ^ (2 * pg)));
+                        dma16(a, off, dst + 1024 * (rt + 4 * i));
+                    }
+            }
         };
-        auto wait_own = [&]() {                            // this wave's copies of the older page landed
-            if (ncp == C::kMaxCopies)
-                wait_vmcnt<C::kMaxCopies>();
-            else
-                wait_vmcnt<C::kMaxCopies - 1>();
+        auto wait_older = [&](int np) {                    // this wave's copies of the older block
+            if (np == 2) {                                 // landed; np pages of the next one may not
+                if (ncp == C::kMaxCopies)
+                    wait_vmcnt<2 * C::kMaxCopies>();
+                else
+                    wait_vmcnt<2 * (C::kMaxCopies - 1)>();
+            } else if (np == 1) {
+                if (ncp == C::kMaxCopies)
+                    wait_vmcnt<C::kMaxCopies>();
+                else
+                    wait_vmcnt<C::kMaxCopies - 1>();
+            } else {
+                wait_vmcnt<0>();
+            }
         };
 
         // ---- prologue: the first page of each key group; Q operands; the second
         __syncthreads();                                   // previous piece's LDS reads done
         float crow = c;                                    // logit multiplier of this lane's row
         if constexpr (KVT == kKvFp8) {
-            if (kg < npg)
+            if (kg < nblk)
                 issue(kg, 0);
             // this wave's row tile, lane (row n, j): dims 128 cc + 32 j .. +32
             const int n = pl & 15, j = pl >> 4;
@@ -1923,7 +2001,7 @@ void va_mla_split_kernel(SplitParams p)
                 if ((cc < 3) == (kg == 0))
                     convert_q_block<1>(qlds, raw[cc], kx, rt * 5 + cc, pl);
             __syncthreads();                               // Q operands visible
-            if (kg + 2 < npg)
+            if (kg + 2 < nblk)
                 issue(kg + 2, 1);
         } else {
             // Q operands copied straight in operand order: copy i = rt' * 18 + sl,
@@ -1960,41 +2038,42 @@ void va_mla_split_kernel(SplitParams p)
             limit = min(ctx + (r >> p.log2g), lk - 1);
         }
 
-        const MlaLane ad = mla_lane<KVT>(rt, pl);          // the loop's LDS offsets: 5 registers
+        const MlaLane ad = mla_lane<KVT>(rt, pl);          // the loop's LDS offsets: 9 registers
         for (int t = 0; t < nsteps; ++t) {
-            const int k = kg + 2 * t;                      // page of the piece
-            if (KVT == kKvFp8 && t == 0 && k + 2 < npg)
-                wait_own();                                // page k landed (page k + 2 may not)
+            const int k = kg + 2 * t;                      // block of the piece
+            if (KVT == kKvFp8 && t == 0)
+                wait_older(pages_in(k + 2));               // block k landed (block k + 2 may not)
             else
                 wait_vmcnt<0>();
             __syncthreads();                               // the group's copies too; stage t-1 free
-            if (t >= 1 && k + 2 < npg)
+            if (t >= 1 && k + 2 < nblk)
                 issue(k + 2, (t + 1) & 1);
-            if (k < npg && rows_live) {
+            if (k < nblk && rows_live) {
                 // other lane-derived values are rederived each step from an
                 // opaque lane index: hoisted out of the loop they would hold
                 // registers next to the 128 accumulators
                 int ln = lane;
                 asm volatile("" : "+v"(ln));
-                const unsigned char *stage = ring + (t & 1) * kPageBytes;
-                const int key0 = (p0 + k) * kPage;
-                const bool masked = key0 + 15 > ctx;
-                floatx4_t S;
-                if constexpr (KVT == kKvFp8)
-                    S = mla_qk_f8(stage, qlds, ad, ln);
-                else
-                    S = mla_qk_bf16(stage, qlds, ad);
-                const shortx4_t pop = mla_softmax(st, S, limit, key0, crow, ln, masked);
-                const bool tail = key0 + 15 >= lk;                 // uniform
-                uint32_t zmask = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (key0 + 4 * (ln >> 4) + e >= lk)
-                        zmask |= 1u << e;
-                if constexpr (KVT == kKvFp8)
-                    mla_pv_f8(st, stage, pop, tail, zmask, ad);
-                else
-                    mla_pv_bf16(st, stage, pop, tail, zmask, ad);
+                const unsigned char *stage = ring + (t & 1) * PP * kPageBytes;
+                const int key0 = (p0 + PP * k) * kPage;
+                if constexpr (KVT == kKvFp8) {
+                    const bool hasb = PP * k + 1 < npg;            // uniform: the step's second page
+                    const bool masked = key0 + 31 > ctx || !hasb;
+                    if (key0 + 31 >= lk || !hasb)                  // uniform: rows past the end
+                        mla_zero_rows<C::kRowBytes>(ring + (t & 1) * PP * kPageBytes, 2, lk - key0,
+                                                    hasb ? lk - key0 - 16 : 0, ln);
+                    floatx4_t S[2];
+                    mla_qk_f8(S, stage, qlds, ad, ln);
+                    const bf16x8_t pop = mla_softmax2(st, S, limit, key0, crow, ln, masked, hasb);
+                    mla_pv_f8(st, stage, pop, ad);
+                } else {
+                    const bool masked = key0 + 15 > ctx;
+                    if (key0 + 15 >= lk)                           // uniform: rows past the end
+                        mla_zero_rows<C::kRowBytes>(ring + (t & 1) * kPageBytes, 1, lk - key0, 0, ln);
+                    const floatx4_t S = mla_qk_bf16(stage, qlds, ad);
+                    const shortx4_t pop = mla_softmax(st, S, limit, key0, crow, ln, masked);
+                    mla_pv_bf16(st, stage, pop, ad);
+                }
             }
         }
         wait_vmcnt<0>();
