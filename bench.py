@@ -158,10 +158,21 @@ def cpu_baseline(p, budget_s: float = 12.0):
         if secs >= budget_s:
             break
     nbytes = algorithmic_bytes(p, done_seqs)
+    if not done_seqs:
+        return None
+    # the same oracle on one thread, over the first sequence with query rows
+    b1 = done_seqs[0]
+    rows1 = np.arange(int(p.cu_seqlens_q[b1]) * G, int(p.cu_seqlens_q[b1 + 1]) * G, dtype=np.int64)
+    t0 = time.perf_counter()
+    run(p, rows=rows1, threads=1)
+    secs1 = time.perf_counter() - t0
+    nbytes1 = algorithmic_bytes(p, [b1])
     return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{len(done_seqs)} of {p.num_seqs} sequences (all their rows), "
-                      f"{nbytes} algorithmic bytes in {secs:.2f} s"}
+                      f"{nbytes} algorithmic bytes in {secs:.2f} s",
+            "value_1_thread": round(nbytes1 / secs1 / 1e9, 4),
+            "sample_1_thread": f"sequence {b1} (all its rows), {nbytes1} algorithmic bytes in {secs1:.2f} s"}
 
 
 def main():
@@ -350,6 +361,21 @@ def main():
     value = alg / (ms_step * 1e-3) / 1e9
     log(f"bench: {args.steps} steps, {ms_step * 1e3:.2f} us/step, {value:.1f} GB/s effective")
 
+    # Spread of single calls: events around every call of a back-to-back run
+    # (a pass of its own; value above comes from the undisturbed run).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i, (ea, eb) in enumerate(ev):
+        ea.record(stream)
+        step(n_warm + args.steps + i)
+        eb.record(stream)
+    torch.cuda.synchronize()
+    per_call = np.array([ea.elapsed_time(eb) * 1e3 for ea, eb in ev])
+    spread = {"p10": round(float(np.percentile(per_call, 10)), 3),
+              "median": round(float(np.median(per_call)), 3),
+              "p90": round(float(np.percentile(per_call, 90)), 3),
+              "method": "HIP events around each call, back to back"}
+
     roofline = None
     if va.VA_STAGE_SPLIT_KV in stages:
         # The main kernel is timed in a run of its own launches.
@@ -379,6 +405,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 6),
         "us_per_call": round(ms_step * 1e3, 3),
+        "us_per_call_spread": spread,
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
         "higher_is_better": True,
         "scaling": "weak",
