@@ -496,13 +496,18 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
 // compiler does not insert a conservative wait for it before every LDS read;
 // the ring below waits on vmcnt itself.  No other vector-memory instruction
 // is issued inside the page loop, so the counts are exact.
+// The copies carry the nontemporal hint (nt): every cache byte is read once
+// per call, so nothing is gained by keeping its lines in L2 or the last-level
+// cache, and with the hint the same calls run 3-10 % faster (measured on the
+// long-context, high-concurrency, shape-sweep and MLA workloads, with four
+// rotating copies of the pools so that no call finds the previous one's data).
 // M0 is written inside the statement and listed as clobbered; nothing else in
 // these kernels reads M0 (clang warns that it is a reserved register).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds_addr)
 {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                  :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -513,7 +518,7 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16_at(const void *addr, uint32_t lds_addr)
 {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
                  :: "v"(addr), "s"(lds_addr) : "memory", "m0");
 }
 #pragma clang diagnostic pop
