@@ -222,8 +222,8 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the kernel is single-device; see DESIGN.md for how the path would shard)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the kernels run on a single device)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -45,7 +45,7 @@
  *
  * FP8 format: OCP E4M3FN (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
  * no infinities, S.1111.111 = NaN, subnormals m/8 * 2^-6).  The pages only say
- * "FP8 KV"; gfx950's native fp8 is this format (reading recorded in the design doc).
+ * "FP8 KV"; this is the e4m3 variant that gfx950 converts and multiplies natively.
  */
 #include <math.h>
 #include <pthread.h>
