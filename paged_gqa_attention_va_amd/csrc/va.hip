@@ -1867,6 +1867,14 @@ void va_mla_split_kernel(SplitParams p)
     const int wave = uniform(threadIdx.x >> 6);
     const int rt = wave & 3;                           // row tile
     const int kg = wave >> 2;                          // key group
+    // Each SIMD holds one wave of each key group (wave w runs on SIMD w % 4),
+    // and both run the same QK -> softmax -> PV order behind one barrier per
+    // step.  Key group 0 issues at a higher priority, so its waves run ahead
+    // and the two waves of a SIMD drift into different phases: one wave's
+    // matrix work then overlaps the other's vector and LDS work (measured 8 %
+    // to 10 % faster with an FP8 cache, 2 % with bf16; bit-identical output).
+    if (kg == 0)
+        __builtin_amdgcn_s_setprio(3);
     const int w = blockIdx.x;
     const int G = 1 << p.log2g;
 
