@@ -12,8 +12,10 @@ random block table.  It is the one the metric is quoted on: 16:1 GQA, FP8 KV,
                algorithmic bytes.  Those are the unique KV pages within
                seqused_k (K and V) plus the Q and O bytes.
   roofline     the main kernel: the same algorithmic bytes over its average
-               launch time, measured with HIP events on the stream it runs on
-               around a run of back-to-back launches, against the 8 TB/s peak.
+               duration inside the timed whole calls, against the 8 TB/s
+               peak.  The duration comes from HIP events that the main
+               kernel's own dispatch records (va_run_timed) on the stream it
+               runs on, in every one of the timed steps.
   cpu_baseline the fp64 oracle, timed on this host's cores on a bounded
                sample of the same workload.
 
@@ -22,6 +24,7 @@ several copies, so the 256 MiB memory-side cache cannot serve a step from
 the previous one.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -35,7 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
-MAIN_KERNEL = {"fp8": "va_split_kv_fp8_w8_kernel", "bf16": "va_split_kv_bf16_w8_kernel"}
+MAIN_KERNEL = {"fp8": "va_split_kv_fp8_w4_kernel", "bf16": "va_split_kv_bf16_w8_kernel"}
 MLA_KERNEL = "va_mla_split_kernel"
 # Arithmetic of the path: FP8 KV runs QK^T on fp8 MFMA (Q as an exact hi/lo fp8
 # pair) and PV on bf16 MFMA; bf16 KV runs both on bf16 MFMA; fp32 accumulation.
@@ -120,6 +123,95 @@ def load_traffic(workload: str):
     return e.get("bytes_per_launch")
 
 
+def host_cpu():
+    """CPU model and core counts of this host (for the cpu_baseline record)."""
+    model, phys = None, set()
+    try:
+        cur = {}
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model is None:
+                    model = v
+                elif k in ("physical id", "core id"):
+                    cur[k] = v
+                elif not k and cur:
+                    phys.add((cur.get("physical id"), cur.get("core id")))
+                    cur = {}
+            if cur:
+                phys.add((cur.get("physical id"), cur.get("core id")))
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"cpu_model": model, "physical_cores": len(phys) or None, "logical_cpus_available": avail}
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime (the library torch already loaded),
+    for va_run_timed, whose main-kernel dispatch records them itself."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h.value)
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(ctypes.c_void_p(h))
+        self.ev = []
+
+
+def stamp_report(st: np.ndarray, grid: int) -> dict:
+    """Phase times (us, from the earliest kernel entry) of one traced call, from the
+    per-wave timestamps of a VA_STAMPS library (16 words per wave, see va.h)."""
+    w = st.reshape(grid, 4, 16).astype(np.int64)
+    live = w[:, 0, 1] > 0                                  # workgroups that found work
+    w = w[live]
+    t0 = w[:, :, 0].min()
+    us = lambda x: (x - t0) / 100.0                        # 100 MHz clock -> us
+    med = lambda a: round(float(np.median(a)), 2)
+    first = w[:, :, 6] > 0
+    steps = w[:, :, 9]
+    per_step = (w[:, :, 6] - w[:, :, 4]) / np.maximum(steps - 1, 1) / 100.0
+    rep = {"workgroups": int(live.sum()),
+           "entry": med(us(w[:, :, 0])),
+           "located": med(us(w[:, :, 1])),
+           "q_landed": med(us(w[:, :, 2][first])),
+           "q_operands_loaded": med(us(w[:, :, 3][first])),
+           "step0_landed": med(us(w[:, :, 4][first])),
+           "step1_landed": med(us(w[:, :, 5][first])),
+           "page_loop_done": med(us(w[:, :, 6][first])),
+           "epilogue_states_out": med(us(w[:, :, 13][first])),
+           "epilogue_o_published": med(us(w[:, :, 14][first])),
+           "epilogue_all_published": med(us(w[:, :, 15][first])),
+           "epilogue_done": med(us(w[:, :, 7][first])),
+           "exit_median": med(us(w[:, :, 8])),
+           "exit_last": round(float(us(w[:, :, 8]).max()), 2),
+           "steps_first_piece_median": int(np.median(steps[first])),
+           "us_per_step_median": med(per_step[first & (steps > 1)]),
+           "pieces_max": int(w[:, :, 10].max()),
+           "second_passes": int((w[:, :, 12] > 1).sum())}
+    return rep
+
+
 def cpu_baseline_pe(pe, budget_s: float = 12.0):
     """Time the oracle on the first sequences of a prefix + extend call, one
     more sequence per round, until about budget_s of work."""
@@ -133,10 +225,12 @@ def cpu_baseline_pe(pe, budget_s: float = 12.0):
         oracle.attn_prefix_extend_problem(sub, threads=threads)
         secs = time.perf_counter() - t0
     nbytes = algorithmic_bytes_pe(pe, range(n))
-    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"the first {n} of {pe.num_seqs} sequences (all their rows, re-layout included), "
-                      f"{nbytes} algorithmic bytes in {secs:.2f} s"}
+    rec = {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"the first {n} of {pe.num_seqs} sequences (all their rows, re-layout included), "
+                     f"{nbytes} algorithmic bytes in {secs:.2f} s"}
+    rec.update(host_cpu())
+    return rec
 
 
 def cpu_baseline(p, budget_s: float = 12.0):
@@ -167,12 +261,14 @@ def cpu_baseline(p, budget_s: float = 12.0):
     run(p, rows=rows1, threads=1)
     secs1 = time.perf_counter() - t0
     nbytes1 = algorithmic_bytes(p, [b1])
-    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{len(done_seqs)} of {p.num_seqs} sequences (all their rows), "
-                      f"{nbytes} algorithmic bytes in {secs:.2f} s",
-            "value_1_thread": round(nbytes1 / secs1 / 1e9, 4),
-            "sample_1_thread": f"sequence {b1} (all its rows), {nbytes1} algorithmic bytes in {secs1:.2f} s"}
+    rec = {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"{len(done_seqs)} of {p.num_seqs} sequences (all their rows), "
+                     f"{nbytes} algorithmic bytes in {secs:.2f} s",
+           "value_1_thread": round(nbytes1 / secs1 / 1e9, 4),
+           "sample_1_thread": f"sequence {b1} (all its rows), {nbytes1} algorithmic bytes in {secs1:.2f} s"}
+    rec.update(host_cpu())
+    return rec
 
 
 def main():
@@ -204,6 +300,14 @@ def main():
                          "(512 latent + 64 RoPE), one kv head, the workload's query heads")
     ap.add_argument("--stage", choices=["all", "split", "merge"], default="all",
                     help="profiling aid: time only one kernel per step")
+    ap.add_argument("--stamps", action="store_true",
+                    help="load the VA_STAMPS build (libva_stamps.so) and report the main kernel's "
+                         "per-phase times of one call after the timed steps")
+    ap.add_argument("--stamps-out", default=None, metavar="NPY",
+                    help="with --stamps: also save the raw per-wave timestamps (.npy)")
+    ap.add_argument("--warm", action="store_true",
+                    help="warm-cache run: one copy of the KV pools, so steps may find the previous "
+                         "step's data in the memory-side cache (the default rotates 4 copies)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -230,6 +334,14 @@ def main():
     import torch
     import paged_gqa_attention_va_amd as va
     import va_inputs
+
+    if args.warm:
+        args.copies = 1
+    if args.stamps:                       # the diagnostic build replaces the library
+        from paged_gqa_attention_va_amd import _build as va_build
+        if not os.path.exists(va_build.LIB_STAMPS):
+            raise RuntimeError(f"{va_build.LIB_STAMPS} is not built (paged_gqa_attention_va_amd._build)")
+        va._lib = va.library(va_build.LIB_STAMPS)
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
@@ -306,8 +418,15 @@ def main():
             slots.append(p.block_table[b, j // p.page_size].astype(np.int64) * p.page_size + j % p.page_size)
         kv_indptr = torch.from_numpy(indptr).to(dev)
         kv_indices = torch.from_numpy(np.concatenate(slots).astype(np.int32)).to(dev)
-    plan = (va.Plan.for_prefix_extend(pe, force_grid=args.grid) if pe is not None
-            else va.Plan.for_problem(p, force_grid=args.grid))
+    make_plan = ((lambda: va.Plan.for_prefix_extend(pe, force_grid=args.grid)) if pe is not None
+                 else (lambda: va.Plan.for_problem(p, force_grid=args.grid)))
+    plan = make_plan()
+    t_plan = []
+    for _ in range(50):                   # host cost of a plan (once per shape, never per call)
+        t0 = time.perf_counter()
+        make_plan()
+        t_plan.append(time.perf_counter() - t0)
+    plan_us = round(float(np.median(t_plan)) * 1e6, 1)
     ws = plan.workspace(dev)
     out = torch.empty((q.shape[0], q.shape[1], plan.v_head_dim), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -330,6 +449,16 @@ def main():
             else:
                 plan.run(q, ks[c], vs[c], bt_i, cu, sk_i, p.scale, kd, vd, out=out, workspace=ws,
                          stream=stream, stage=s, sinks=sinks)
+
+    def step_timed(i, ev_a, ev_b):
+        """One whole call whose main-kernel dispatch records ev_a / ev_b."""
+        c = i % args.copies
+        bt_i, sk_i = bt, sk
+        if args.draft_extend:
+            bt_i, sk_i = va.spec_block_table(kv_indptr, kv_indices, p.block_table.shape[1],
+                                             p.page_size, stream=stream)
+        plan.run_timed(q, ks[c], vs[c], bt_i, cu, sk_i, p.scale, kd, vd, out, ws, stream, ev_a, ev_b,
+                       sinks=sinks)
 
     def timed(n, first, stage_list=stages):
         """Average ms per step over n back-to-back steps, HIP events on `stream`
@@ -354,7 +483,8 @@ def main():
         if n_warm % 64 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    log(f"bench: {n_warm} warmup steps done in {time.perf_counter() - t_w:.1f} s")
+    warm_s = time.perf_counter() - t_w
+    log(f"bench: {n_warm} warmup steps done in {warm_s:.1f} s")
 
     ms_step = timed(args.steps, n_warm)
     alg = algorithmic_bytes_pe(pe) if pe is not None else algorithmic_bytes(p)
@@ -378,18 +508,59 @@ def main():
 
     roofline = None
     if va.VA_STAGE_SPLIT_KV in stages:
-        # The main kernel is timed in a run of its own launches.
-        if stages == (va.VA_STAGE_SPLIT_KV,):
-            main_ms = ms_step
+        # Main-only launches back to back: a labelled extra, not the roofline.
+        main_only_ms = ms_step if stages == (va.VA_STAGE_SPLIT_KV,) else \
+            timed(args.steps, n_warm, (va.VA_STAGE_SPLIT_KV,))
+        main_ms, ms_step_ev = None, None
+        if args.stage == "all" and pe is None:
+            # The roofline time: the main kernel inside whole calls, from events its
+            # own dispatch records in every one of a second run of timed steps.
+            evs = HipEvents(2 * args.steps)
+            a = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for i in range(args.steps):
+                step_timed(n_warm + i, evs.ev[2 * i], evs.ev[2 * i + 1])
+            e.record(stream)
+            torch.cuda.synchronize()
+            ms_step_ev = a.elapsed_time(e) / args.steps
+            durs = [evs.elapsed_ms(evs.ev[2 * i], evs.ev[2 * i + 1]) for i in range(args.steps)]
+            evs.close()
+            main_ms = float(np.mean(durs))
+            log(f"bench: main kernel inside whole calls {main_ms * 1e3:.2f} us (whole calls of that run "
+                f"{ms_step_ev * 1e3:.2f} us); main-only launches {main_only_ms * 1e3:.2f} us")
         else:
-            main_ms = timed(args.steps, n_warm, (va.VA_STAGE_SPLIT_KV,))
+            main_ms = main_only_ms
+            log(f"bench: main kernel {main_ms * 1e3:.2f} us/launch (main-only launches)")
         achieved = alg / (main_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                     "traffic": load_traffic(workload),
                     "kernel": MLA_KERNEL if args.mla else MAIN_KERNEL[p.kv_dtype],
-                    "us_per_launch": round(main_ms * 1e3, 3)}
-        log(f"bench: main kernel {main_ms * 1e3:.2f} us/launch, {achieved:.1f} GB/s")
+                    "us_per_launch": round(main_ms * 1e3, 3),
+                    "timing": ("events recorded by the main kernel's own dispatch, in every step of a "
+                               "run of timed whole calls" if ms_step_ev is not None
+                               else "back-to-back main-kernel launches"),
+                    "us_per_call_of_that_run": None if ms_step_ev is None else round(ms_step_ev * 1e3, 3),
+                    "us_per_launch_main_only": round(main_only_ms * 1e3, 3)}
+
+    stamps = None
+    if args.stamps and pe is None:
+        # every call of a back-to-back run overwrites the buffer: it ends up holding
+        # the last call, in steady state
+        buf = torch.zeros(plan.grid * 4 * 16, dtype=torch.int64, device=dev)
+        va.set_stamp_buffer(buf)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(n_warm + 3 * args.steps + i)
+        torch.cuda.synchronize()
+        va.set_stamp_buffer(None)
+        raw = buf.cpu().numpy()
+        stamps = stamp_report(raw, plan.grid)
+        log(f"bench: phase stamps (last of {args.steps} back-to-back calls) {stamps}")
+        if args.stamps_out:
+            np.save(args.stamps_out, raw)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -402,7 +573,8 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": n_warm,
+        "warmup_seconds": round(warm_s, 2),
         "ms_per_step": round(ms_step, 6),
         "us_per_call": round(ms_step * 1e3, 3),
         "us_per_call_spread": spread,
@@ -417,10 +589,14 @@ def main():
                    "kv_len_max": int(p.max_seqlen_k), "q_heads": p.num_q_heads,
                    "kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "page": p.page_size,
                    "kv_dtype": p.kv_dtype, "algorithmic_bytes": alg, "grid": plan.grid,
-                   "pool_copies": args.copies, "stage": args.stage},
+                   "pool_copies": args.copies, "cache": "warm" if args.warm else "cold",
+                   "stage": args.stage},
+        "plan_host_us": plan_us,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if stamps is not None:
+        rec["stamps"] = stamps
     print(json.dumps(rec), flush=True)
 
 

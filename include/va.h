@@ -217,6 +217,35 @@ va_status va_run_ex(va_plan_t plan, int32_t stage, const void *q, const void *k_
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * va_run_ex (stage VA_STAGE_ALL) for a caller that measures the split-KV main
+ * kernel inside whole calls: main_start and main_stop are hipEvent_t handles
+ * (created by the caller with timing enabled) that the main kernel's dispatch
+ * records itself (hipExtLaunchKernelGGL), so hipEventElapsedTime(main_start,
+ * main_stop) is that kernel's execution time, with no separate event commands
+ * between the two kernels of the call.  Paged-layout plans only (a prefix +
+ * extend plan is VA_ERR_INVALID_ARG, as for va_run_ex).  Null events are
+ * VA_ERR_INVALID_ARG.  Other arguments and errors as va_run_ex.
+ */
+va_status va_run_timed(va_plan_t plan, const void *q, const void *k_pool, const void *v_pool,
+                       const int32_t *block_table, const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                       float softmax_scale, const float *k_descale, const float *v_descale,
+                       const float *sinks, void *out, void *workspace, size_t workspace_bytes,
+                       void *stream, void *main_start, void *main_stop);
+
+/*
+ * Diagnostic.  A library compiled with -DVA_STAMPS records, for every wave of
+ * the FP8 paged main kernel, the GPU's constant 100 MHz clock at the phase
+ * boundaries of its first piece (work located, Q landed, Q operands loaded,
+ * first and second steps' pages landed, page loop done, epilogue done) and at
+ * exit, plus step, piece and pass counts and the wave's XCD, into `buffer`:
+ * 16 uint64 words per wave, wave kg (0..3) of workgroup w at (w * 4 + kg) * 16.
+ * `buffer` is a device pointer of `bytes` bytes; runs whose grid does not fit
+ * record nothing.  NULL turns recording off.  The setting is process-wide.
+ * Without VA_STAMPS this returns VA_ERR_UNSUPPORTED and records nothing.
+ */
+va_status va_set_stamp_buffer(void *buffer, size_t bytes);
+
+/*
  * Check one call's device metadata against the plan (the rules below), as
  * va_run would read it.  Every rule follows from the operation: query rows are
  * the prefix sums cu_seqlens_q, each sequence has at most max_seqlen_q of

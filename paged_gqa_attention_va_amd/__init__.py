@@ -31,7 +31,7 @@ VA_BAD_CU_SEQLENS_Q, VA_BAD_Q_LEN, VA_BAD_SEQUSED_K, VA_BAD_Q_GT_K, VA_BAD_PAGE 
 
 EXPORTED = ("va_plan", "va_plan_workspace_bytes", "va_plan_grid", "va_run", "va_run_ex",
             "va_plan_destroy", "va_status_str", "va_fp8_to_bf16", "va_spec_block_table",
-            "va_validate", "va_run_prefix_extend")
+            "va_validate", "va_run_prefix_extend", "va_run_timed", "va_set_stamp_buffer")
 
 _lib = None
 
@@ -90,6 +90,10 @@ def library(path: str = LIB_PATH):
     lib.va_validate.argtypes = [P, P, P, P, P, P]
     lib.va_fp8_to_bf16.restype = ctypes.c_int
     lib.va_fp8_to_bf16.argtypes = [P, P, ctypes.c_int64, P]
+    lib.va_run_timed.restype = ctypes.c_int
+    lib.va_run_timed.argtypes = run_args[:10] + [P] + run_args[10:] + [P, P]
+    lib.va_set_stamp_buffer.restype = ctypes.c_int
+    lib.va_set_stamp_buffer.argtypes = [P, ctypes.c_size_t]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -276,6 +280,23 @@ class Plan:
         _check(st, "va_run")
         return out
 
+    def run_timed(self, q, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k, softmax_scale: float,
+                  k_descale, v_descale, out, workspace, stream, main_start: int, main_stop: int, sinks=None):
+        """Enqueue one whole call (va_run_timed) whose main-kernel dispatch records
+        the two hipEvent_t handles main_start / main_stop (ints)."""
+        self._check_tensors(q, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k, k_descale, v_descale)
+        _same_device(q.device, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k, k_descale, v_descale,
+                     sinks, out, workspace)
+        sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        st = self._lib.va_run_timed(
+            self._h, ptr(q), ptr(k_pool), ptr(v_pool), ptr(block_table), ptr(cu_seqlens_q), ptr(seqused_k),
+            ctypes.c_float(softmax_scale), ptr(k_descale), ptr(v_descale), ptr(sinks), ptr(out), ptr(workspace),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size()), ctypes.c_void_p(sptr),
+            ctypes.c_void_p(main_start), ctypes.c_void_p(main_stop))
+        _check(st, "va_run_timed")
+        return out
+
     def validate(self, block_table, cu_seqlens_q, seqused_k, result=None, stream=None):
         """Enqueue va_validate; returns the int32 device tensor [bits, first bad
         sequence] (read it after the stream has reached it)."""
@@ -336,6 +357,17 @@ def fp8_to_bf16(codes, stream=None):
     _check(lib.va_fp8_to_bf16(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                               codes.numel(), ctypes.c_void_p(stream.cuda_stream)), "va_fp8_to_bf16")
     return out
+
+
+def set_stamp_buffer(buf, lib=None) -> None:
+    """Point a VA_STAMPS build of the library at a device buffer (a uint8 or
+    int64 tensor) for phase timestamps; None turns recording off."""
+    lib = lib or library()
+    if buf is None:
+        _check(lib.va_set_stamp_buffer(None, 0), "va_set_stamp_buffer")
+    else:
+        _check(lib.va_set_stamp_buffer(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size()),
+               "va_set_stamp_buffer")
 
 
 def build(verbose: bool = False) -> str:

@@ -29,16 +29,28 @@ def compile_flags():
             "-Wall"]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile csrc/va.hip into paged_gqa_attention_va_amd/libva.so (always recompiles)."""
-    tmp = LIB + f".tmp{os.getpid()}"
+# The same source with the phase timestamps of the FP8 paged kernel compiled in
+# (va_set_stamp_buffer); a diagnostic library, loaded only by bench.py --stamps.
+LIB_STAMPS = os.path.join(HERE, "libva_stamps.so")
+
+
+def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
+    """Compile csrc/va.hip into `out` (default paged_gqa_attention_va_amd/libva.so;
+    always recompiles)."""
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [hipcc()] + compile_flags() + list(extra) + [SRC, "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build_stamps(verbose: bool = False) -> str:
+    """Compile the diagnostic libva_stamps.so (-DVA_STAMPS)."""
+    return build(verbose=verbose, extra=("-DVA_STAMPS",), out=LIB_STAMPS)
 
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_stamps(verbose=True))

@@ -40,6 +40,7 @@
 // with no host-side lengths (graph-safe).  Only a WG's first and last piece can
 // be split: they write their partials to workspace slots 2w and 2w + 1.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -100,6 +101,7 @@ struct SplitParams {
     const uint8_t *vext;
     int64_t num_indices;  // elements of kv_indices
     int64_t num_rows;     // rows of the k / v buffers
+    unsigned long long *stamps;   // phase timestamps (library built with VA_STAMPS), else null
 };
 
 struct MergeParams {
@@ -113,6 +115,34 @@ struct MergeParams {
     uint16_t *out;
     int32_t num_seqs, hq, hkv, log2g, max_q, rows_max, total_q;
 };
+
+// ------------------------------------------------------ phase timestamps --
+//
+// A library built with -DVA_STAMPS records, per wave of the one-wave-per-SIMD
+// FP8 kernel, the constant 100 MHz clock (s_memrealtime) at phase boundaries
+// into the buffer given to va_set_stamp_buffer: kStampSlots 64-bit words per
+// wave, wave (w, kg) at ((w * 4 + kg) * kStampSlots).  Slots: 0 entry,
+// 1 work located, 2 own Q rows landed, 3 Q operands in registers, 4 first
+// step's pages landed, 5 second step's pages landed, 6 page loop done, 7
+// epilogue done (these six for the workgroup's first piece), 8 exit, 9 steps
+// of the first piece, 10 pieces, 11 XCD of the workgroup, 12 page-loop passes
+// of the first piece, 13..15 the epilogue of the first piece: row states
+// exchanged, scaled O published, all published.  Without VA_STAMPS the
+// statements compile to nothing.
+constexpr int kStampSlots = 16;
+#ifdef VA_STAMPS
+#define VA_STAMP(p, w, kg, lane, k, value)                                                   \
+    do {                                                                                 \
+        if ((p).stamps && (lane) == 0)                                                   \
+            (p).stamps[((int64_t)(w) * 4 + (kg)) * kStampSlots + (k)] = (value);        \
+    } while (0)
+#define VA_NOW() __builtin_amdgcn_s_memrealtime()
+#else
+#define VA_STAMP(p, w, kg, lane, k, value) \
+    do {                                   \
+    } while (0)
+#define VA_NOW() 0ull
+#endif
 
 // ------------------------------------------------------------ primitives --
 
@@ -1156,6 +1186,887 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
         base += cnt;
         ++bg;
     }
+}
+
+// ------------------------------------ FP8 kernel, one wave per SIMD (w4) --
+//
+// 4 waves, one per SIMD.  Wave kg is key group kg: it computes every 4th step
+// (page pair) of the piece for every packed row of the piece (RT row tiles,
+// up to 64 rows), so each K and V byte a workgroup copies into LDS is read
+// once and each V element is converted to bf16 once.  A wave's O^T
+// accumulators (16 dim tiles x RT row tiles x 4 floats: 256 at RT = 4) sit in
+// the accumulation registers; its fp8 hi / lo Q operands (32 registers per
+// row tile) stay in vector registers for the whole piece, so the page loop
+// reads only K and V from LDS.
+//
+// Each wave owns 40 KiB of LDS: a K ring of 6 page slots and a V ring of 4
+// (4 KiB each: 16 key rows of 256 bytes; in K the 16-byte chunk c of row n
+// sits at slot c ^ n, so the 16 rows a QK read touches fall in different
+// banks; V rows are unswizzled, see w4_pv).  It copies its own pages into them and waits for them with vmcnt
+// alone: no workgroup barrier inside the page loop, so the four waves run
+// their steps independently.  Step t computes the wave's local pages 2t and
+// 2t + 1; at its top the wave copies K of pages 2t + 4, 2t + 5 and V of pages
+// 2t + 2, 2t + 3 into the slots step t - 1 used.  K therefore arrives two
+// steps ahead of its QK and V one step ahead (plus the QK and softmax of its
+// own step) of its PV: one step of lead was less than the memory latency of a
+// loaded GPU.
+//
+// Prologue of a piece: wave kg copies the bf16 rows of row tile kg into V
+// slots 2 and 3, converts them in place into the hi / lo operands, and puts
+// the rows' logit multipliers into K slot 4; after a barrier every wave loads
+// all row tiles' operands into registers; after a second barrier (every wave
+// holds them) those slots are handed back to the rings.
+// Epilogue: each wave writes its rows' m, l and scaled O (fp16) into its own
+// 40 KiB (see w4_epilogue); after barriers all 256 threads combine them.
+constexpr int kW4KSlots = 6;
+constexpr int kW4VSlots = 4;
+constexpr int kW4PageBytes = 4096;                          // one page of one kv head, K or V
+constexpr int kW4VBase = kW4KSlots * kW4PageBytes;           // V ring offset in a wave's region
+constexpr int kW4RingBytes = (kW4KSlots + kW4VSlots) * kW4PageBytes;   // 40 KiB per wave, 160 KiB in all
+constexpr int kW4QStage = kW4VBase + 2 * kW4PageBytes;       // prologue: row tile (V slots 2, 3)
+constexpr int kW4CStage = 4 * kW4PageBytes;                  // prologue: row multipliers (K slot 4)
+constexpr int kW4Ml = 8 * kW4PageBytes;                      // epilogue: (m, l) of the rows (V slot 2)
+constexpr int kW4Mw = kW4Ml + 512;                           // epilogue: (M, W) of the rows (wave 0)
+
+// QK^T of a step on fp8 from register-resident Q operands: K page a at ka,
+// page b at kb (slots of the ring).  qop[rt][kc][part]: row tile rt, dims
+// [128 kc, 128 kc + 128), part 0 = hi, 1 = lo (lane layout as qk_lds_f8).
+//
+// The MFMAs are written as inline assembly so that their results stay in
+// vector registers: with one wave per SIMD the compiler gives every MFMA an
+// accumulation-register destination, and the 256 O^T accumulators already fill
+// that file.  The compiler's hazard checks do not look inside the statements,
+// so they carry the required gaps themselves:
+//   - each statement starts with "s_nop 1": a vector ALU write of an operand
+//     needs 2 wait states before an MFMA reads it;
+//   - a chain accumulates into exactly its own registers, which same-shape
+//     MFMAs may do back to back, and 2 RT - 1 other MFMAs separate them;
+//   - w4_qk_done follows the last MFMA and every read of S depends on it: 19
+//     wait states, where an MFMA of this shape (8 passes) needs 11 before
+//     another instruction reads or writes its result.
+// One group of a step's QK MFMAs: dims [128 kc, 128 kc + 128), part 0 (hi) or
+// 1 (lo) of Q, all 2 RT chains (S[a][rt]: page a, row tile rt).  The first
+// group starts the chains from zero.  Operands: S first (a-major), then the two
+// K operands, then the RT Q operands.
+template <int RT> struct W4QkGroup;
+template <> struct W4QkGroup<1> {
+    __device__ static __forceinline__ void first(floatx4_t (&S)[2][1], const intx8_t (&k)[2],
+                                                 const intx8_t (&q)[1])
+    {
+        asm("s_nop 1\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %0, %2, %4, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %1, %3, %4, 0\n\t"
+            : "=&v"(S[0][0]), "=&v"(S[1][0])
+            : "v"(k[0]), "v"(k[1]), "v"(q[0]));
+    }
+    __device__ static __forceinline__ void acc(floatx4_t (&S)[2][1], const intx8_t (&k)[2],
+                                               const intx8_t (&q)[1])
+    {
+        asm("s_nop 1\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %0, %2, %4, %0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %1, %3, %4, %1\n\t"
+            : "+v"(S[0][0]), "+v"(S[1][0])
+            : "v"(k[0]), "v"(k[1]), "v"(q[0]));
+    }
+};
+template <> struct W4QkGroup<2> {
+    __device__ static __forceinline__ void first(floatx4_t (&S)[2][2], const intx8_t (&k)[2],
+                                                 const intx8_t (&q)[2])
+    {
+        asm("s_nop 1\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %0, %4, %6, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %2, %5, %6, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %1, %4, %7, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %3, %5, %7, 0\n\t"
+            : "=&v"(S[0][0]), "=&v"(S[0][1]), "=&v"(S[1][0]), "=&v"(S[1][1])
+            : "v"(k[0]), "v"(k[1]), "v"(q[0]), "v"(q[1]));
+    }
+    __device__ static __forceinline__ void acc(floatx4_t (&S)[2][2], const intx8_t (&k)[2],
+                                               const intx8_t (&q)[2])
+    {
+        asm("s_nop 1\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %0, %4, %6, %0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %2, %5, %6, %2\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %1, %4, %7, %1\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %3, %5, %7, %3\n\t"
+            : "+v"(S[0][0]), "+v"(S[0][1]), "+v"(S[1][0]), "+v"(S[1][1])
+            : "v"(k[0]), "v"(k[1]), "v"(q[0]), "v"(q[1]));
+    }
+};
+template <> struct W4QkGroup<3> {
+    __device__ static __forceinline__ void first(floatx4_t (&S)[2][3], const intx8_t (&k)[2],
+                                                 const intx8_t (&q)[3])
+    {
+        asm("s_nop 1\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %0, %6, %8, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %3, %7, %8, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %1, %6, %9, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %4, %7, %9, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %2, %6, %10, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %5, %7, %10, 0\n\t"
+            : "=&v"(S[0][0]), "=&v"(S[0][1]), "=&v"(S[0][2]), "=&v"(S[1][0]), "=&v"(S[1][1]), "=&v"(S[1][2])
+            : "v"(k[0]), "v"(k[1]), "v"(q[0]), "v"(q[1]), "v"(q[2]));
+    }
+    __device__ static __forceinline__ void acc(floatx4_t (&S)[2][3], const intx8_t (&k)[2],
+                                               const intx8_t (&q)[3])
+    {
+        asm("s_nop 1\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %0, %6, %8, %0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %3, %7, %8, %3\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %1, %6, %9, %1\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %4, %7, %9, %4\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %2, %6, %10, %2\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %5, %7, %10, %5\n\t"
+            : "+v"(S[0][0]), "+v"(S[0][1]), "+v"(S[0][2]), "+v"(S[1][0]), "+v"(S[1][1]), "+v"(S[1][2])
+            : "v"(k[0]), "v"(k[1]), "v"(q[0]), "v"(q[1]), "v"(q[2]));
+    }
+};
+template <> struct W4QkGroup<4> {
+    __device__ static __forceinline__ void first(floatx4_t (&S)[2][4], const intx8_t (&k)[2],
+                                                 const intx8_t (&q)[4])
+    {
+        asm("s_nop 1\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %0, %8, %10, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %4, %9, %10, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %1, %8, %11, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %5, %9, %11, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %2, %8, %12, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %6, %9, %12, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %3, %8, %13, 0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %7, %9, %13, 0\n\t"
+            : "=&v"(S[0][0]), "=&v"(S[0][1]), "=&v"(S[0][2]), "=&v"(S[0][3]), "=&v"(S[1][0]), "=&v"(S[1][1]), "=&v"(S[1][2]), "=&v"(S[1][3])
+            : "v"(k[0]), "v"(k[1]), "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]));
+    }
+    __device__ static __forceinline__ void acc(floatx4_t (&S)[2][4], const intx8_t (&k)[2],
+                                               const intx8_t (&q)[4])
+    {
+        asm("s_nop 1\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %0, %8, %10, %0\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %4, %9, %10, %4\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %1, %8, %11, %1\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %5, %9, %11, %5\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %2, %8, %12, %2\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %6, %9, %12, %6\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %3, %8, %13, %3\n\t"
+                "v_mfma_f32_16x16x128_f8f6f4 %7, %9, %13, %7\n\t"
+            : "+v"(S[0][0]), "+v"(S[0][1]), "+v"(S[0][2]), "+v"(S[0][3]), "+v"(S[1][0]), "+v"(S[1][1]), "+v"(S[1][2]), "+v"(S[1][3])
+            : "v"(k[0]), "v"(k[1]), "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]));
+    }
+};
+
+template <int RT>
+__device__ __forceinline__ void w4_qk_done(floatx4_t (&S)[2][RT])
+{
+    if constexpr (RT == 1)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(S[0][0]), "+v"(S[1][0]));
+    else if constexpr (RT == 2)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2"
+                     : "+v"(S[0][0]), "+v"(S[1][0]), "+v"(S[0][1]), "+v"(S[1][1]));
+    else if constexpr (RT == 3)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2"
+                     : "+v"(S[0][0]), "+v"(S[1][0]), "+v"(S[0][1]), "+v"(S[1][1]), "+v"(S[0][2]), "+v"(S[1][2]));
+    else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2"
+                     : "+v"(S[0][0]), "+v"(S[1][0]), "+v"(S[0][1]), "+v"(S[1][1]), "+v"(S[0][2]), "+v"(S[1][2]),
+                       "+v"(S[0][3]), "+v"(S[1][3]));
+}
+
+template <int RT>
+__device__ __forceinline__ void w4_qk(floatx4_t (&S)[2][RT], const unsigned char *ka, const unsigned char *kb,
+                                      const intx8_t (&qop)[RT][2][2], int lane)
+{
+    const int n = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        intx8_t kop[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const unsigned char *kp = a ? kb : ka;
+            const int c0 = 8 * kc + 2 * j;
+            const uint4 lo4 = *reinterpret_cast<const uint4 *>(kp + 256 * n + 16 * (c0 ^ n));
+            const uint4 hi4 = *reinterpret_cast<const uint4 *>(kp + 256 * n + 16 * ((c0 + 1) ^ n));
+            kop[a] = intx8_t{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
+                             (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+        }
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+            intx8_t q[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                q[rt] = qop[rt][kc][part];
+            if (kc == 0 && part == 0)
+                W4QkGroup<RT>::first(S, kop, q);
+            else
+                W4QkGroup<RT>::acc(S, kop, q);
+        }
+    }
+    w4_qk_done<RT>(S);
+}
+
+// Softmax part of a w4 step.  The accumulators are never rescaled inside the
+// page loop: each row keeps a reference m (log2 units), set from its first
+// visible keys, and p = 2^(x - m) is accumulated as long as x <= m + kTauW4.
+// Then p <= 2^64, |p v| <= 2^73 for any e4m3 value, and fp32 sums of up to
+// 2^24 keys stay below 2^97: no overflow, and the final O / l does not depend
+// on m.  A step whose row maximum t exceeds m + kTauW4 sets `retry` and moves
+// m to t; the rest of that pass is discarded, and the caller runs the piece's
+// page loop again from the final m.  Every logit of the piece is then at most
+// m + kTauW4 (steps that did not move m were within kTauW4 of an m that only
+// grew; the others are at most the final m), so the second pass never moves
+// m.  The row limit (last visible key) is derived only on masked steps.
+// Other arguments as softmax_step.
+constexpr float kTauW4 = 64.0f;
+
+template <int RT, bool CAP, bool MASKED>
+__device__ __forceinline__ void w4_softmax(RowState<RT> &st, bool &retry, bf16x8_t (&pop)[RT],
+                                           const floatx4_t (&S)[2][RT], int ctx, int lk, int log2g,
+                                           uint32_t wlim, int key0, bool has_b, const float (&c)[RT], float cap,
+                                           int lane)
+{
+    const int j = lane >> 4;
+    // ok[rt][i]: key i of this lane is visible to row (lane % 16) of tile rt
+    auto visible = [&](int rt, int a, int e) {
+        // last key row (lane % 16) of tile rt may see; a window starts wlim keys before it
+        const int limit = min(ctx + ((16 * rt + (lane & 15)) >> log2g), lk - 1);
+        const int key = key0 + 16 * a + 4 * j + e;
+        return (a == 0 || has_b) && (uint32_t)(limit - key) <= wlim;
+    };
+    // Without a softcap the multiplier c >= 0 (a negative one is folded into
+    // the sign of Q) only scales the logits: the row maximum is c max(S), and
+    // p = 2^(S c - m) is one fma and one exp2.  With a softcap the capped
+    // logits x are formed first.
+    float x[RT][8];
+    bool need_any = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v = S[a][rt][e];
+                if constexpr (CAP)
+                    v = softcap_log2(v * c[rt], cap);
+                if constexpr (MASKED)
+                    v = visible(rt, a, e) ? v : -INFINITY;
+                x[rt][4 * a + e] = v;
+            }
+        float lmax = fmaxf(fmaxf(fmaxf(x[rt][0], x[rt][1]), fmaxf(x[rt][2], x[rt][3])),
+                           fmaxf(fmaxf(x[rt][4], x[rt][5]), fmaxf(x[rt][6], x[rt][7])));
+        if constexpr (!CAP)
+            lmax = lmax == -INFINITY ? -INFINITY : lmax * c[rt];
+        need_any |= lmax > st.m[rt] + kTauW4;                 // also a row's first visible keys
+    }
+    if (__any(need_any)) {                                     // rare: never touches O
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float t = x[rt][0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i)
+                t = fmaxf(t, x[rt][i]);
+            if constexpr (!CAP)
+                t = t == -INFINITY ? -INFINITY : t * c[rt];
+            t = fmaxf(t, __shfl_xor(t, 16));
+            t = fmaxf(t, __shfl_xor(t, 32));                  // row max of this step
+            if (t > st.m[rt] + kTauW4) {
+                retry |= st.m[rt] != -INFINITY;                // else nothing is accumulated yet
+                st.m[rt] = t;
+            }
+        }
+    }
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const float mref = st.m[rt] == -INFINITY ? 0.0f : st.m[rt];
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (CAP)
+                p[i] = exp2_fast(x[rt][i] - mref);
+            else if constexpr (MASKED)                         // a masked key is -inf, even when c = 0
+                p[i] = x[rt][i] == -INFINITY ? 0.f : exp2_fast(__builtin_fmaf(x[rt][i], c[rt], -mref));
+            else
+                p[i] = exp2_fast(__builtin_fmaf(x[rt][i], c[rt], -mref));
+        }
+        uint4 w;
+        w.x = pack_bf16x2(p[0], p[1]);
+        w.y = pack_bf16x2(p[2], p[3]);
+        w.z = pack_bf16x2(p[4], p[5]);
+        w.w = pack_bf16x2(p[6], p[7]);
+        // l sums the bf16 weights the PV MFMA uses
+        float l = st.l[rt];
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), ones, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), ones, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), ones, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), ones, l, false);
+        st.l[rt] = l;
+        pop[rt] = __builtin_bit_cast(bf16x8_t, w);
+    }
+}
+
+// PV of a step: O^T += V^T P^T, as pv_lds, with the V pages of the step in two
+// slots (va, vb) whose rows are stored unswizzled (chunk c of key row n at
+// 256 n + 16 c): lane (m, j) reads dims 16 m + 8 h .. + 7 of key rows 4 j + e,
+// so every read of a step is one lane base plus an immediate.
+template <int RT>
+__device__ __forceinline__ void w4_pv(RowState<RT> &st, const unsigned char *va, const unsigned char *vb,
+                                      const bf16x8_t (&pop)[RT], bool masked, uint32_t zmask, int lane)
+{
+    const int m = lane & 15, j = lane >> 4;
+    const int lo = 1024 * j + 16 * m;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint2 vv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            vv[e] = *reinterpret_cast<const uint2 *>((e >> 2 ? vb : va) + lo + 256 * (e & 3) + 8 * h);
+        if (masked) {                                  // wave-uniform
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (zmask & (1u << e))
+                    vv[e] = make_uint2(0, 0);
+        }
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            const int q = 2 * h + qq;
+            uint32_t A[4][4];
+#pragma unroll
+            for (int kp = 0; kp < 4; ++kp) {
+                const uint32_t X = qq ? vv[2 * kp].y : vv[2 * kp].x;
+                const uint32_t Y = qq ? vv[2 * kp + 1].y : vv[2 * kp + 1].x;
+                const uint32_t lo2 = byte_perm(Y, X, 0x05010400u);   // X0 Y0 X1 Y1
+                const uint32_t hi2 = byte_perm(Y, X, 0x07030602u);   // X2 Y2 X3 Y3
+                A[0][kp] = fp8x2_lo_to_bf16x2(lo2);
+                A[1][kp] = fp8x2_hi_to_bf16x2(lo2);
+                A[2][kp] = fp8x2_lo_to_bf16x2(hi2);
+                A[3][kp] = fp8x2_hi_to_bf16x2(hi2);
+            }
+#pragma unroll
+            for (int xx = 0; xx < 4; ++xx) {
+                const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, make_uint4(A[xx][0], A[xx][1], A[xx][2], A[xx][3]));
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    st.o[4 * q + xx][rt] = mfma16(vop, pop[rt], st.o[4 * q + xx][rt]);
+            }
+        }
+    }
+}
+
+// Row tile of 16 packed rows staged in LDS as bf16 (row n at 512 n, its
+// 16-byte chunk c at slot c ^ n; rows n >= nr are not live and read as zero),
+// converted in place into the fp8 hi / lo operands [kc][part][half][lane] x
+// 16 B (the split of convert_q_block), and the rows' logit multipliers
+// |c| 2^-k_n into cst[n] (Q negated when c < 0).
+__device__ __forceinline__ void w4_convert_q(unsigned char *qst, float *cst, float c, int nr, int lane)
+{
+    const int n = lane & 15, j = lane >> 4;
+    const bool live = n < nr;
+    // a negative logit multiplier c is moved into the sign of Q, so that the
+    // multiplier the softmax sees is >= 0
+    const uint32_t flip = c < 0.f ? 0x80008000u : 0u;
+    c = fabsf(c);
+    uint32_t raw[2][16];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int chunk = 16 * kc + 4 * j + i;          // dims 8 chunk .. +8
+            const uint4 q4 = live ? *reinterpret_cast<const uint4 *>(qst + n * 512 + ((chunk ^ n) * 16))
+                                  : make_uint4(0, 0, 0, 0);
+            raw[kc][4 * i] = q4.x ^ flip;
+            raw[kc][4 * i + 1] = q4.y ^ flip;
+            raw[kc][4 * i + 2] = q4.z ^ flip;
+            raw[kc][4 * i + 3] = q4.w ^ flip;
+        }
+    float amax = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, raw[kc][i] << 16)),
+                                     fabsf(__builtin_bit_cast(float, raw[kc][i] & 0xFFFF0000u))));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));             // row max (4 lanes)
+    int k = 0;
+    if (amax > 0.f) {
+        int e;
+        frexpf(amax, &e);                                  // amax in [2^(e-1), 2^e)
+        k = min(8 - e, 127);
+    }
+    if (j == 0)
+        cst[n] = ldexpf(c, -k);
+    // every lane has read its rows (the writes below depend on those reads)
+    convert_q_block<1>(qst, raw[0], k, 0, lane);
+    convert_q_block<1>(qst, raw[1], k, 1, lane);
+}
+
+// Epilogue of a w4 piece.  The four key groups hold states (m_k, l_k, O_k) of
+// the same rows over disjoint keys; the piece's result is
+//   O = sum_k O_k 2^(m_k - M) / W,  W = sum_k l_k 2^(m_k - M),  M = max_k m_k,
+// and its log2-domain LSE is M + log2 W.  Three phases:
+//   1. each wave publishes its rows' m_k, l_k (at kW4Ml of its region);
+//   2. after a barrier each wave reads the four states of its rows, scales its
+//      own O_k by f_k = 2^(m_k - M) / W and publishes it in fp16 (the first
+//      32 KiB of its region: row r at 512 r, 16-byte chunk c at c ^ (r & 15); every
+//      scaled term is a part of a convex combination of V rows, so it is at
+//      most max |V| <= 448 for an e4m3 cache); wave 0 also publishes M, W;
+//   3. after a barrier every thread sums the four fp16 terms of (row, 8-dim
+//      chunk) items with packed fp16 adds, and writes the bf16 output row
+//      (whole piece: times v_descale, with a sink in the denominator) or the
+//      fp16 partial and the LSE (split piece).
+typedef _Float16 half2v_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t h2add(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v_t, a) + __builtin_bit_cast(half2v_t, b));
+}
+
+template <int RT>
+__device__ __forceinline__ void w4_epilogue(RowState<RT> &st, unsigned char *lds, const SplitParams &p, int kg,
+                                            int lane, int lq, int q0, int g, int slot, bool whole, float vd,
+                                            bool stamp)
+{
+    (void)stamp;
+    constexpr int NG = 4;
+    const int G = 1 << p.log2g;
+    const int n = lane & 15, j = lane >> 4;
+    const int R = min(lq * G, 16 * RT);
+    unsigned char *own = lds + kg * kW4RingBytes;
+    float *ml = reinterpret_cast<float *>(own + kW4Ml);                          // [row] (m, l)
+    float *mw = reinterpret_cast<float *>(lds + kW4Mw);                          // [row] (M, W), wave 0
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        float t = st.l[rt];
+        t += __shfl_xor(t, 16);
+        t += __shfl_xor(t, 32);
+        st.l[rt] = t;
+        if (16 * rt < R && j == 0) {
+            ml[(16 * rt + n) * 2] = st.m[rt];
+            ml[(16 * rt + n) * 2 + 1] = t;
+        }
+    }
+    __syncthreads();                                     // every key group's row states are out
+#ifdef VA_STAMPS
+    if (stamp)
+        VA_STAMP(p, blockIdx.x, kg, lane, 13, VA_NOW());
+#endif
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        if (16 * rt >= R)
+            break;                                       // uniform
+        const int row = 16 * rt + n;
+        float mk[NG], lk[NG];
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+            const float *mlk = reinterpret_cast<const float *>(lds + k * kW4RingBytes + kW4Ml);
+            mk[k] = mlk[row * 2];
+            lk[k] = mlk[row * 2 + 1];
+            M = fmaxf(M, lk[k] > 0.f ? mk[k] : -INFINITY);
+        }
+        float W = 0.f;
+#pragma unroll
+        for (int k = 0; k < NG; ++k)
+            W += lk[k] > 0.f ? lk[k] * exp2_fast(mk[k] - M) : 0.f;
+        const float f = (st.l[rt] > 0.f && W > 0.f) ? exp2_fast(st.m[rt] - M) / W : 0.f;
+        if (kg == 0 && j == 0) {
+            mw[row * 2] = M;
+            mw[row * 2 + 1] = W;
+        }
+        unsigned char *orow = own + (size_t)row * 512;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {                    // dims 64 j + 16 e + t, t = 0..15
+            uint4 a, b;
+            a.x = pack_f16x2(st.o[0][rt][e] * f, st.o[1][rt][e] * f);
+            a.y = pack_f16x2(st.o[2][rt][e] * f, st.o[3][rt][e] * f);
+            a.z = pack_f16x2(st.o[4][rt][e] * f, st.o[5][rt][e] * f);
+            a.w = pack_f16x2(st.o[6][rt][e] * f, st.o[7][rt][e] * f);
+            b.x = pack_f16x2(st.o[8][rt][e] * f, st.o[9][rt][e] * f);
+            b.y = pack_f16x2(st.o[10][rt][e] * f, st.o[11][rt][e] * f);
+            b.z = pack_f16x2(st.o[12][rt][e] * f, st.o[13][rt][e] * f);
+            b.w = pack_f16x2(st.o[14][rt][e] * f, st.o[15][rt][e] * f);
+            const int c0 = 8 * j + 2 * e;
+            *reinterpret_cast<uint4 *>(orow + ((c0 ^ n) * 16)) = a;
+            *reinterpret_cast<uint4 *>(orow + (((c0 + 1) ^ n) * 16)) = b;
+        }
+    }
+#ifdef VA_STAMPS
+    if (stamp)
+        VA_STAMP(p, blockIdx.x, kg, lane, 14, VA_NOW());
+#endif
+    __syncthreads();                                     // every scaled O_k is out
+#ifdef VA_STAMPS
+    if (stamp)
+        VA_STAMP(p, blockIdx.x, kg, lane, 15, VA_NOW());
+#endif
+    const int tid = opaque_tid();
+    const int c = tid & 31;
+    // thread: chunk c of rows tid / 32 + 8 it; every row's four terms are read
+    // first (rows past R re-read row R - 1 and are not stored)
+    uint4 s[2 * RT];
+#pragma unroll
+    for (int it = 0; it < 2 * RT; ++it) {
+        const int r = min((tid >> 5) + 8 * it, R - 1);
+        const int off = r * 512 + ((c ^ (r & 15)) * 16);
+        s[it] = *reinterpret_cast<const uint4 *>(lds + off);
+#pragma unroll
+        for (int k = 1; k < NG; ++k) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(lds + k * kW4RingBytes + off);
+            s[it].x = h2add(s[it].x, v.x);
+            s[it].y = h2add(s[it].y, v.y);
+            s[it].z = h2add(s[it].z, v.z);
+            s[it].w = h2add(s[it].w, v.w);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < 2 * RT; ++it) {
+        const int r = (tid >> 5) + 8 * it;
+        if (r >= R)
+            break;
+        const float M = mw[r * 2], W = mw[r * 2 + 1];
+        const int t = r >> p.log2g, h = r & (G - 1);
+        if (whole) {
+            float sc = W > 0.f ? vd : 0.f;
+            if (p.sinks) {                               // the sink joins the denominator only
+                const float sk = p.sinks[g * G + h] * 1.4426950408889634f;
+                const float mm = fmaxf(M, sk);
+                const float Wf = W > 0.f ? W * exp2_fast(M - mm) : 0.f;
+                sc = vd * Wf / (Wf + exp2_fast(sk - mm));
+            }
+            uint4 o;
+            o.x = pack_bf16x2(f16_lo(s[it].x) * sc, f16_hi(s[it].x) * sc);
+            o.y = pack_bf16x2(f16_lo(s[it].y) * sc, f16_hi(s[it].y) * sc);
+            o.z = pack_bf16x2(f16_lo(s[it].z) * sc, f16_hi(s[it].z) * sc);
+            o.w = pack_bf16x2(f16_lo(s[it].w) * sc, f16_hi(s[it].w) * sc);
+            *reinterpret_cast<uint4 *>(p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + 8 * c) = o;
+        } else {                                         // fp16 partial O / l as summed
+            const int64_t sr = ((int64_t)slot * p.rows_max + r) * kHeadDim + 8 * c;
+            *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.ws_o) + sr) = s[it];
+            if (c == 0)
+                p.ws_lse[(int64_t)slot * p.rows_max + r] = W > 0.f ? M + __log2f(W) : -INFINITY;
+        }
+    }
+}
+
+template <int RT, bool CAP>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void va_split_kv_fp8_w4_kernel(SplitParams p)
+{
+    constexpr int NG = 4;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[NG * kW4RingBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int kg = uniform(threadIdx.x >> 6);
+    const int w = blockIdx.x;
+    const int G = 1 << p.log2g;
+    VA_STAMP(p, w, kg, lane, 0, VA_NOW());
+
+    Share sh = locate(p, w, lane, w == 0 && kg == 0);
+    sh.n_eff = uniform(sh.n_eff);
+    sh.s = uniform(sh.s);
+    sh.e = uniform(sh.e);
+    sh.bg = uniform(sh.bg);
+    sh.base = uniform(sh.base);
+    if (w >= sh.n_eff)
+        return;                                        // uniform over the workgroup
+    VA_STAMP(p, w, kg, lane, 1, VA_NOW());
+#ifdef VA_STAMPS
+    int npieces = 0;
+    VA_STAMP(p, w, kg, lane, 11, (unsigned long long)__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)));
+#endif
+
+    const float kd = p.kdesc ? p.kdesc[0] : 1.0f;
+    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
+    const float c = p.scale_log2 * kd;
+    unsigned char *ring = lds + kg * kW4RingBytes;
+    const uint32_t ring_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(ring));
+    const int64_t page_bytes = (int64_t)kPage * p.hkv * kHeadDim;
+
+    const int bh = p.num_seqs * p.hkv;
+    int s = sh.s, bg = sh.bg, base = sh.base;
+    while (s < sh.e && bg < bh) {
+        int pl = lane;                                 // opaque per piece (see the w8 kernel)
+        asm volatile("" : "+v"(pl));
+        uint32_t off[4];
+        dma_lane_offsets(off, p.hkv, pl);
+        const int b = uniform(bg / p.hkv);
+        const int g = bg - b * p.hkv;
+        const int q0 = load_uniform(p.cu, b);
+        const int lq = checked_q_len(q0, load_uniform(p.cu, b + 1), p.total_q, p.max_q);
+        const int lk = load_uniform(p.seqused, b);
+        const int pb = first_page(lk, lq, p.window_left);      // the range starts at logical page pb
+        const int cnt = (lq <= 0 || lk <= 0) ? 0 : max(0, min((lk + kPage - 1) / kPage, p.mbps) - pb);
+        if (cnt == 0) {
+            ++bg;
+            continue;
+        }
+        const int ctx = lk - lq;
+        const int r0 = s - base;                               // piece = pages r0 .. r1 of the pair's range
+        const int r1 = min(sh.e, base + cnt) - base;
+        const bool whole = (r0 == 0 && r1 == cnt);
+        const int p0 = pb + r0, p1 = pb + r1;
+        const int slot = 2 * w + (s != sh.s);           // first or last piece of this workgroup
+        const int lo_max = p.window_left < 0 ? INT_MIN : ctx + lq - 1 - p.window_left;
+        const uint32_t wlim = p.window_left < 0 ? 0x7FFFFFFFu : (uint32_t)p.window_left;
+
+        // Wave kg computes a contiguous quarter of the piece's page pairs, so the
+        // block-table entries of its pages are consecutive.  Its local page i is
+        // logical page lp0 + i; the missing second page of the piece's last pair
+        // (an odd page count) re-reads the first, and its keys are masked.
+        const int npairs = (p1 - p0 + 1) >> 1;
+        const int pr0 = (int)(((int64_t)kg * npairs) / NG);
+        const int nst = (int)(((int64_t)(kg + 1) * npairs) / NG) - pr0;   // steps of this wave
+        const int npg = 2 * nst;
+        const int lp0 = p0 + 2 * pr0;
+        const int32_t *btrow = p.bt + (int64_t)b * p.mbps;
+        const uint8_t *kpool = p.k + (int64_t)g * kHeadDim;
+        const uint8_t *vpool = p.v + (int64_t)g * kHeadDim;
+        const int maxpage = (int)min(p.num_blocks - 1, (int64_t)INT_MAX);
+        auto entry = [&](int i) -> int {                       // pool page of local page i, clamped
+            const int pg = min(lp0 + i, p1 - 1);
+            const int y = load_uniform(btrow, pg);
+            return y < 0 ? 0 : (y > maxpage ? maxpage : y);
+        };
+        auto issue_k = [&](int y, int slot_i) {                // K of pool page y into K slot slot_i
+            const uint8_t *src_pg = kpool + (int64_t)y * page_bytes;
+            const uint32_t dst = ring_addr + (uint32_t)(slot_i * kW4PageBytes);
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                dma16(src_pg, off[x], dst + 1024 * x);
+        };
+        uint32_t off_v[4];                                     // V rows are stored unswizzled
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            off_v[x] = (uint32_t)((4 * x + (pl >> 4)) * p.hkv * kHeadDim + 16 * (pl & 15));
+        auto issue_v = [&](int y, int slot_i) {                // V of pool page y into V slot slot_i
+            const uint8_t *src_pg = vpool + (int64_t)y * page_bytes;
+            const uint32_t dst = ring_addr + (uint32_t)(kW4VBase + slot_i * kW4PageBytes);
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                dma16(src_pg, off_v[x], dst + 1024 * x);
+        };
+
+        // ---- prologue
+        __syncthreads();                                       // previous piece's LDS reads done
+        const int R = lq * G;
+        const int nr = min(max(R - 16 * kg, 0), 16);           // live rows of row tile kg
+        unsigned char *qst = ring + kW4QStage;
+        float *cst = reinterpret_cast<float *>(ring + kW4CStage);
+        for (int i = 0; 2 * i < nr; ++i) {                     // row pairs (G is even): 1 KiB each
+            const int r = 16 * kg + 2 * i;
+            const int64_t row0 = uniform((int)((int64_t)(q0 + (r >> p.log2g)) * p.hq + g * G + (r & (G - 1))));
+            const int rr = 2 * i + (pl >> 5), sl = pl & 31;    // lane's LDS row and slot
+            dma16(p.q + row0 * kHeadDim, (uint32_t)((pl >> 5) * 512 + ((sl ^ (rr & 15)) * 16)),
+                  ring_addr + (uint32_t)(kW4QStage + 2 * i * 512));
+        }
+        // With the Q rows go K and V of pages 0, 1 and K of pages 2, 3; after the
+        // exchange K of pages 4, 5 and V of pages 2, 3 (the exchange's slots).
+        int e2 = 0, e3 = 0, e4 = 0, e5 = 0;                    // block-table entries of pages 2 .. 5
+        auto prologue_copies = [&](int part) {
+            if (part == 0) {
+                if (nst > 0) {
+                    const int e0 = entry(0), e1 = entry(1);
+                    issue_k(e0, 0);
+                    issue_k(e1, 1);
+                    issue_v(e0, 0);
+                    issue_v(e1, 1);
+                }
+                e2 = entry(2);
+                e3 = entry(3);
+                e4 = entry(4);
+                e5 = entry(5);
+                if (nst > 1) {
+                    issue_k(e2, 2);
+                    issue_k(e3, 3);
+                }
+            } else {
+                if (nst > 2) {
+                    issue_k(e4, 4);
+                    issue_k(e5, 5);
+                }
+                if (nst > 1) {
+                    issue_v(e2, 2);
+                    issue_v(e3, 3);
+                }
+            }
+        };
+        prologue_copies(0);
+        if (nst > 1)
+            wait_vmcnt<24>();                                  // this wave's Q copies landed
+        else if (nst > 0)
+            wait_vmcnt<16>();
+        else
+            wait_vmcnt<0>();
+#ifdef VA_STAMPS
+        const bool first_piece = npieces++ == 0;
+        if (first_piece)
+            VA_STAMP(p, w, kg, lane, 2, VA_NOW());
+#endif
+        if (kg < RT)
+            w4_convert_q(qst, cst, c, nr, pl);
+        __syncthreads();                                       // every row tile converted
+        intx8_t qop[RT][2][2];
+        float crow[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const unsigned char *qs = lds + rt * kW4RingBytes + kW4QStage + pl * 16;
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int part = 0; part < 2; ++part) {
+                    const uint4 b0 = *reinterpret_cast<const uint4 *>(qs + (kc * 2 + part) * 2048);
+                    const uint4 b1 = *reinterpret_cast<const uint4 *>(qs + (kc * 2 + part) * 2048 + 1024);
+                    qop[rt][kc][part] = intx8_t{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                                                (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+                }
+            crow[rt] = reinterpret_cast<const float *>(lds + rt * kW4RingBytes + kW4CStage)[pl & 15];
+        }
+        __syncthreads();                                       // every wave holds the operands
+#ifdef VA_STAMPS
+        if (first_piece)
+            VA_STAMP(p, w, kg, lane, 3, VA_NOW());
+#endif
+        prologue_copies(1);
+
+        RowState<RT> st;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            st.m[rt] = -INFINITY;
+        for (int pass = 0;; ++pass) {                          // a second pass only after `retry`
+            if (pass > 0) {
+                prologue_copies(0);
+                prologue_copies(1);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                st.l[rt] = 0.f;
+#pragma unroll
+                for (int t = 0; t < 16; ++t)
+                    st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            bool retry = false;
+            // block-table entries of the copies at the top of step t: eK for K of pages
+            // 2t + 4, 2t + 5, eV for V of pages 2t + 2, 2t + 3 (the K copies of the step
+            // before), eN for K of pages 2t + 6, 2t + 7, loaded a step ahead (entry()
+            // clamps to the piece, so the loads past its end are harmless)
+            int eK0 = entry(6), eK1 = entry(7), eV0 = e4, eV1 = e5;
+            int eN0 = entry(8), eN1 = entry(9);
+            int ks = 0, vs = 0;                                // K / V slots of local page 2t
+            for (int t = 0; t < nst; ++t) {
+                // K of pages 2t, 2t+1 must have landed; the copies issued after them may
+                // not (their count follows from the fixed order of the copies)
+                if (t == 0) {
+                    if (nst > 2)
+                        wait_vmcnt<32>();
+                    else if (nst > 1)
+                        wait_vmcnt<24>();
+                    else
+                        wait_vmcnt<8>();
+                } else if (t == 1) {
+                    if (nst > 2)
+                        wait_vmcnt<16>();
+                    else
+                        wait_vmcnt<8>();
+                } else if (t + 1 < nst) {
+                    wait_vmcnt<24>();
+                } else {
+                    wait_vmcnt<16>();
+                }
+#ifdef VA_STAMPS
+                if (first_piece && pass == 0 && t <= 1)
+                    VA_STAMP(p, w, kg, lane, 4 + t, VA_NOW());
+#endif
+                if (t >= 1) {                                  // into the slots of step t - 1
+                    const int kslot = ks == 0 ? kW4KSlots - 2 : ks - 2;
+                    const int vslot = vs == 0 ? kW4VSlots - 2 : vs - 2;
+                    if (t + 2 < nst) {
+                        issue_k(eK0, kslot);
+                        issue_k(eK1, kslot + 1);
+                    }
+                    if (t + 1 < nst) {
+                        issue_v(eV0, vslot);
+                        issue_v(eV1, vslot + 1);
+                    }
+                    eV0 = eK0;
+                    eV1 = eK1;
+                    eK0 = eN0;
+                    eK1 = eN1;
+                    eN0 = entry(2 * t + 8);                    // for the K copies two steps on
+                    eN1 = entry(2 * t + 9);
+                }
+                const unsigned char *ka = ring + ks * kW4PageBytes;
+                const unsigned char *va = ring + kW4VBase + vs * kW4PageBytes;
+                ks = ks + 2 == kW4KSlots ? 0 : ks + 2;
+                vs = vs + 2 == kW4VSlots ? 0 : vs + 2;
+                // lane-derived LDS offsets are rederived each step from an
+                // opaque lane index: hoisted out of the loop they would hold
+                // registers next to the Q operands
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                floatx4_t S[2][RT];
+                w4_qk<RT>(S, ka, ka + kW4PageBytes, qop, ln);
+                __builtin_amdgcn_sched_barrier(0);
+                const int pa = lp0 + 2 * t;
+                const bool hb = pa + 1 < p1;
+                const int key0 = pa * kPage;
+                bf16x8_t pop[RT];
+                // uniform: a causal, length or window edge.  Only the softmax has two
+                // versions: two copies of the PV would give O two definitions per step
+                const bool masked = !hb || key0 + 31 > ctx || key0 < lo_max;
+                if (masked)
+                    w4_softmax<RT, CAP, true>(st, retry, pop, S, ctx, lk, p.log2g, wlim, key0, hb, crow, p.cap_log2,
+                                              ln);
+                else
+                    w4_softmax<RT, CAP, false>(st, retry, pop, S, ctx, lk, p.log2g, wlim, key0, hb, crow,
+                                               p.cap_log2, ln);
+                // V of pages 2t, 2t+1 must have landed
+                if (t == 0) {
+                    if (nst > 2)
+                        wait_vmcnt<24>();
+                    else if (nst > 1)
+                        wait_vmcnt<16>();
+                    else
+                        wait_vmcnt<0>();
+                } else if (t + 2 < nst) {
+                    wait_vmcnt<16>();
+                } else if (t + 1 < nst) {
+                    wait_vmcnt<8>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                w4_pv<RT>(st, va, va + kW4PageBytes, pop, masked, masked ? v_zero_mask(key0, hb, lk, ln) : 0u, ln);
+            }
+            wait_vmcnt<0>();
+            if (!__any(retry) || pass == 1) {                  // a second pass cannot move m again
+#ifdef VA_STAMPS
+                if (first_piece) {
+                    VA_STAMP(p, w, kg, lane, 6, VA_NOW());
+                    VA_STAMP(p, w, kg, lane, 9, (unsigned long long)nst);
+                    VA_STAMP(p, w, kg, lane, 12, (unsigned long long)(pass + 1));
+                }
+#endif
+                break;
+            }
+        }
+
+#ifdef VA_STAMPS
+        w4_epilogue<RT>(st, lds, p, kg, pl, lq, q0, g, slot, whole, vd, first_piece);
+#else
+        w4_epilogue<RT>(st, lds, p, kg, pl, lq, q0, g, slot, whole, vd, false);
+#endif
+#ifdef VA_STAMPS
+        if (first_piece)
+            VA_STAMP(p, w, kg, lane, 7, VA_NOW());
+#endif
+
+        s = base + r1;
+        base += cnt;
+        ++bg;
+    }
+#ifdef VA_STAMPS
+    VA_STAMP(p, w, kg, lane, 8, VA_NOW());
+    VA_STAMP(p, w, kg, lane, 10, (unsigned long long)npieces);
+#endif
 }
 
 // ------------------------------------------------- bf16 cache, LDS design --
@@ -2402,37 +3313,56 @@ __global__ __launch_bounds__(kThreads) void va_validate_kernel(ValidateParams p)
 
 // ------------------------------------------------------------------ host --
 
-typedef void (*launch_fn)(SplitParams, int, hipStream_t);
+// A split-KV kernel: every one takes a single SplitParams argument.  All are
+// launched through hipExtLaunchKernel, whose optional start / stop events take
+// the timestamps of the dispatch itself (va_run_timed); without events it is
+// an ordinary launch.
+struct SplitKernel {
+    const void *fn;
+    int threads;
+};
 
-template <int RTW, bool CAP, bool TOK>
-void launch_fp8_w8(SplitParams p, int grid, hipStream_t s)
+template <typename K>
+SplitKernel kref(K *fn, int threads)
 {
-    hipLaunchKernelGGL((va_split_kv_fp8_w8_kernel<RTW, CAP, TOK>), dim3(grid), dim3(512), 0, s, p);
+    return SplitKernel{reinterpret_cast<const void *>(fn), threads};
 }
 
 template <int RTW, bool CAP, bool TOK>
-void launch_bf16_w8(SplitParams p, int grid, hipStream_t s)
+SplitKernel pick_w8(bool fp8)
 {
-    hipLaunchKernelGGL((va_split_kv_bf16_w8_kernel<RTW, CAP, TOK>), dim3(grid), dim3(512), 0, s, p);
+    return fp8 ? kref(&va_split_kv_fp8_w8_kernel<RTW, CAP, TOK>, 512)
+               : kref(&va_split_kv_bf16_w8_kernel<RTW, CAP, TOK>, 512);
 }
 
-template <int RTW, bool CAP, bool TOK>
-launch_fn pick_kv(bool fp8)
+template <bool CAP>
+SplitKernel pick_fp8_w4(int row_tiles)
 {
-    return fp8 ? launch_fp8_w8<RTW, CAP, TOK> : launch_bf16_w8<RTW, CAP, TOK>;
+    switch (row_tiles) {
+    case 1: return kref(&va_split_kv_fp8_w4_kernel<1, CAP>, 256);
+    case 2: return kref(&va_split_kv_fp8_w4_kernel<2, CAP>, 256);
+    case 3: return kref(&va_split_kv_fp8_w4_kernel<3, CAP>, 256);
+    default: return kref(&va_split_kv_fp8_w4_kernel<4, CAP>, 256);
+    }
 }
 
 template <int RTW, bool CAP>
-launch_fn pick_layout(bool fp8, bool tok)
+SplitKernel pick_layout(bool fp8, bool tok)
 {
-    return tok ? pick_kv<RTW, CAP, true>(fp8) : pick_kv<RTW, CAP, false>(fp8);
+    return tok ? pick_w8<RTW, CAP, true>(fp8) : pick_w8<RTW, CAP, false>(fp8);
 }
 
-// Row tiles needed -> kernels.  Both kernels use two row groups of RTW row
-// tiles: one or two row tiles take RTW = 1, three or four RTW = 2 (a wave's
-// O^T accumulators stay at 128 registers).  Then KV dtype, softcap, layout.
-launch_fn select_launch(int row_tiles, bool fp8, bool cap, bool tok)
+// Row tiles needed -> kernel.  A paged FP8 cache runs the one-wave-per-SIMD
+// kernel with exactly the row tiles needed.  The others use two row groups of
+// RTW row tiles: one or two row tiles take RTW = 1, three or four RTW = 2 (a
+// wave's O^T accumulators stay at 128 registers).  Then KV dtype, softcap,
+// layout; absorbed MLA has its own kernel.
+SplitKernel select_kernel(int row_tiles, bool fp8, bool cap, bool tok, bool mla)
 {
+    if (mla)
+        return fp8 ? kref(&va_mla_split_kernel<kKvFp8>, 512) : kref(&va_mla_split_kernel<kKvBf16>, 512);
+    if (fp8 && !tok)
+        return cap ? pick_fp8_w4<true>(row_tiles) : pick_fp8_w4<false>(row_tiles);
     if (row_tiles <= 2)
         return cap ? pick_layout<1, true>(fp8, tok) : pick_layout<1, false>(fp8, tok);
     return cap ? pick_layout<2, true>(fp8, tok) : pick_layout<2, false>(fp8, tok);
@@ -2644,10 +3574,14 @@ struct TokArgs {                 // prefix + extend layout arguments
     const void *v_extend;
 };
 
+unsigned long long *g_stamps = nullptr;       // va_set_stamp_buffer (VA_STAMPS builds)
+size_t g_stamp_bytes = 0;
+
 va_status run_impl(va_plan_t plan, int32_t stage, const void *q, const void *k_pool, const void *v_pool,
                    const int32_t *block_table, const int32_t *cu_seqlens_q, const int32_t *seqused_k,
                    const TokArgs *tok, float softmax_scale, const float *k_descale, const float *v_descale,
-                   const float *sinks, void *out, void *workspace, size_t workspace_bytes, void *stream)
+                   const float *sinks, void *out, void *workspace, size_t workspace_bytes, void *stream,
+                   hipEvent_t main_start = nullptr, hipEvent_t main_stop = nullptr)
 {
     if (!plan)
         return VA_ERR_INVALID_ARG;
@@ -2735,17 +3669,14 @@ va_status run_impl(va_plan_t plan, int32_t stage, const void *q, const void *k_p
         sp.vext = tok ? static_cast<const uint8_t *>(tok->v_extend) : nullptr;
         sp.num_indices = tok ? tok->num_kv_indices : 0;
         sp.num_rows = pr.num_blocks * pr.page_size;
-        if (plan->mla) {
-            if (pr.kv_dtype == VA_DT_FP8_E4M3FN)
-                hipLaunchKernelGGL(va_mla_split_kernel<kKvFp8>, dim3(plan->grid), dim3(512), 0, s, sp);
-            else
-                hipLaunchKernelGGL(va_mla_split_kernel<kKvBf16>, dim3(plan->grid), dim3(512), 0, s, sp);
-        } else {
-            launch_fn fn = select_launch(plan->rt, pr.kv_dtype == VA_DT_FP8_E4M3FN, pr.softcap > 0.f,
-                                         tok != nullptr);
-            fn(sp, plan->grid, s);
-        }
-        if (hipGetLastError() != hipSuccess)
+        sp.stamps = g_stamp_bytes >= (size_t)plan->grid * 4 * kStampSlots * sizeof(unsigned long long) ? g_stamps
+                                                                                                 : nullptr;
+        const SplitKernel k = select_kernel(plan->rt, pr.kv_dtype == VA_DT_FP8_E4M3FN, pr.softcap > 0.f,
+                                            tok != nullptr, plan->mla);
+        void *args[] = {&sp};
+        if (hipExtLaunchKernel(k.fn, dim3(plan->grid), dim3(k.threads), args, 0, s, main_start, main_stop, 0) !=
+                hipSuccess ||
+            hipGetLastError() != hipSuccess)
             return VA_ERR_HIP;
     }
     if (stage == VA_STAGE_ALL || stage == VA_STAGE_MERGE) {
@@ -2806,6 +3737,32 @@ va_status va_run_prefix_extend(va_plan_t plan, int32_t stage, const void *q, con
     const TokArgs tok = {kv_indptr, kv_indices, num_kv_indices, k_extend, v_extend};
     return run_impl(plan, stage, q, k_buffer, v_buffer, nullptr, cu_seqlens_q, nullptr, &tok, softmax_scale,
                     k_descale, v_descale, sinks, out, workspace, workspace_bytes, stream);
+}
+
+va_status va_run_timed(va_plan_t plan, const void *q, const void *k_pool, const void *v_pool,
+                       const int32_t *block_table, const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                       float softmax_scale, const float *k_descale, const float *v_descale, const float *sinks,
+                       void *out, void *workspace, size_t workspace_bytes, void *stream, void *main_start,
+                       void *main_stop)
+{
+    if (!main_start || !main_stop)
+        return VA_ERR_INVALID_ARG;
+    return run_impl(plan, VA_STAGE_ALL, q, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k, nullptr,
+                    softmax_scale, k_descale, v_descale, sinks, out, workspace, workspace_bytes, stream,
+                    reinterpret_cast<hipEvent_t>(main_start), reinterpret_cast<hipEvent_t>(main_stop));
+}
+
+va_status va_set_stamp_buffer(void *buffer, size_t bytes)
+{
+#ifdef VA_STAMPS
+    g_stamps = static_cast<unsigned long long *>(buffer);
+    g_stamp_bytes = buffer ? bytes : 0;
+    return VA_OK;
+#else
+    (void)buffer;
+    (void)bytes;
+    return VA_ERR_UNSUPPORTED;
+#endif
 }
 
 va_status va_run(va_plan_t plan, const void *q, const void *k_pool, const void *v_pool,

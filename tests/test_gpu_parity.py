@@ -120,6 +120,24 @@ def test_segment_markers_expose_a_dropped_or_doubled_piece():
     check_problem(p, force_grid=37)
 
 
+@pytest.mark.parametrize("where", ["late", "first", "last"])
+def test_logit_spike_far_above_the_first_keys(where):
+    # One key row is 16 * sign(q) of query row (token 0, head 0): that row's
+    # logit there is about 200 (natural units) above the others, far beyond the
+    # FP8 kernel's accumulation headroom (64 in log2 units above the first keys
+    # a row sees).  A spike after the first step makes the kernel run the
+    # piece's page loop again from the new maximum; other heads see logits of
+    # about +-16 from the same key.  Every row must still match the oracle.
+    p = va_inputs.custom([4, 2], [6000, 3000], 16, 1, "fp8", seed=50, poison=False)
+    q0 = p.q.view(np.uint16)[0, 0].astype(np.uint32) << 16
+    sign = np.where(q0.view(np.float32) < 0, -1.0, 1.0)
+    spike = torch.from_numpy((16.0 * sign).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    key = {"late": 5000, "first": 3, "last": 5995}[where]
+    p.k[p.block_table[0, key // 16], key % 16, 0] = spike
+    for grid in (0, 7):
+        check_problem(p, force_grid=grid)
+
+
 def test_q_len_zero_rows_untouched_and_others_correct():
     p = va_inputs.custom([0, 4, 0, 2], [100, 3000, 50, 20], 8, 1, "fp8", seed=48)
     check_problem(p)
