@@ -233,6 +233,26 @@ va_status va_run_timed(va_plan_t plan, const void *q, const void *k_pool, const 
                        void *stream, void *main_start, void *main_stop);
 
 /*
+ * va_run_ex (stage VA_STAGE_ALL) with no workspace argument and no device
+ * allocation, for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  The workspace is a fixed 80 MiB array in the library's own
+ * device memory (one per device the library runs on, held until the process
+ * ends), enough for every plan at the default grid (one workgroup per CU);
+ * a plan whose va_plan_workspace_bytes exceeds it gets VA_ERR_WORKSPACE.  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); the array's device address is looked up once per device, on the
+ * first call with that device current.  Every call on a device shares that
+ * device's array, so calls that overlap in time on one device (other streams,
+ * other threads) race on it and give undefined results; serialise them.
+ * Paged-layout plans only.  Other arguments and errors as va_run_ex.
+ */
+va_status va_run_noalloc(va_plan_t plan, const void *q, const void *k_pool, const void *v_pool,
+                         const int32_t *block_table, const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                         float softmax_scale, const float *k_descale, const float *v_descale,
+                         const float *sinks, void *out, void *stream);
+
+/*
  * Diagnostic.  A library compiled with -DVA_STAMPS records, for every wave of
  * the FP8 paged main kernel, the GPU's constant 100 MHz clock at the phase
  * boundaries of its first piece (work located, Q landed, Q operands loaded,

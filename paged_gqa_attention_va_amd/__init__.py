@@ -31,7 +31,8 @@ VA_BAD_CU_SEQLENS_Q, VA_BAD_Q_LEN, VA_BAD_SEQUSED_K, VA_BAD_Q_GT_K, VA_BAD_PAGE 
 
 EXPORTED = ("va_plan", "va_plan_workspace_bytes", "va_plan_grid", "va_run", "va_run_ex",
             "va_plan_destroy", "va_status_str", "va_fp8_to_bf16", "va_spec_block_table",
-            "va_validate", "va_run_prefix_extend", "va_run_timed", "va_set_stamp_buffer")
+            "va_validate", "va_run_prefix_extend", "va_run_timed", "va_set_stamp_buffer",
+            "va_run_noalloc")
 
 _lib = None
 
@@ -94,6 +95,8 @@ def library(path: str = LIB_PATH):
     lib.va_run_timed.argtypes = run_args[:10] + [P] + run_args[10:] + [P, P]
     lib.va_set_stamp_buffer.restype = ctypes.c_int
     lib.va_set_stamp_buffer.argtypes = [P, ctypes.c_size_t]
+    lib.va_run_noalloc.restype = ctypes.c_int
+    lib.va_run_noalloc.argtypes = run_args[:10] + [P, P, P]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -295,6 +298,33 @@ class Plan:
             ctypes.c_size_t(workspace.numel() * workspace.element_size()), ctypes.c_void_p(sptr),
             ctypes.c_void_p(main_start), ctypes.c_void_p(main_stop))
         _check(st, "va_run_timed")
+        return out
+
+    def run_noalloc(self, q, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k, softmax_scale: float,
+                    k_descale=None, v_descale=None, out=None, stream=None, sinks=None):
+        """Enqueue the attention through va_run_noalloc (the library's own scratch
+        instead of a workspace; calls on one device must not overlap)."""
+        import torch
+        self._check_tensors(q, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k, k_descale, v_descale)
+        oshape = (q.shape[0], q.shape[1], self.v_head_dim)
+        if out is None:
+            out = torch.empty(oshape, dtype=torch.bfloat16, device=q.device)
+        if out.dtype != torch.bfloat16 or tuple(out.shape) != oshape or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous bf16 tensor of shape {oshape}")
+        if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != self.problem.num_q_heads
+                                  or not sinks.is_cuda or not sinks.is_contiguous()):
+            raise ValueError("sinks must be a contiguous float32 device tensor with num_q_heads elements")
+        _same_device(q.device, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k, k_descale, v_descale,
+                     sinks, out)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        st = self._lib.va_run_noalloc(
+            self._h, ptr(q), ptr(k_pool), ptr(v_pool), ptr(block_table), ptr(cu_seqlens_q), ptr(seqused_k),
+            ctypes.c_float(softmax_scale), ptr(k_descale), ptr(v_descale), ptr(sinks), ptr(out),
+            ctypes.c_void_p(sptr))
+        _check(st, "va_run_noalloc")
         return out
 
     def validate(self, block_table, cu_seqlens_q, seqused_k, result=None, stream=None):

@@ -48,6 +48,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 
 #include "va.h"
@@ -3712,6 +3713,38 @@ va_status run_impl(va_plan_t plan, int32_t stage, const void *q, const void *k_p
     return VA_OK;
 }
 
+// ------------------------------------------------ no-allocation entry point --
+//
+// va_run_noalloc runs the same kernels with a workspace that lives in this
+// library's own device memory: the file-scope array `scratch` (each device
+// that loads the library holds one copy until the process ends).  In host code
+// the name `scratch` is only a stand-in for the symbol, so the array's device
+// address is looked up once per device with hipGetSymbolAddress and kept; only
+// that address is ever passed to a kernel.  The kernels need no zeroed
+// workspace: every word they read in it was written earlier in the same call.
+constexpr size_t kScratchBytes = (size_t)80 << 20;
+__device__ __align__(256) static unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+va_status scratch_address(void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return VA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return VA_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return VA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -3774,6 +3807,23 @@ va_status va_run(va_plan_t plan, const void *q, const void *k_pool, const void *
     return va_run_ex(plan, VA_STAGE_ALL, q, k_pool, v_pool, block_table, cu_seqlens_q,
                      seqused_k, softmax_scale, k_descale, v_descale, nullptr, out, workspace,
                      workspace_bytes, stream);
+}
+
+va_status va_run_noalloc(va_plan_t plan, const void *q, const void *k_pool, const void *v_pool,
+                         const int32_t *block_table, const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                         float softmax_scale, const float *k_descale, const float *v_descale,
+                         const float *sinks, void *out, void *stream)
+{
+    if (!plan)
+        return VA_ERR_INVALID_ARG;
+    if (plan->ws_bytes > kScratchBytes)
+        return VA_ERR_WORKSPACE;                       // beyond the library's scratch
+    void *ws = nullptr;
+    const va_status st = scratch_address(&ws);
+    if (st != VA_OK)
+        return st;
+    return run_impl(plan, VA_STAGE_ALL, q, k_pool, v_pool, block_table, cu_seqlens_q, seqused_k, nullptr,
+                    softmax_scale, k_descale, v_descale, sinks, out, ws, kScratchBytes, stream);
 }
 
 va_status va_validate(va_plan_t plan, const int32_t *block_table, const int32_t *cu_seqlens_q,
