@@ -106,6 +106,8 @@ def attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, kv_dtype: str,
     alternative build of the oracle (tests that plant mistakes use this).
     window_left (-1 = none), softcap (0 = none) and sinks ([Hq] logits or None)
     select the optional sliding window, logit softcap and attention sinks.
+    Raises ValueError when a sequence has more query tokens than keys
+    (q_len > seqused_k), a call outside the operation's domain.
     """
     if lib is None:
         lib = _load()
@@ -152,6 +154,9 @@ def attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, kv_dtype: str,
         int(window_left), float(softcap), _ptr(sk_arr),
         _ptr(seg_start), _ptr(seg_ptr), _ptr(rows_arr), n, _ptr(out), _ptr(lse),
         default_threads() if threads is None else int(threads))
+    if st == -4:
+        raise ValueError("a sequence has more query tokens than keys (q_len > seqused_k): "
+                         "seqused_k counts the verify tokens, so the call has no defined result")
     if st != 0:
         raise RuntimeError(f"va_oracle_attn failed with status {st}")
     return out, lse

@@ -320,7 +320,11 @@ static void *worker(void *vp)
 
 /*
  * Exported entry.  Returns 0 on success, -1 on a row that belongs to no
- * sequence, -2 on allocation failure, -3 on bad arguments.
+ * sequence, -2 on allocation failure, -3 on bad arguments, -4 when a
+ * sequence has more query tokens than keys (q_len > seqused_k).  seqused_k
+ * counts the verify tokens themselves (the PR #36330 summary page's gate
+ * passes seq_lens + max_q_len), so such a call is outside the operation's
+ * domain and has no defined result.
  * window_left: -1 or >= 0; softcap: 0 or > 0; sinks: NULL or [num_q_heads].
  */
 int va_oracle_attn_ex(const uint16_t *q, const void *k_pool, const void *v_pool,
@@ -347,6 +351,9 @@ int va_oracle_attn_ex(const uint16_t *q, const void *k_pool, const void *v_pool,
         return -3;
     if (window_left < -1 || !(softcap >= 0.0))
         return -3;
+    for (b = 0; b < num_seqs; ++b)
+        if (cu_seqlens_q[b + 1] - cu_seqlens_q[b] > seqused_k[b])
+            return -4;
     p.q = q; p.k_pool = k_pool; p.v_pool = v_pool; p.kv_is_fp8 = kv_is_fp8;
     p.block_table = block_table; p.bt_stride = bt_stride;
     p.cu_seqlens_q = cu_seqlens_q; p.seqused_k = seqused_k;

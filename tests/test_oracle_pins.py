@@ -200,6 +200,21 @@ def test_first_query_of_full_verify_sees_exactly_one_key():
             assert np.array_equal(out[q0, h], p.v_descale * V[page, 0, 0])
 
 
+def test_query_tokens_beyond_the_keys_are_refused():
+    # seqused_k counts the verify tokens themselves, so a sequence with more
+    # query tokens than keys is outside the operation's domain
+    p = small_problem(None, [4, 3], [20, 3], 8, 1, seed=23)
+    oracle.attn_problem(p)                         # q_len == seqused_k is in the domain
+    p.seqused_k[1] = 2                             # 3 query tokens, 2 keys
+    with pytest.raises(ValueError):
+        oracle.attn_problem(p)
+    with pytest.raises(ValueError):                # also when only other rows are asked for
+        oracle.attn_problem(p, rows=[0, 1])
+    p.seqused_k[1] = 0
+    with pytest.raises(ValueError):
+        oracle.attn_problem(p)
+
+
 def test_identical_keys_give_mean_of_visible_values():
     p = small_problem(None, [3], [50], 4, 1, seed=5)
     K = p.k
