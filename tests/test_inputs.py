@@ -55,3 +55,15 @@ def test_config3_lengths_and_descales():
     pages = np.ceil(p.seqused_k / 16).astype(int)
     used = np.concatenate([p.block_table[b, :pages[b]] for b in range(64)])
     assert np.array_equal(np.sort(used), np.arange(p.num_blocks))
+
+
+def test_sample_rows_cover_every_sequence_boundary():
+    p = va_inputs.custom([1, 3, 0, 2, 4], [20, 40, 9, 33, 70], 8, 1, "fp8", seed=4)
+    rows = va_inputs.sample_rows(p, 5, seed=2)
+    assert np.all(np.diff(rows) > 0) and rows[0] >= 0 and rows[-1] < p.total_q * 8
+    tokens = set((rows // 8).tolist())
+    cu = p.cu_seqlens_q
+    for b in range(p.num_seqs):
+        if cu[b + 1] > cu[b]:
+            assert int(cu[b]) in tokens and int(cu[b + 1]) - 1 in tokens
+    assert np.array_equal(va_inputs.sample_rows(p, 10 ** 6), np.arange(p.total_q * 8))

@@ -53,7 +53,7 @@ def test_page_ids_come_from_the_first_token_of_each_page():
 @pytest.mark.gpu
 @pytest.mark.parametrize("case", [
     ([4, 2], [1024, 769], 16, 1, "fp8"),
-    ([1, 3, 2, 4], [5000, 17, 1, 2049], 16, 1, "fp8"),
+    ([1, 3, 2, 4], [5000, 17, 2, 2049], 16, 1, "fp8"),
     ([3, 3], [700, 1300], 8, 2, "bf16"),
 ])
 def test_device_conversion_and_attention_through_it(case):
@@ -137,3 +137,33 @@ def test_graph_replay_with_new_lengths_in_place(kv_dtype):
             torch.cuda.synchronize()
             ref, _ = oracle.attn_problem(p)
             compare(as_f64(out), ref, f"{p.name} replay {rep}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_draft_extend_metadata_into_an_mla_plan(kv_dtype):
+    # The PR #30105 summary page's draft-extend path with a query/key width
+    # (576) other than the value width (512): the converted block table and
+    # lengths drive the absorbed-MLA plan, whose output rows are 512 wide.
+    import torch
+    import paged_gqa_attention_va_amd as va
+    from gpu_util import as_f64, compare
+    p = va_inputs.mla([4, 1, 3], [3000, 17, 700], 16, kv_dtype, seed=31, k_descale=0.8, v_descale=1.25,
+                      name=f"draft-extend-mla-{kv_dtype}")
+    indptr, idx = token_slots(p)
+    mbps = p.block_table.shape[1]
+    bt, sk = va.spec_block_table(torch.from_numpy(indptr).cuda(), torch.from_numpy(idx).cuda(), mbps)
+    pool = torch.from_numpy(p.k)
+    if kv_dtype == "bf16":
+        pool = pool.view(torch.int16).view(torch.bfloat16)
+    pool = pool.cuda()
+    q = torch.from_numpy(p.q.view(np.int16)).view(torch.bfloat16).cuda()
+    cu = torch.from_numpy(p.cu_seqlens_q).cuda()
+    kd = torch.tensor([p.k_descale], dtype=torch.float32, device="cuda")
+    vd = torch.tensor([p.v_descale], dtype=torch.float32, device="cuda")
+    plan = va.Plan.for_problem(p, force_grid=32)
+    out = plan.run(q, pool, pool, bt, cu, sk, p.scale, kd, vd)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (p.total_q, p.num_q_heads, va_inputs.MLA_LATENT)
+    ref, _ = oracle.attn_mla_problem(p)
+    compare(as_f64(out), ref, p.name)

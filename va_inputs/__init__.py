@@ -138,6 +138,9 @@ def custom(q_lens: Sequence[int], kv_lens: Sequence[int], num_q_heads: int,
     B = len(q_lens)
     assert B == len(kv_lens) and B >= 1
     assert num_q_heads % num_kv_heads == 0
+    if any(q > k for q, k in zip(q_lens, kv_lens)):
+        # kv_lens count the verify tokens themselves
+        raise ValueError(f"q_lens {q_lens} exceed kv_lens {kv_lens}")
     gen = torch.Generator(device="cpu")
     gen.manual_seed(int(seed))
     pages = [math.ceil(k / PAGE) for k in kv_lens]
@@ -260,15 +263,22 @@ def mla(q_lens: Sequence[int], kv_lens: Sequence[int], num_q_heads: int, kv_dtyp
 
 
 def sample_rows(p: Problem, n: int, seed: int = 0) -> np.ndarray:
-    """A seeded sample of flat output rows (q_row * Hq + head), always including
-    the first and last query token of every sampled sequence."""
+    """A seeded sample of flat output rows (q_row * Hq + head): n rows drawn
+    at random, plus, for every sequence with query tokens, one row of its
+    first query token and one of its last (each at a seeded head), so that
+    every sequence's boundaries are checked.  All rows when n covers them."""
     rng = np.random.default_rng(seed)
-    total = p.total_q * p.num_q_heads
+    hq = p.num_q_heads
+    total = p.total_q * hq
     if n >= total:
         return np.arange(total, dtype=np.int64)
     pick = set(rng.choice(total, size=n, replace=False).tolist())
-    pick.add(0)
-    pick.add(total - 1)
+    cu = np.asarray(p.cu_seqlens_q)
+    for b in range(p.num_seqs):
+        q0, q1 = int(cu[b]), int(cu[b + 1])
+        if q1 > q0:
+            pick.add(q0 * hq + int(rng.integers(hq)))
+            pick.add((q1 - 1) * hq + int(rng.integers(hq)))
     return np.array(sorted(pick), dtype=np.int64)
 
 
