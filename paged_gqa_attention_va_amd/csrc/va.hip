@@ -85,7 +85,9 @@ struct SplitParams {
                           // those two pieces of a workgroup can be split)
     float *ws_lse;        // [2 grid][rows_max]   log2-domain LSE of the scaled logits
     int32_t *ws_prefix;   // [BH + 1] exclusive prefix of page counts, [BH] = total
+    int32_t *ws_cost;     // [BH + 1] exclusive prefix of the pairs' costs (see locate)
     int32_t *ws_meta;     // [0] = workgroups in use
+    int32_t piece_cost;   // pages charged for a pair that starts inside a workgroup's range
     float scale_log2;     // softmax_scale * log2(e)
     float cap_log2;       // logit softcap * log2(e) (0 = no softcap)
     const float *sinks;   // [Hq] sink logits (natural-log units) or null
@@ -112,6 +114,7 @@ struct MergeParams {
     const void *ws_o;     // fp16 or fp32 partials, see SplitParams
     const float *ws_lse;
     const int32_t *ws_prefix;
+    const int32_t *ws_cost;
     const int32_t *ws_meta;
     uint16_t *out;
     int32_t num_seqs, hq, hkv, log2g, max_q, rows_max, total_q;
@@ -186,28 +189,40 @@ __device__ __forceinline__ floatx4_t mfma16_f8(const intx8_t &a, const intx8_t &
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-__device__ __forceinline__ int wave_sum(int x)
+// Inclusive prefix sum over the wave with DPP moves: row_shr 1, 2, 4, 8 scan
+// each row of 16 lanes, then row_bcast 15 and 31 add the totals of the rows
+// before (lanes a move does not reach take the 0 of `old`).
+__device__ __forceinline__ int wave_scan_dpp(int x)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        x += __shfl_xor(x, o);
-    return x;
-}
-
-__device__ __forceinline__ int wave_incl_scan(int x, int lane)
-{
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o);
-        if (lane >= o)
-            x += y;
-    }
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
     return x;
 }
 
 __device__ __forceinline__ float exp2_fast(float x)
 {
     return __builtin_amdgcn_exp2f(x);      // v_exp_f32; exp2(-inf) = 0
+}
+
+// Maxima of values that come out of inline assembly: written as instructions
+// so that no canonicalising v_max x, x is put in front of each operand (the
+// inputs are never NaN where these are used).
+__device__ __forceinline__ float max3f(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+__device__ __forceinline__ float max2f(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
 }
 
 __device__ __forceinline__ int uniform(int x)
@@ -446,77 +461,148 @@ struct Share {
     int total;      // pages over all (sequence, kv head) pairs
 };
 
-// Every wave runs this (no LDS, no barrier).  Total page count, the number of
-// workgroups in use, this workgroup's range, and where it starts.
+// Work split (stream-K over pages).  The (sequence, kv head) pairs are laid
+// end to end in page order; workgroup w takes an equal share of their cost.
+// A pair costs its page count, plus piece_cost pages when its first page does
+// not start a workgroup's share of an equal split by pages: such a workgroup
+// then works on two pieces, and the extra piece's epilogue and prologue take
+// about as long as piece_cost pages (with piece_cost = 0 the split is by pages
+// alone).  The cost of a pair sits before its pages: a cost position x inside
+// pair bg (cost range [C_bg, C_bg + cost_bg)) is page
+//   base_bg + max(0, x - C_bg - (cost_bg - cnt_bg))
+// of the flat page order, and workgroup w works on the pages between those of
+// cost positions w T / n and (w + 1) T / n (T = total cost, n = workgroups).
+// The merge kernel inverts the same mapping from ws_prefix and ws_cost.
+//
+// Every wave runs this (no LDS, no barrier): total page count, the number of
+// workgroups in use, this workgroup's page range, and where it starts.
+__device__ __forceinline__ bool starts_a_share(int base, int total, int n)
+{
+    // is base one of the page boundaries floor(w total / n), w = 0 .. n, of an
+    // equal split?  With r = (base n) mod total that holds iff r == 0 or
+    // r > total - n.  The quotient comes from a float estimate, corrected.
+    const int64_t bn = (int64_t)base * n;
+    int64_t w = (int64_t)((float)bn * __builtin_amdgcn_rcpf((float)total));
+    int64_t r = bn - w * total;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        if (r < 0) {
+            --w;
+            r += total;
+        }
+        if (r >= total) {
+            ++w;
+            r -= total;
+        }
+    }
+    return r == 0 || r > total - n;
+}
+
 __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix)
 {
     const int bh = p.num_seqs * p.hkv;
-    if (bh <= 64) {                                    // one pass: one count per lane
-        const int cnt = lane < bh ? pages_of(p, lane) : 0;
-        const int incl = wave_incl_scan(cnt, lane);
-        const int total = __shfl(incl, 63);
-        Share sh;
-        sh.n_eff = min(p.grid_n, max(1, total / max(1, p.min_pages)));
-        sh.total = total;
-        sh.s = (int)(((int64_t)w * total) / sh.n_eff);
-        sh.e = (int)(((int64_t)(w + 1) * total) / sh.n_eff);
-        const unsigned long long hit = __ballot(lane < bh && incl > sh.s);
-        if (hit) {
-            const int ln = __ffsll((long long)hit) - 1;
-            sh.bg = ln;
-            sh.base = __shfl(incl - cnt, ln);
-        } else {
-            sh.bg = bh;
-            sh.base = total;
+    const int C = p.piece_cost;
+    const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;   // lanes < this one
+    Share sh;
+    sh.s = sh.e = sh.base = 0;
+    sh.bg = bh;
+    // One chunk of up to 64 pairs, lane = pair: page counts, their prefix, the
+    // pairs whose start falls inside a share and the prefix of the costs; then
+    // the pairs holding the cost positions cs and ce of this workgroup's share.
+    // With at most 64 pairs everything comes from one load of the counts.
+    auto chunk = [&](int c0, int cnt, int incl, int base, int cbase, int total, int n, int64_t cs, int64_t ce,
+                     bool &found_s, bool &found_e) {
+        const int bg = c0 + lane;
+        const int pb = base + incl - cnt;              // this lane's pair: first page
+        const bool inside = C > 0 && bg < bh && bg > 0 && cnt > 0 && !starts_a_share(pb, total, n);
+        const unsigned long long im = __ballot(inside);
+        const int extra = inside ? C : 0;              // cost beyond the pages
+        const int cb = cbase + (pb - base) + C * __builtin_popcountll(im & below);   // first cost position
+        const int cend = cb + cnt + extra;
+        if (write_prefix && bg < bh) {
+            p.ws_prefix[bg] = pb;
+            p.ws_cost[bg] = cb;
         }
-        if (write_prefix) {
-            if (lane < bh)
-                p.ws_prefix[lane] = incl - cnt;
-            if (lane == 0) {
-                p.ws_prefix[bh] = total;
-                p.ws_meta[0] = sh.n_eff;
+        if (!found_s) {
+            const unsigned long long hit = __ballot(bg < bh && cend > cs);
+            if (hit) {
+                const int ln = __ffsll((long long)hit) - 1;
+                const int pg = pb + (int)max((int64_t)0, cs - cb - extra);
+                sh.bg = c0 + ln;
+                sh.base = __builtin_amdgcn_readlane(pb, ln);
+                sh.s = __builtin_amdgcn_readlane(pg, ln);
+                found_s = true;
             }
         }
+        if (!found_e) {
+            const unsigned long long hit = __ballot(bg < bh && cend > ce);
+            if (hit) {
+                const int ln = __ffsll((long long)hit) - 1;
+                const int pg = pb + (int)max((int64_t)0, ce - cb - extra);
+                sh.e = __builtin_amdgcn_readlane(pg, ln);
+                found_e = true;
+            }
+        }
+        return C * __builtin_popcountll(im);           // the chunk's cost beyond its pages
+    };
+    auto finish = [&](int total, int n, int64_t T) {
+        if (write_prefix && lane == 0) {
+            p.ws_prefix[bh] = total;
+            p.ws_cost[bh] = (int)T;
+            p.ws_meta[0] = n;
+        }
+    };
+    if (bh <= 64) {
+        const int cnt = lane < bh ? pages_of(p, lane) : 0;
+        const int incl = wave_scan_dpp(cnt);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        const int n = min(p.grid_n, max(1, total / max(1, p.min_pages)));
+        sh.n_eff = n;
+        sh.total = total;
+        const bool inside = C > 0 && lane < bh && lane > 0 && cnt > 0 && !starts_a_share(incl - cnt, total, n);
+        const int64_t T = total + (int64_t)C * __builtin_popcountll(__ballot(inside));
+        const int64_t cs = ((int64_t)w * T) / n, ce = ((int64_t)(w + 1) * T) / n;
+        sh.s = sh.e = sh.base = total;
+        bool found_s = false, found_e = false;
+        chunk(0, cnt, incl, 0, 0, total, n, cs, ce, found_s, found_e);
+        finish(total, n, T);
         return sh;
     }
     int total = 0;
     for (int c0 = 0; c0 < bh; c0 += 64) {
         const int bg = c0 + lane;
-        const int cnt = bg < bh ? pages_of(p, bg) : 0;
-        total += wave_sum(cnt);
+        total += __builtin_amdgcn_readlane(wave_scan_dpp(bg < bh ? pages_of(p, bg) : 0), 63);
     }
-    Share sh;
-    sh.n_eff = min(p.grid_n, max(1, total / max(1, p.min_pages)));
+    const int n = min(p.grid_n, max(1, total / max(1, p.min_pages)));
+    sh.n_eff = n;
     sh.total = total;
-    sh.s = (int)(((int64_t)w * total) / sh.n_eff);
-    sh.e = (int)(((int64_t)(w + 1) * total) / sh.n_eff);
-    sh.bg = bh;
-    sh.base = total;
-    bool found = false;
-    int base = 0;
+    int64_t T = total;
+    if (C > 0) {
+        int base = 0;
+        for (int c0 = 0; c0 < bh; c0 += 64) {
+            const int bg = c0 + lane;
+            const int cnt = bg < bh ? pages_of(p, bg) : 0;
+            const int incl = wave_scan_dpp(cnt);
+            const bool inside = bg < bh && bg > 0 && cnt > 0 && !starts_a_share(base + incl - cnt, total, n);
+            T += (int64_t)C * __builtin_popcountll(__ballot(inside));
+            base += __builtin_amdgcn_readlane(incl, 63);
+        }
+    }
+    const int64_t cs = ((int64_t)w * T) / n, ce = ((int64_t)(w + 1) * T) / n;
+    sh.s = sh.e = sh.base = total;
+    bool found_s = false, found_e = false;
+    int base = 0, cbase = 0;
     for (int c0 = 0; c0 < bh; c0 += 64) {
         const int bg = c0 + lane;
         const int cnt = bg < bh ? pages_of(p, bg) : 0;
-        const int incl = wave_incl_scan(cnt, lane);
-        if (write_prefix && bg < bh)
-            p.ws_prefix[bg] = base + incl - cnt;
-        if (!found) {
-            const unsigned long long hit = __ballot(bg < bh && base + incl > sh.s);
-            if (hit) {
-                const int ln = __ffsll((long long)hit) - 1;
-                sh.bg = c0 + ln;
-                sh.base = base + __shfl(incl - cnt, ln);
-                found = true;
-                if (!write_prefix)
-                    break;
-            }
-        }
-        base += __shfl(incl, 63);
+        const int incl = wave_scan_dpp(cnt);
+        const int ctotal = __builtin_amdgcn_readlane(incl, 63);
+        cbase += ctotal + chunk(c0, cnt, incl, base, cbase, total, n, cs, ce, found_s, found_e);
+        base += ctotal;
+        if (found_s && found_e && !write_prefix)
+            break;
     }
-    if (write_prefix && lane == 0) {
-        p.ws_prefix[bh] = total;
-        p.ws_meta[0] = sh.n_eff;
-    }
+    finish(total, n, T);
     return sh;
 }
 
@@ -583,6 +669,24 @@ __device__ __forceinline__ void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n that is a multiple of 8 in [0, 40]
+// (a smaller n only waits longer).
+__device__ __forceinline__ void wait_vmcnt_x8(int n)
+{
+    if (n >= 40)
+        wait_vmcnt<40>();
+    else if (n >= 32)
+        wait_vmcnt<32>();
+    else if (n >= 24)
+        wait_vmcnt<24>();
+    else if (n >= 16)
+        wait_vmcnt<16>();
+    else if (n >= 8)
+        wait_vmcnt<8>();
+    else
+        wait_vmcnt<0>();
 }
 
 // One ring stage = one step (two pages) of one kv head, 16 KiB:
@@ -1504,36 +1608,178 @@ __device__ __forceinline__ void w4_softmax(RowState<RT> &st, bool &retry, bf16x8
     }
 }
 
+// QK^T and softmax of an unmasked step without a softcap, with the row tiles
+// pipelined: the MFMAs of row tile rt are issued between the vector
+// instructions of row tile rt - 1's softmax, so that with one wave per SIMD the
+// matrix unit and the vector unit work at the same time (in program order a
+// run of MFMAs would hold the wave until the last one issues).  The softmax is
+// computed optimistically from the current reference m: every p and l is what
+// w4_softmax would produce unless some logit of the step exceeds m + kTauW4.
+// That is tested per lane on the way; if any lane finds it, the l of the step
+// is rolled back and w4_softmax redoes the step (it moves m and sets `retry`),
+// so the result is w4_softmax's in every case.  The first step of a pass is
+// such a case for each row (m starts at -inf).
+//
+// One pair of QK MFMAs (the two key pages of the step) of one (kc, part) group
+// of row tile rt.  Same hazard handling as W4QkGroup; w4_qk_pad gives the 19
+// wait states after the last pair of a row tile, before its S is read.
+__device__ __forceinline__ void w4_qk_pair_first(floatx4_t &s0, floatx4_t &s1, const intx8_t &k0,
+                                                 const intx8_t &k1, const intx8_t &q)
+{
+    asm volatile("s_nop 1\n\t"
+                 "v_mfma_f32_16x16x128_f8f6f4 %0, %2, %4, 0\n\t"
+                 "v_mfma_f32_16x16x128_f8f6f4 %1, %3, %4, 0"
+                 : "=&v"(s0), "=&v"(s1)
+                 : "v"(k0), "v"(k1), "v"(q));
+}
+
+__device__ __forceinline__ void w4_qk_pair_acc(floatx4_t &s0, floatx4_t &s1, const intx8_t &k0,
+                                               const intx8_t &k1, const intx8_t &q)
+{
+    asm volatile("s_nop 1\n\t"
+                 "v_mfma_f32_16x16x128_f8f6f4 %0, %2, %4, %0\n\t"
+                 "v_mfma_f32_16x16x128_f8f6f4 %1, %3, %4, %1"
+                 : "+v"(s0), "+v"(s1)
+                 : "v"(k0), "v"(k1), "v"(q));
+}
+
+__device__ __forceinline__ void w4_qk_pad(floatx4_t &s0, floatx4_t &s1)
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(s0), "+v"(s1));
+}
+
+// after_k(a) is called for a = 0, 1 once every K read of the step has
+// returned (the K slots may then be refilled), in the places of row tile 0,
+// which have no softmax work beside them.
+template <int RT, typename AfterK>
+__device__ __forceinline__ void w4_qk_softmax(RowState<RT> &st, bool &retry, bf16x8_t (&pop)[RT],
+                                              floatx4_t (&S)[2][RT], const unsigned char *ka,
+                                              const unsigned char *kb, const intx8_t (&qop)[RT][2][2],
+                                              int ctx, int lk, int log2g, uint32_t wlim, int key0,
+                                              const float (&c)[RT], int lane, AfterK after_k)
+{
+    const int n = lane & 15, j = lane >> 4;
+    intx8_t kop[2][2];                                    // [kc][page]
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const unsigned char *kp = a ? kb : ka;
+            const int c0 = 8 * kc + 2 * j;
+            const uint4 lo4 = *reinterpret_cast<const uint4 *>(kp + 256 * n + 16 * (c0 ^ n));
+            const uint4 hi4 = *reinterpret_cast<const uint4 *>(kp + 256 * n + 16 * ((c0 + 1) ^ n));
+            kop[kc][a] = intx8_t{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
+                                 (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+        }
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float lold[RT], mref[RT], pk[RT][2];
+    uint32_t w[RT][4];
+    bool need = false;
+    // softmax of row tile rt, in four parts of similar issue time
+    auto sm_part = [&](int rt, int part) {
+        const floatx4_t &s0 = S[0][rt];
+        const floatx4_t &s1 = S[1][rt];
+        auto p_of = [&](float x) { return exp2_fast(__builtin_fmaf(x, c[rt], -mref[rt])); };
+        // each part ends in an empty statement that takes its results, which keeps
+        // the part's instructions between the MFMAs it was written between
+        if (part == 0) {
+            lold[rt] = st.l[rt];
+            mref[rt] = st.m[rt] == -INFINITY ? 0.0f : st.m[rt];
+            const float lmax = max3f(max3f(s0[0], s0[1], s0[2]), max3f(s0[3], s1[0], s1[1]), max2f(s1[2], s1[3]));
+            need |= lmax * c[rt] > st.m[rt] + kTauW4;
+            asm volatile("" : "+v"(mref[rt]));
+        } else if (part == 1) {
+            const float p0 = p_of(s0[0]), p1 = p_of(s0[1]);
+            pk[rt][0] = p_of(s0[2]);
+            w[rt][0] = pack_bf16x2(p0, p1);
+            st.l[rt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[rt][0]), ones, st.l[rt], false);
+            asm volatile("" : "+v"(w[rt][0]), "+v"(st.l[rt]), "+v"(pk[rt][0]));
+        } else if (part == 2) {
+            const float p3 = p_of(s0[3]);
+            pk[rt][1] = p_of(s1[0]);
+            const float p5 = p_of(s1[1]);
+            w[rt][1] = pack_bf16x2(pk[rt][0], p3);
+            st.l[rt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[rt][1]), ones, st.l[rt], false);
+            pk[rt][0] = p5;
+            asm volatile("" : "+v"(w[rt][1]), "+v"(st.l[rt]), "+v"(pk[rt][0]), "+v"(pk[rt][1]));
+        } else {
+            const float p6 = p_of(s1[2]), p7 = p_of(s1[3]);
+            w[rt][2] = pack_bf16x2(pk[rt][1], pk[rt][0]);
+            w[rt][3] = pack_bf16x2(p6, p7);
+            st.l[rt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[rt][2]), ones, st.l[rt], false);
+            st.l[rt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[rt][3]), ones, st.l[rt], false);
+            asm volatile("" : "+v"(w[rt][2]), "+v"(w[rt][3]), "+v"(st.l[rt]));
+            pop[rt] = __builtin_bit_cast(bf16x8_t, make_uint4(w[rt][0], w[rt][1], w[rt][2], w[rt][3]));
+        }
+    };
+#pragma unroll
+    for (int rt = 0; rt <= RT; ++rt) {
+#pragma unroll
+        for (int part = 0; part < 4; ++part) {
+            if (rt < RT) {
+                const int kc = part >> 1, h = part & 1;
+                if (part == 0)
+                    w4_qk_pair_first(S[0][rt], S[1][rt], kop[0][0], kop[0][1], qop[rt][0][0]);
+                else
+                    w4_qk_pair_acc(S[0][rt], S[1][rt], kop[kc][0], kop[kc][1], qop[rt][kc][h]);
+            }
+            if (rt > 0 && part == 0)
+                w4_qk_pad(S[0][rt - 1], S[1][rt - 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (rt > 0) {
+                sm_part(rt - 1, part);
+            } else if (part < 2) {
+                if (part == 0)
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                after_k(part);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if (__any(need)) {                                    // rare: redo the step, moving m
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            st.l[rt] = lold[rt];
+        w4_softmax<RT, false, false>(st, retry, pop, S, ctx, lk, log2g, wlim, key0, true, c, 0.f, lane);
+    }
+}
+
 // PV of a step: O^T += V^T P^T, as pv_lds, with the V pages of the step in two
 // slots (va, vb) whose rows are stored unswizzled (chunk c of key row n at
-// 256 n + 16 c): lane (m, j) reads dims 16 m + 8 h .. + 7 of key rows 4 j + e,
-// so every read of a step is one lane base plus an immediate.
-template <int RT>
+// 256 n + 16 c): lane (m, j) reads dims 16 m .. + 15 of key rows 4 j + e, all
+// of the step's V in eight 16-byte reads at one lane base plus immediates.
+// after_v() is called once they have returned (the V slots may then be
+// refilled).
+template <int RT, typename AfterV>
 __device__ __forceinline__ void w4_pv(RowState<RT> &st, const unsigned char *va, const unsigned char *vb,
-                                      const bf16x8_t (&pop)[RT], bool masked, uint32_t zmask, int lane)
+                                      const bf16x8_t (&pop)[RT], bool masked, uint32_t zmask, int lane,
+                                      AfterV after_v)
 {
     const int m = lane & 15, j = lane >> 4;
     const int lo = 1024 * j + 16 * m;
+    uint4 vv[8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint2 vv[8];
+    for (int e = 0; e < 8; ++e)
+        vv[e] = *reinterpret_cast<const uint4 *>((e >> 2 ? vb : va) + lo + 256 * (e & 3));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    after_v();
+    if (masked) {                                      // wave-uniform
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            vv[e] = *reinterpret_cast<const uint2 *>((e >> 2 ? vb : va) + lo + 256 * (e & 3) + 8 * h);
-        if (masked) {                                  // wave-uniform
+            if (zmask & (1u << e))
+                vv[e] = make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (zmask & (1u << e))
-                    vv[e] = make_uint2(0, 0);
-        }
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
-            const int q = 2 * h + qq;
+            const int q = 2 * h + qq;                  // dims 16 m + 4 q .. + 3
             uint32_t A[4][4];
 #pragma unroll
             for (int kp = 0; kp < 4; ++kp) {
-                const uint32_t X = qq ? vv[2 * kp].y : vv[2 * kp].x;
-                const uint32_t Y = qq ? vv[2 * kp + 1].y : vv[2 * kp + 1].x;
+                const uint4 &x4 = vv[2 * kp], &y4 = vv[2 * kp + 1];
+                const uint32_t X = h ? (qq ? x4.w : x4.z) : (qq ? x4.y : x4.x);
+                const uint32_t Y = h ? (qq ? y4.w : y4.z) : (qq ? y4.y : y4.x);
                 const uint32_t lo2 = byte_perm(Y, X, 0x05010400u);   // X0 Y0 X1 Y1
                 const uint32_t hi2 = byte_perm(Y, X, 0x07030602u);   // X2 Y2 X3 Y3
                 A[0][kp] = fp8x2_lo_to_bf16x2(lo2);
@@ -1816,7 +2062,6 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
         const int npairs = (p1 - p0 + 1) >> 1;
         const int pr0 = (int)(((int64_t)kg * npairs) / NG);
         const int nst = (int)(((int64_t)(kg + 1) * npairs) / NG) - pr0;   // steps of this wave
-        const int npg = 2 * nst;
         const int lp0 = p0 + 2 * pr0;
         const int32_t *btrow = p.bt + (int64_t)b * p.mbps;
         const uint8_t *kpool = p.k + (int64_t)g * kHeadDim;
@@ -1945,97 +2190,81 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
                     st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             }
             bool retry = false;
-            // block-table entries of the copies at the top of step t: eK for K of pages
-            // 2t + 4, 2t + 5, eV for V of pages 2t + 2, 2t + 3 (the K copies of the step
-            // before), eN for K of pages 2t + 6, 2t + 7, loaded a step ahead (entry()
-            // clamps to the piece, so the loads past its end are harmless)
+            // Copies: the prologue issues K(0), V(0), K(1), K(2), V(1) (X(s) = the two
+            // pages of step s); step t then refills its own slots as soon as it has
+            // read them: K(t + 3) once its K reads have returned, V(t + 2) once its V
+            // reads have.  Block-table entries at the start of step t: eK for K(t + 3)
+            // (pages 2t + 6, 2t + 7), eV for V(t + 2) (pages 2t + 4, 2t + 5), eN for
+            // the next step's K (pages 2t + 8, 2t + 9), loaded a step ahead (entry()
+            // clamps to the piece, so the loads past its end are harmless).
             int eK0 = entry(6), eK1 = entry(7), eV0 = e4, eV1 = e5;
             int eN0 = entry(8), eN1 = entry(9);
             int ks = 0, vs = 0;                                // K / V slots of local page 2t
             for (int t = 0; t < nst; ++t) {
-                // K of pages 2t, 2t+1 must have landed; the copies issued after them may
-                // not (their count follows from the fixed order of the copies)
-                if (t == 0) {
-                    if (nst > 2)
-                        wait_vmcnt<32>();
-                    else if (nst > 1)
-                        wait_vmcnt<24>();
-                    else
-                        wait_vmcnt<8>();
-                } else if (t == 1) {
-                    if (nst > 2)
-                        wait_vmcnt<16>();
-                    else
-                        wait_vmcnt<8>();
-                } else if (t + 1 < nst) {
-                    wait_vmcnt<24>();
-                } else {
-                    wait_vmcnt<16>();
-                }
+                // K(t) must have landed.  Issued after it so far (in issue order, each
+                // 8 copies): at t = 0, 1: V(t), K(t+1) and V(t+1) if t+1 < nst, K(t+2)
+                // if t+2 < nst; from t = 2 on also V(t-1)
+                wait_vmcnt_x8(8 * ((t >= 2 ? 2 : 1) + 2 * (t + 1 < nst) + (t + 2 < nst)));
 #ifdef VA_STAMPS
                 if (first_piece && pass == 0 && t <= 1)
                     VA_STAMP(p, w, kg, lane, 4 + t, VA_NOW());
 #endif
-                if (t >= 1) {                                  // into the slots of step t - 1
-                    const int kslot = ks == 0 ? kW4KSlots - 2 : ks - 2;
-                    const int vslot = vs == 0 ? kW4VSlots - 2 : vs - 2;
-                    if (t + 2 < nst) {
-                        issue_k(eK0, kslot);
-                        issue_k(eK1, kslot + 1);
-                    }
-                    if (t + 1 < nst) {
-                        issue_v(eV0, vslot);
-                        issue_v(eV1, vslot + 1);
-                    }
-                    eV0 = eK0;
-                    eV1 = eK1;
-                    eK0 = eN0;
-                    eK1 = eN1;
-                    eN0 = entry(2 * t + 8);                    // for the K copies two steps on
-                    eN1 = entry(2 * t + 9);
-                }
+                const int kslot = ks, vslot = vs;
                 const unsigned char *ka = ring + ks * kW4PageBytes;
                 const unsigned char *va = ring + kW4VBase + vs * kW4PageBytes;
                 ks = ks + 2 == kW4KSlots ? 0 : ks + 2;
                 vs = vs + 2 == kW4VSlots ? 0 : vs + 2;
+                auto after_k = [&](int a) {                    // K(t + 3) into this step's K slots
+                    if (t + 3 < nst)
+                        issue_k(a ? eK1 : eK0, kslot + a);
+                };
+                auto after_v = [&]() {                         // V(t + 2) into this step's V slots
+                    if (t + 2 < nst) {
+                        issue_v(eV0, vslot);
+                        issue_v(eV1, vslot + 1);
+                    }
+                };
                 // lane-derived LDS offsets are rederived each step from an
                 // opaque lane index: hoisted out of the loop they would hold
                 // registers next to the Q operands
                 int ln = lane;
                 asm volatile("" : "+v"(ln));
                 floatx4_t S[2][RT];
-                w4_qk<RT>(S, ka, ka + kW4PageBytes, qop, ln);
-                __builtin_amdgcn_sched_barrier(0);
                 const int pa = lp0 + 2 * t;
                 const bool hb = pa + 1 < p1;
                 const int key0 = pa * kPage;
                 bf16x8_t pop[RT];
-                // uniform: a causal, length or window edge.  Only the softmax has two
-                // versions: two copies of the PV would give O two definitions per step
+                // uniform: a causal, length or window edge.  Only QK and the softmax have
+                // two versions: two copies of the PV would give O two definitions per step
                 const bool masked = !hb || key0 + 31 > ctx || key0 < lo_max;
-                if (masked)
-                    w4_softmax<RT, CAP, true>(st, retry, pop, S, ctx, lk, p.log2g, wlim, key0, hb, crow, p.cap_log2,
-                                              ln);
-                else
-                    w4_softmax<RT, CAP, false>(st, retry, pop, S, ctx, lk, p.log2g, wlim, key0, hb, crow,
-                                               p.cap_log2, ln);
-                // V of pages 2t, 2t+1 must have landed
-                if (t == 0) {
-                    if (nst > 2)
-                        wait_vmcnt<24>();
-                    else if (nst > 1)
-                        wait_vmcnt<16>();
+                if (CAP || masked) {
+                    w4_qk<RT>(S, ka, ka + kW4PageBytes, qop, ln);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    after_k(0);
+                    after_k(1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (masked)
+                        w4_softmax<RT, CAP, true>(st, retry, pop, S, ctx, lk, p.log2g, wlim, key0, hb, crow,
+                                                  p.cap_log2, ln);
                     else
-                        wait_vmcnt<0>();
-                } else if (t + 2 < nst) {
-                    wait_vmcnt<16>();
-                } else if (t + 1 < nst) {
-                    wait_vmcnt<8>();
+                        w4_softmax<RT, CAP, false>(st, retry, pop, S, ctx, lk, p.log2g, wlim, key0, hb, crow,
+                                                   p.cap_log2, ln);
                 } else {
-                    wait_vmcnt<0>();
+                    w4_qk_softmax<RT>(st, retry, pop, S, ka, ka + kW4PageBytes, qop, ctx, lk, p.log2g, wlim, key0,
+                                      crow, ln, after_k);
                 }
+                // V(t) must have landed.  Issued after it so far: V(t+1), K(t+2) and
+                // K(t+3) where those steps exist, and at t = 0 also K(1)
+                wait_vmcnt_x8(8 * ((t + 1 < nst) * (t == 0 ? 2 : 1) + (t + 2 < nst) + (t + 3 < nst)));
                 __builtin_amdgcn_sched_barrier(0);
-                w4_pv<RT>(st, va, va + kW4PageBytes, pop, masked, masked ? v_zero_mask(key0, hb, lk, ln) : 0u, ln);
+                w4_pv<RT>(st, va, va + kW4PageBytes, pop, masked, masked ? v_zero_mask(key0, hb, lk, ln) : 0u, ln,
+                          after_v);
+                eV0 = eK0;
+                eV1 = eK1;
+                eK0 = eN0;
+                eK1 = eN1;
+                eN0 = entry(2 * t + 10);
+                eN1 = entry(2 * t + 11);
             }
             wait_vmcnt<0>();
             if (!__any(retry) || pass == 1) {                  // a second pass cannot move m again
@@ -3136,24 +3365,29 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
     const int q1 = load_uniform(p.cu, b + 1);
     const int s = load_uniform(p.ws_prefix, bg);
     const int e = load_uniform(p.ws_prefix, bg + 1);
-    const int total = load_uniform(p.ws_prefix, bh);
+    const int cs = load_uniform(p.ws_cost, bg);
+    const int ce = load_uniform(p.ws_cost, bg + 1);
+    const int ctot = load_uniform(p.ws_cost, bh);
     const int nw = load_uniform(p.ws_meta, 0);
-    asm volatile("" :: "s"(q0), "s"(q1), "s"(s), "s"(e), "s"(total), "s"(nw));   // keep the loads together
+    asm volatile("" :: "s"(q0), "s"(q1), "s"(s), "s"(e), "s"(cs), "s"(ce), "s"(ctot), "s"(nw));   // one round trip
     const int64_t n = nw;
     const int lq = checked_q_len(q0, q1, p.total_q, p.max_q);
-    if (t >= lq || e <= s || total <= 0)
+    if (t >= lq || e <= s || ctot <= 0)
         return;
-    const int w0 = (int)(((int64_t)(s + 1) * n - 1) / total);
-    const int w1 = (int)(((int64_t)e * n - 1) / total);
+    // The split of locate() in cost positions: the pair's pages occupy cost
+    // positions [ce - (e - s), ce); workgroup w covers [w T / n, (w + 1) T / n).
+    const int64_t x0 = ce - (e - s);                   // cost position of the pair's first page
+    const int w0 = (int)(((x0 + 1) * n - 1) / ctot);
+    const int w1 = (int)(((int64_t)ce * n - 1) / ctot);
     if (w0 == w1)
         return;                                        // written by the main kernel
     const int h = hq4 * kHpb + threadIdx.x / kTpr;
     const int row = (t << p.log2g) + h;
     const int d = (threadIdx.x % kTpr) * 4;
     // Slots of the pieces: workgroup w0 holds this pair as its first piece
-    // (slot 2 w0) if the pair starts where w0's range starts, else as its last
+    // (slot 2 w0) if its range starts inside the pair's costs, else as its last
     // (2 w0 + 1); every later workgroup w holds it as its first piece (2 w).
-    const int first0 = s > (int)(((int64_t)w0 * total) / n) ? 1 : 0;
+    const int first0 = cs > (int)(((int64_t)w0 * ctot) / n) ? 1 : 0;
     const int ns = w1 - w0 + 1;
     auto slot_of = [&](int si) -> int64_t { return si == 0 ? 2 * w0 + first0 : 2 * (w0 + si); };
 
@@ -3384,7 +3618,8 @@ struct va_plan_s {
     int32_t mbps;       // pages per sequence bound: the block-table row, or (prefix + extend)
                         // ceil(max_seqlen_k / 16)
     bool mla;           // absorbed MLA: 576-wide rows, 512-wide values (va_mla_split_kernel)
-    size_t off_prefix, off_lse, off_o, ws_bytes;
+    size_t off_prefix, off_cost, off_lse, off_o, ws_bytes;
+    int32_t piece_cost;
     bool debug;         // VA_DEBUG set at va_plan: validate mode and a plan dump on stderr
 };
 
@@ -3517,8 +3752,18 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     pl->grid = p.force_grid > 0 ? p.force_grid : cus;
     pl->min_pages = 8;
     pl->slots = 2 * (int64_t)pl->grid;                 // a first and a last piece per workgroup
+    // Pages charged for a pair that starts inside a workgroup's share (see
+    // locate): about the time of one more epilogue and prologue, in pages of
+    // the kernel's own streaming rate (measured on the high-concurrency
+    // workload for the FP8 cache; scaled by page bytes for the others).
+    pl->piece_cost = mla ? (p.kv_dtype == VA_DT_FP8_E4M3FN ? 24 : 12)
+                         : (p.kv_dtype == VA_DT_FP8_E4M3FN ? 32 : 16);
+    if ((int64_t)bh * (mbps + pl->piece_cost) > INT32_MAX)
+        pl->piece_cost = 0;                            // costs must stay 32-bit: split by pages
     size_t off = 256;                                   // meta
     pl->off_prefix = off;
+    off = align_up(off + (size_t)(bh + 1) * 4, 256);
+    pl->off_cost = off;
     off = align_up(off + (size_t)(bh + 1) * 4, 256);
     pl->off_lse = off;
     off = align_up(off + (size_t)pl->slots * pl->rows_max * 4, 256);
@@ -3648,7 +3893,9 @@ va_status run_impl(va_plan_t plan, int32_t stage, const void *q, const void *k_p
         sp.ws_o = ws + plan->off_o;
         sp.ws_lse = reinterpret_cast<float *>(ws + plan->off_lse);
         sp.ws_prefix = reinterpret_cast<int32_t *>(ws + plan->off_prefix);
+        sp.ws_cost = reinterpret_cast<int32_t *>(ws + plan->off_cost);
         sp.ws_meta = reinterpret_cast<int32_t *>(ws);
+        sp.piece_cost = plan->piece_cost;
         sp.scale_log2 = softmax_scale * 1.4426950408889634f;
         sp.cap_log2 = pr.softcap * 1.4426950408889634f;
         sp.sinks = sinks;
@@ -3688,6 +3935,7 @@ va_status run_impl(va_plan_t plan, int32_t stage, const void *q, const void *k_p
         mp.ws_o = ws + plan->off_o;
         mp.ws_lse = reinterpret_cast<const float *>(ws + plan->off_lse);
         mp.ws_prefix = reinterpret_cast<const int32_t *>(ws + plan->off_prefix);
+        mp.ws_cost = reinterpret_cast<const int32_t *>(ws + plan->off_cost);
         mp.ws_meta = reinterpret_cast<const int32_t *>(ws);
         mp.out = static_cast<uint16_t *>(out);
         mp.num_seqs = pr.num_seqs;

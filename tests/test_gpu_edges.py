@@ -65,7 +65,7 @@ def test_many_pairs_prefix_extend():
 def test_many_pairs_mla():
     from test_gpu_mla import run_mla
     n = 80
-    p = va_inputs.mla(_lens(n, 0, 4, 13), _lens(n, 1, 400, 14), 8, "fp8", seed=15, name="many-pairs-mla")
+    p = va_inputs.mla(_lens(n, 0, 4, 13), _lens(n, 4, 400, 14), 8, "fp8", seed=15, name="many-pairs-mla")
     ref, _ = oracle.attn_mla_problem(p)
     compare(as_f64(run_mla(p, force_grid=7)), ref, p.name)
 
