@@ -38,6 +38,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0                 # dense MFMA, MI355X
+PEAK_FP8_TFLOPS = 5000.0
 MAIN_KERNEL = {"fp8": "va_split_kv_fp8_w4_kernel", "bf16": "va_split_kv_bf16_w8_kernel"}
 MLA_KERNEL = "va_mla_split_kernel"
 # Arithmetic of the path: FP8 KV runs QK^T on fp8 MFMA (Q as an exact hi/lo fp8
@@ -271,6 +273,75 @@ def cpu_baseline(p, budget_s: float = 12.0):
     return rec
 
 
+def mfma_bound(p, main_ms):
+    """The matrix-core bound of the main kernel: the MFMA work it executes
+    (every key of every streamed page against every row of the 16-row tiles),
+    at MI355X's dense peaks.  QK^T on an FP8 cache runs as two fp8 MFMAs per
+    product (Q split into exact e4m3 hi and lo parts, 5.0 PFLOP/s); on a bf16
+    cache as bf16 MFMAs (2.5 PFLOP/s); PV always in bf16.  frac is the time at
+    those peaks over the measured main-kernel time (1 = bound by MFMA)."""
+    qk_w = p.head_dim
+    pv_w = getattr(p, "v_head_dim", None) or p.head_dim
+    g = p.num_q_heads // p.num_kv_heads
+    qk_fl = pv_fl = 0
+    for b in range(p.num_seqs):
+        lq, lk = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b]), int(p.seqused_k[b])
+        if lq <= 0 or lk <= 0:
+            continue
+        rows = -(-lq * g // 16) * 16                      # rows in 16-row MFMA tiles
+        keys = -(-lk // p.page_size) * p.page_size        # every key of the streamed pages
+        qk_fl += 2 * rows * keys * qk_w * p.num_kv_heads
+        pv_fl += 2 * rows * keys * pv_w * p.num_kv_heads
+    fp8 = p.kv_dtype == "fp8"
+    t_qk = qk_fl * (2 if fp8 else 1) / ((PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS) * 1e12)
+    t_pv = pv_fl / (PEAK_BF16_TFLOPS * 1e12)
+    return {"qk_flops": qk_fl, "pv_flops": pv_fl, "qk_mfma": "fp8 hi + lo" if fp8 else "bf16",
+            "pv_mfma": "bf16", "us_at_peak": round((t_qk + t_pv) * 1e6, 3),
+            "frac": round((t_qk + t_pv) / (main_ms * 1e-3), 4)}
+
+
+def ceiling(args):
+    """Streaming ceiling of the copy path alone: va_stream_pages over the
+    long-context workload's bytes (2 x 32768 pages of 4 KiB = 268 MB per
+    launch), pages in a seeded random order, four disjoint page sets of a
+    1 GiB pool so that no launch finds the previous one's data in a cache.
+    One line of JSON per ring depth."""
+    import torch
+    import paged_gqa_attention_va_amd as va
+    dev = torch.device("cuda:0")
+    n_pool = 1 << 18                                      # 4 KiB pages: 1 GiB
+    n_launch = 2 * 32768                                  # K and V pages of the long-context workload
+    g = torch.Generator(device="cpu")
+    g.manual_seed(7)
+    pool = torch.randint(0, 256, (n_pool * 4096,), dtype=torch.uint8, generator=g).to(dev)
+    order = torch.randperm(n_pool, generator=g).to(torch.int32)
+    sets = [order[i * n_launch:(i + 1) * n_launch].contiguous().to(dev) for i in range(4)]
+    grid = torch.cuda.get_device_properties(dev).multi_processor_count
+    sums = torch.zeros(grid * 4, dtype=torch.int32, device=dev)
+    for depth in (2, 4, 6, 8, 10):
+        t_w = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t_w < args.warmup_seconds or i < 20:
+            va.stream_pages(pool, sets[i % 4], depth, grid, sums)
+            i += 1
+            if i % 64 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for j in range(args.steps):
+            va.stream_pages(pool, sets[j % 4], depth, grid, sums)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / args.steps
+        gbps = n_launch * 4096 / (us * 1e-6) / 1e9
+        print(json.dumps({"ceiling": "va_stream_pages", "depth_pages_per_wave": depth, "grid": grid,
+                          "bytes_per_launch": n_launch * 4096, "launches": args.steps,
+                          "us_per_launch": round(us, 3), "GBps": round(gbps, 1),
+                          "pct_of_8TBps": round(100.0 * gbps / PEAK_HBM_GBPS, 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,6 +379,10 @@ def main():
     ap.add_argument("--warm", action="store_true",
                     help="warm-cache run: one copy of the KV pools, so steps may find the previous "
                          "step's data in the memory-side cache (the default rotates 4 copies)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only measure the streaming ceiling of the FP8 kernel's copy path "
+                         "(va_stream_pages): the long-context workload's 268 MB of 4 KiB pages, "
+                         "random order, from a 1 GiB pool rotated over four page sets, no compute")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -323,6 +398,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
                           "launches": 3}), flush=True)
+        return
+
+    if args.ceiling:
+        ceiling(args)
         return
 
     if args.gpus != 1:
@@ -544,6 +623,8 @@ def main():
                                else "back-to-back main-kernel launches"),
                     "us_per_call_of_that_run": None if ms_step_ev is None else round(ms_step_ev * 1e3, 3),
                     "us_per_launch_main_only": round(main_only_ms * 1e3, 3)}
+        if pe is None:
+            roofline["mfma_bound"] = mfma_bound(p, main_ms)
 
     stamps = None
     if args.stamps and pe is None:

@@ -363,6 +363,22 @@ va_status va_spec_block_table(const int32_t *kv_indptr, const int32_t *kv_indice
  */
 va_status va_fp8_to_bf16(const uint8_t *in, uint16_t *out, int64_t n, void *stream);
 
+/*
+ * Diagnostic: the streaming ceiling of the FP8 paged kernel's copy path.
+ * Copies npages 4 KiB pages, pool + 4096 * pages[i] (device int32 page
+ * indices; one outside [0, pool_bytes / 4096) is clamped into it), into
+ * LDS with the kernel's global_load_lds copies (nontemporal), grid
+ * workgroups of four waves, each wave an equal contiguous share of the list
+ * in order with depth (2, 4, 6, 8 or 10) pages in flight, and no other work.
+ * sums[grid * 4] (device) receives, per wave, the sum of the first 32-bit
+ * word of every page it copied (for a check).  Returns VA_ERR_INVALID_ARG for
+ * null pointers, a pool not 16-byte aligned or shorter than one page, an
+ * unsupported depth, or grid outside [1, 65536].  The caller owns every
+ * buffer; asynchronous on stream.
+ */
+va_status va_stream_pages(const void *pool, int64_t pool_bytes, const int32_t *pages, int64_t npages,
+                          int32_t depth, int32_t grid, uint32_t *sums, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

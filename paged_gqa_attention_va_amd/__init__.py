@@ -30,7 +30,7 @@ VA_LAYOUT_PAGED, VA_LAYOUT_PREFIX_EXTEND = 0, 1
 VA_BAD_CU_SEQLENS_Q, VA_BAD_Q_LEN, VA_BAD_SEQUSED_K, VA_BAD_Q_GT_K, VA_BAD_PAGE = 1, 2, 4, 8, 16
 
 EXPORTED = ("va_plan", "va_plan_workspace_bytes", "va_plan_grid", "va_run", "va_run_ex",
-            "va_plan_destroy", "va_status_str", "va_fp8_to_bf16", "va_spec_block_table",
+            "va_plan_destroy", "va_status_str", "va_fp8_to_bf16", "va_stream_pages", "va_spec_block_table",
             "va_validate", "va_run_prefix_extend", "va_run_timed", "va_set_stamp_buffer",
             "va_run_noalloc")
 
@@ -91,6 +91,8 @@ def library(path: str = LIB_PATH):
     lib.va_validate.argtypes = [P, P, P, P, P, P]
     lib.va_fp8_to_bf16.restype = ctypes.c_int
     lib.va_fp8_to_bf16.argtypes = [P, P, ctypes.c_int64, P]
+    lib.va_stream_pages.restype = ctypes.c_int
+    lib.va_stream_pages.argtypes = [P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P]
     lib.va_run_timed.restype = ctypes.c_int
     lib.va_run_timed.argtypes = run_args[:10] + [P] + run_args[10:] + [P, P]
     lib.va_set_stamp_buffer.restype = ctypes.c_int
@@ -387,6 +389,28 @@ def fp8_to_bf16(codes, stream=None):
     _check(lib.va_fp8_to_bf16(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                               codes.numel(), ctypes.c_void_p(stream.cuda_stream)), "va_fp8_to_bf16")
     return out
+
+
+def stream_pages(pool, pages, depth: int = 10, grid: int = 256, sums=None, stream=None):
+    """Diagnostic streaming ceiling (va_stream_pages): copy the 4 KiB pages
+    pool[4096 * pages[i]] into LDS as the FP8 kernel's ring does and nothing
+    else.  pool: a device uint8 tensor, pages: a device int32 tensor.  Returns
+    the per-wave sums of each page's first 32-bit word, modulo 2^32 (an int32
+    tensor of grid * 4 holding the uint32 bits)."""
+    import torch
+    lib = library()
+    if pool.dtype != torch.uint8 or not pool.is_cuda or not pool.is_contiguous():
+        raise ValueError("pool must be a contiguous device uint8 tensor")
+    if pages.dtype != torch.int32 or not pages.is_cuda or not pages.is_contiguous():
+        raise ValueError("pages must be a contiguous device int32 tensor")
+    if sums is None:
+        sums = torch.zeros(grid * 4, dtype=torch.int32, device=pool.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(pool.device)
+    _check(lib.va_stream_pages(ctypes.c_void_p(pool.data_ptr()), pool.numel(), ctypes.c_void_p(pages.data_ptr()),
+                               pages.numel(), depth, grid, ctypes.c_void_p(sums.data_ptr()),
+                               ctypes.c_void_p(stream.cuda_stream)), "va_stream_pages")
+    return sums
 
 
 def set_stamp_buffer(buf, lib=None) -> None:

@@ -3472,6 +3472,50 @@ __global__ __launch_bounds__(kThreads) void va_spec_block_table_kernel(const int
     bt[i] = tok < n ? indices[t0 + tok] / page_size : 0;
 }
 
+// Streaming ceiling (diagnostic): the copy path of the FP8 paged kernel with
+// nothing else.  Each wave takes an equal contiguous share of a list of 4 KiB
+// pages and copies them in that order into a ring of DEPTH 4 KiB slots of its
+// own LDS region (40 KiB, as the FP8 kernel's ring) with the same
+// global_load_lds_dwordx4 ... nt copies, keeping DEPTH pages in flight.  When
+// a slot is reused, the first dword of the page that landed there is added to
+// the wave's sum (so the copies are checked, not only issued); sums[wave]
+// holds the total.  Pages are pool + 4096 * pages[i], with the index clamped
+// to the pool.
+template <int DEPTH>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void va_stream_pages_kernel(const uint8_t *pool, int64_t pool_pages, const int32_t *pages, int64_t npages,
+                            uint32_t *sums)
+{
+    static_assert(DEPTH >= 1 && DEPTH <= 10, "ring of at most 10 slots");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * 10 * 4096];
+    const int lane = threadIdx.x & 63;
+    const int wv = uniform(threadIdx.x >> 6);
+    const int64_t nw = (int64_t)gridDim.x * 4;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + wv;
+    const int64_t a = (gw * npages) / nw, b = ((gw + 1) * npages) / nw;
+    unsigned char *ring = lds + wv * 10 * 4096;
+    const uint32_t ring_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(ring));
+    uint32_t sum = 0;
+    for (int64_t i = a; i < b; ++i) {
+        const int slot = (int)((i - a) % DEPTH);
+        if (i - a >= DEPTH) {
+            wait_vmcnt<4 * (DEPTH - 1)>();              // the page that used this slot landed
+            sum += *reinterpret_cast<const uint32_t *>(ring + slot * 4096);
+        }
+        const int64_t pg = min(max((int64_t)load_uniform(pages, i), (int64_t)0), pool_pages - 1);   // clamped
+        const uint8_t *src = pool + pg * 4096;
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            dma16(src, (uint32_t)(1024 * x + 16 * lane), ring_addr + (uint32_t)(slot * 4096 + 1024 * x));
+    }
+    wait_vmcnt<0>();
+    const int64_t done = b - a;
+    for (int64_t i = max(a, b - DEPTH); i < b; ++i)
+        sum += *reinterpret_cast<const uint32_t *>(ring + (int)((i - a) % DEPTH) * 4096);
+    if (lane == 0)
+        sums[gw] = done > 0 ? sum : 0u;
+}
+
 __global__ __launch_bounds__(kThreads) void va_fp8_to_bf16_kernel(const uint8_t *in, uint16_t *out, int64_t n)
 {
     const int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
@@ -4099,6 +4143,27 @@ va_status va_spec_block_table(const int32_t *kv_indptr, const int32_t *kv_indice
     hipLaunchKernelGGL(va_spec_block_table_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), kv_indptr, kv_indices, num_seqs, page_size,
                        max_blocks_per_seq, block_table, seqused_k);
+    return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+}
+
+va_status va_stream_pages(const void *pool, int64_t pool_bytes, const int32_t *pages, int64_t npages,
+                          int32_t depth, int32_t grid, uint32_t *sums, void *stream)
+{
+    if (!pool || !pages || !sums || npages < 0 || pool_bytes < 4096 || grid < 1 || grid > 65536 ||
+        (reinterpret_cast<uintptr_t>(pool) & 15) != 0)
+        return VA_ERR_INVALID_ARG;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    void (*k)(const uint8_t *, int64_t, const int32_t *, int64_t, uint32_t *) = nullptr;
+    switch (depth) {
+    case 2: k = va_stream_pages_kernel<2>; break;
+    case 4: k = va_stream_pages_kernel<4>; break;
+    case 6: k = va_stream_pages_kernel<6>; break;
+    case 8: k = va_stream_pages_kernel<8>; break;
+    case 10: k = va_stream_pages_kernel<10>; break;
+    default: return VA_ERR_INVALID_ARG;
+    }
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const uint8_t *>(pool),
+                       pool_bytes / 4096, pages, npages, sums);
     return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 

@@ -160,3 +160,17 @@ def test_binding_rejects_tensors_on_another_device():
     va._same_device(torch.device("cpu"), torch.zeros(1), None)
     with pytest.raises(ValueError):
         va._same_device(torch.device("cpu"), torch.zeros(1), torch.empty(1, device="meta"))
+
+
+def test_stream_pages_rejects_bad_arguments_before_launching():
+    lib = va.library()
+    P = ctypes.c_void_p
+    pool, pages, sums = P(0x10000), P(0x20000), P(0x30000)     # never dereferenced: refused first
+    assert lib.va_stream_pages(None, 1 << 20, pages, 10, 8, 4, sums, None) == va.VA_ERR_INVALID_ARG
+    assert lib.va_stream_pages(pool, 1 << 20, None, 10, 8, 4, sums, None) == va.VA_ERR_INVALID_ARG
+    assert lib.va_stream_pages(pool, 1 << 20, pages, 10, 8, 4, None, None) == va.VA_ERR_INVALID_ARG
+    assert lib.va_stream_pages(pool, 1 << 20, pages, 10, 7, 4, sums, None) == va.VA_ERR_INVALID_ARG
+    assert lib.va_stream_pages(pool, 1 << 20, pages, 10, 8, 0, sums, None) == va.VA_ERR_INVALID_ARG
+    assert lib.va_stream_pages(pool, 4095, pages, 10, 8, 4, sums, None) == va.VA_ERR_INVALID_ARG
+    assert lib.va_stream_pages(P(0x10008), 1 << 20, pages, 10, 8, 4, sums, None) == va.VA_ERR_INVALID_ARG
+    assert lib.va_stream_pages(pool, 1 << 20, pages, -1, 8, 4, sums, None) == va.VA_ERR_INVALID_ARG
