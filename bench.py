@@ -40,7 +40,13 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0                 # dense MFMA, MI355X
 PEAK_FP8_TFLOPS = 5000.0
-MAIN_KERNEL = {"fp8": "va_split_kv_fp8_w4_kernel", "bf16": "va_split_kv_bf16_w8_kernel"}
+def main_kernel(kv_dtype: str, plan_kernel: int) -> str:
+    """Name of the split-KV kernel a plan launches (plan_kernel as va_plan_kernel
+    reports it: 1 or 2 for paged FP8 GQA, 0 otherwise)."""
+    if kv_dtype == "bf16":
+        return "va_split_kv_bf16_w8_kernel"
+    return "va_split_kv_fp8_w4_kernel" if plan_kernel == 1 else "va_split_kv_fp8_w8_kernel"
+
 MLA_KERNEL = "va_mla_split_kernel"
 # Arithmetic of the path: FP8 KV runs QK^T on fp8 MFMA (Q as an exact hi/lo fp8
 # pair) and PV on bf16 MFMA; bf16 KV runs both on bf16 MFMA; fp32 accumulation.
@@ -186,6 +192,8 @@ def stamp_report(st: np.ndarray, grid: int) -> dict:
     per-wave timestamps of a VA_STAMPS library (16 words per wave, see va.h)."""
     w = st.reshape(grid, 4, 16).astype(np.int64)
     live = w[:, 0, 1] > 0                                  # workgroups that found work
+    if not live.any():                                     # the kernel that ran records no stamps
+        return None
     w = w[live]
     t0 = w[:, :, 0].min()
     us = lambda x: (x - t0) / 100.0                        # 100 MHz clock -> us
@@ -354,6 +362,9 @@ def main():
     ap.add_argument("--variant", type=int, default=0, help="sweep variant of workload 4")
     ap.add_argument("--copies", type=int, default=4, help="KV pool copies to rotate over")
     ap.add_argument("--grid", type=int, default=0, help="force the split-KV grid (0 = plan)")
+    ap.add_argument("--kernel", type=int, default=0, choices=[0, 1, 2],
+                    help="paged FP8 GQA split-KV kernel: 0 = plan's choice, 1 = one wave per SIMD, "
+                         "2 = two row groups")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--window", type=int, default=-1,
                     help="sliding window size (keys a query sees, itself included; -1 = none)")
@@ -498,7 +509,7 @@ def main():
         kv_indptr = torch.from_numpy(indptr).to(dev)
         kv_indices = torch.from_numpy(np.concatenate(slots).astype(np.int32)).to(dev)
     make_plan = ((lambda: va.Plan.for_prefix_extend(pe, force_grid=args.grid)) if pe is not None
-                 else (lambda: va.Plan.for_problem(p, force_grid=args.grid)))
+                 else (lambda: va.Plan.for_problem(p, force_grid=args.grid, kernel=args.kernel)))
     plan = make_plan()
     t_plan = []
     for _ in range(50):                   # host cost of a plan (once per shape, never per call)
@@ -616,7 +627,7 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                     "traffic": load_traffic(workload),
-                    "kernel": MLA_KERNEL if args.mla else MAIN_KERNEL[p.kv_dtype],
+                    "kernel": MLA_KERNEL if args.mla else main_kernel((pe if pe is not None else p).kv_dtype, plan.kernel),
                     "us_per_launch": round(main_ms * 1e3, 3),
                     "timing": ("events recorded by the main kernel's own dispatch, in every step of a "
                                "run of timed whole calls" if ms_step_ev is not None

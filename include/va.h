@@ -120,6 +120,14 @@ typedef struct {
     int32_t layout;              /* va_layout of the KV cache (VA_LAYOUT_PAGED = 0) */
     int32_t v_head_dim;          /* value / output width; 0 = head_dim.  head_dim 576 with
                                     v_head_dim 512 is absorbed MLA (see below) */
+    int32_t kernel;              /* split-KV kernel of a paged FP8 GQA call: 0 = automatic,
+                                    1 = one wave per SIMD holding every row (best with many
+                                    pages per workgroup), 2 = two row groups per key group
+                                    (best with few).  Automatic picks 1 when the pages a
+                                    workgroup can get, from max_seqlen_k (and the window),
+                                    are at least 112.  Every choice gives the same result up
+                                    to floating-point summation order.  Other layouts and
+                                    dtypes take 0 only; other values are VA_ERR_INVALID_ARG. */
 } va_problem;
 
 typedef struct va_plan_s *va_plan_t;
@@ -157,6 +165,14 @@ va_status va_plan(const va_problem *problem, va_plan_t *out);
 
 /* Bytes of device workspace va_run needs for this plan. */
 va_status va_plan_workspace_bytes(va_plan_t plan, size_t *bytes);
+
+/*
+ * The split-KV kernel the plan runs for a paged FP8 GQA call, as in
+ * va_problem.kernel: 1 = one wave per SIMD, 2 = two row groups; 0 for every
+ * other call (bf16, prefix + extend, MLA).  VA_ERR_INVALID_ARG for null
+ * pointers.
+ */
+va_status va_plan_kernel(va_plan_t plan, int32_t *kernel);
 
 /* Number of split-KV workgroups the plan launches (after force_grid). */
 va_status va_plan_grid(va_plan_t plan, int32_t *grid);

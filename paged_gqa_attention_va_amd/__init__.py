@@ -30,7 +30,7 @@ VA_LAYOUT_PAGED, VA_LAYOUT_PREFIX_EXTEND = 0, 1
 VA_BAD_CU_SEQLENS_Q, VA_BAD_Q_LEN, VA_BAD_SEQUSED_K, VA_BAD_Q_GT_K, VA_BAD_PAGE = 1, 2, 4, 8, 16
 
 EXPORTED = ("va_plan", "va_plan_workspace_bytes", "va_plan_grid", "va_run", "va_run_ex",
-            "va_plan_destroy", "va_status_str", "va_fp8_to_bf16", "va_stream_pages", "va_spec_block_table",
+            "va_plan_destroy", "va_plan_kernel", "va_status_str", "va_fp8_to_bf16", "va_stream_pages", "va_spec_block_table",
             "va_validate", "va_run_prefix_extend", "va_run_timed", "va_set_stamp_buffer",
             "va_run_noalloc")
 
@@ -54,6 +54,7 @@ class _Problem(ctypes.Structure):
         ("num_cus", ctypes.c_int32), ("force_grid", ctypes.c_int32),
         ("window_left", ctypes.c_int32), ("softcap", ctypes.c_float),
         ("layout", ctypes.c_int32), ("v_head_dim", ctypes.c_int32),
+        ("kernel", ctypes.c_int32),
     ]
 
 
@@ -73,6 +74,8 @@ def library(path: str = LIB_PATH):
     lib.va_plan_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.va_plan_grid.restype = ctypes.c_int
     lib.va_plan_grid.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
+    lib.va_plan_kernel.restype = ctypes.c_int
+    lib.va_plan_kernel.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
     run_args = [P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, ctypes.c_size_t, P]
     lib.va_run.restype = ctypes.c_int
     lib.va_run.argtypes = run_args
@@ -141,7 +144,7 @@ class Plan:
                  num_cus: int = 0, force_grid: int = 0, head_dim: int = 256,
                  window_left: int = -1, softcap: float = 0.0,
                  page_size: int = 16, q_dtype: str = "bf16", layout: str = "paged",
-                 v_head_dim: int = 0):
+                 v_head_dim: int = 0, kernel: int = 0):
         self._lib = library()
         if layout not in ("paged", "prefix_extend"):
             raise ValueError(f"unknown layout {layout!r}")
@@ -149,7 +152,8 @@ class Plan:
                       max_seqlen_q, max_seqlen_k, max_blocks_per_seq, num_blocks, total_q,
                       _dtype_code(q_dtype), _dtype_code(kv_dtype), num_cus, force_grid,
                       int(window_left), float(softcap),
-                      VA_LAYOUT_PAGED if layout == "paged" else VA_LAYOUT_PREFIX_EXTEND, int(v_head_dim))
+                      VA_LAYOUT_PAGED if layout == "paged" else VA_LAYOUT_PREFIX_EXTEND, int(v_head_dim),
+                      int(kernel))
         self.problem = pr
         self.v_head_dim = int(v_head_dim) or int(head_dim)
         self.kv_dtype = kv_dtype
@@ -163,6 +167,9 @@ class Plan:
         g = ctypes.c_int32()
         _check(self._lib.va_plan_grid(h, ctypes.byref(g)), "va_plan_grid")
         self.grid = int(g.value)
+        kk = ctypes.c_int32()
+        _check(self._lib.va_plan_kernel(h, ctypes.byref(kk)), "va_plan_kernel")
+        self.kernel = int(kk.value)        # FP8 paged GQA: 1 one wave per SIMD, 2 two row groups
 
     def __del__(self):
         h = getattr(self, "_h", None)

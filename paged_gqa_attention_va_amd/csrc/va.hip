@@ -3636,11 +3636,11 @@ SplitKernel pick_layout(bool fp8, bool tok)
 // RTW row tiles: one or two row tiles take RTW = 1, three or four RTW = 2 (a
 // wave's O^T accumulators stay at 128 registers).  Then KV dtype, softcap,
 // layout; absorbed MLA has its own kernel.
-SplitKernel select_kernel(int row_tiles, bool fp8, bool cap, bool tok, bool mla)
+SplitKernel select_kernel(int row_tiles, bool fp8, bool cap, bool tok, bool mla, bool w4)
 {
     if (mla)
         return fp8 ? kref(&va_mla_split_kernel<kKvFp8>, 512) : kref(&va_mla_split_kernel<kKvBf16>, 512);
-    if (fp8 && !tok)
+    if (fp8 && !tok && w4)
         return cap ? pick_fp8_w4<true>(row_tiles) : pick_fp8_w4<false>(row_tiles);
     if (row_tiles <= 2)
         return cap ? pick_layout<1, true>(fp8, tok) : pick_layout<1, false>(fp8, tok);
@@ -3662,6 +3662,7 @@ struct va_plan_s {
     int32_t mbps;       // pages per sequence bound: the block-table row, or (prefix + extend)
                         // ceil(max_seqlen_k / 16)
     bool mla;           // absorbed MLA: 576-wide rows, 512-wide values (va_mla_split_kernel)
+    bool fp8_w4;        // FP8 paged GQA on the one-wave-per-SIMD kernel
     size_t off_prefix, off_cost, off_lse, off_o, ws_bytes;
     int32_t piece_cost;
     bool debug;         // VA_DEBUG set at va_plan: validate mode and a plan dump on stderr
@@ -3758,6 +3759,9 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
         return VA_ERR_UNSUPPORTED;
     if (p.window_left < -1 || !(p.softcap >= 0.f) || p.softcap > 3.0e38f)
         return VA_ERR_INVALID_ARG;
+    const bool fp8_paged = p.kv_dtype == VA_DT_FP8_E4M3FN && !tok && !mla;
+    if (p.kernel < 0 || p.kernel > 2 || (p.kernel != 0 && !fp8_paged))
+        return VA_ERR_INVALID_ARG;
     if (p.total_q * (int64_t)p.num_q_heads >= INT32_MAX)    // q rows are indexed with 32-bit integers
         return VA_ERR_UNSUPPORTED;
     const int64_t bh = (int64_t)p.num_seqs * p.num_kv_heads;
@@ -3794,6 +3798,17 @@ va_status va_plan(const va_problem *pr, va_plan_t *out)
     pl->mla = mla;
     pl->rows_max = mla ? kMlaRows : 16 * 2 * (pl->rt <= 2 ? 1 : 2);   // 2 row groups x RTW row tiles
     pl->grid = p.force_grid > 0 ? p.force_grid : cus;
+    // FP8 paged GQA: the one-wave-per-SIMD kernel streams a page faster, the
+    // two-row-group kernel has about 6 us less fixed cost per piece (prologue
+    // and epilogue).  Measured crossover at 96-128 pages per workgroup (long
+    // context, 128: the first; 16 x 24576-key windows, 96: the second).
+    {
+        const int64_t keys = p.window_left >= 0
+                                 ? std::min<int64_t>(p.max_seqlen_k, (int64_t)p.window_left + p.max_seqlen_q + kPage)
+                                 : p.max_seqlen_k;
+        const int64_t pages = bh * ((keys + kPage - 1) / kPage);
+        pl->fp8_w4 = fp8_paged && (p.kernel == 1 || (p.kernel == 0 && pages >= 112 * (int64_t)pl->grid));
+    }
     pl->min_pages = 8;
     pl->slots = 2 * (int64_t)pl->grid;                 // a first and a last piece per workgroup
     // Pages charged for a pair that starts inside a workgroup's share (see
@@ -3836,6 +3851,16 @@ va_status va_plan_workspace_bytes(va_plan_t plan, size_t *bytes)
     if (!plan || !bytes)
         return VA_ERR_INVALID_ARG;
     *bytes = plan->ws_bytes;
+    return VA_OK;
+}
+
+va_status va_plan_kernel(va_plan_t plan, int32_t *kernel)
+{
+    if (!plan || !kernel)
+        return VA_ERR_INVALID_ARG;
+    const bool fp8_paged = plan->prob.kv_dtype == VA_DT_FP8_E4M3FN && plan->prob.layout == VA_LAYOUT_PAGED &&
+                           !plan->mla;
+    *kernel = !fp8_paged ? 0 : (plan->fp8_w4 ? 1 : 2);
     return VA_OK;
 }
 
@@ -3964,7 +3989,7 @@ va_status run_impl(va_plan_t plan, int32_t stage, const void *q, const void *k_p
         sp.stamps = g_stamp_bytes >= (size_t)plan->grid * 4 * kStampSlots * sizeof(unsigned long long) ? g_stamps
                                                                                                  : nullptr;
         const SplitKernel k = select_kernel(plan->rt, pr.kv_dtype == VA_DT_FP8_E4M3FN, pr.softcap > 0.f,
-                                            tok != nullptr, plan->mla);
+                                            tok != nullptr, plan->mla, plan->fp8_w4);
         void *args[] = {&sp};
         if (hipExtLaunchKernel(k.fn, dim3(plan->grid), dim3(k.threads), args, 0, s, main_start, main_stop, 0) !=
                 hipSuccess ||

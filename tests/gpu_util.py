@@ -3,6 +3,7 @@ its C ABI, and the comparison rules against the oracle."""
 import sys
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -15,6 +16,27 @@ RTOL = 1e-2
 # Stricter internal bar: relative RMS error.  bf16 output rounding alone is
 # about 2^-9 / sqrt(3) ~ 1.1e-3; P is rounded to bf16 once more inside the kernel.
 REL_RMS = 5e-3
+
+
+# The two split-KV kernels of paged FP8 GQA (va_problem.kernel): 1 runs one
+# wave per SIMD, 2 two row groups.  The plan picks one by pages per workgroup;
+# tests force each so both stay covered at every shape.
+FP8_KERNELS = (1, 2)
+
+
+def kernel_for(dt: str, k: int) -> int:
+    """The kernel value to force for a paged GQA case: k for an FP8 cache,
+    0 (the only choice) for bf16."""
+    return k if dt == "fp8" else 0
+
+
+def with_kernels(cases, dt_of):
+    """pytest params: each FP8 case once per FP8 kernel, each other case once."""
+    out = []
+    for i, c in enumerate(cases):
+        ks = FP8_KERNELS if dt_of(c) == "fp8" else (0,)
+        out += [pytest.param(c, k, id=f"{i}-k{k}") for k in ks]
+    return out
 
 
 def note(msg: str) -> None:

@@ -174,3 +174,24 @@ def test_stream_pages_rejects_bad_arguments_before_launching():
     assert lib.va_stream_pages(pool, 4095, pages, 10, 8, 4, sums, None) == va.VA_ERR_INVALID_ARG
     assert lib.va_stream_pages(P(0x10008), 1 << 20, pages, 10, 8, 4, sums, None) == va.VA_ERR_INVALID_ARG
     assert lib.va_stream_pages(pool, 1 << 20, pages, -1, 8, 4, sums, None) == va.VA_ERR_INVALID_ARG
+
+
+def test_plan_picks_the_fp8_kernel_by_pages_per_workgroup():
+    """Auto choice: the one-wave-per-SIMD kernel once each workgroup streams at
+    least 112 pages, the two-row-group kernel below; an explicit choice is only
+    accepted for paged FP8 GQA."""
+    assert va.Plan(**base_problem()).kernel == 1                          # 16 x 32768: 128 pages / WG
+    assert va.Plan(**base_problem(max_seqlen_k=8192, max_blocks_per_seq=512)).kernel == 2
+    assert va.Plan(**base_problem(), window_left=4095).kernel == 2        # 16 x 4100 keys read
+    assert va.Plan(**base_problem(), window_left=24575).kernel == 2       # 1538 pages per sequence
+    assert va.Plan(**base_problem(), window_left=28671).kernel == 1
+    assert va.Plan(**base_problem(max_seqlen_k=8192, max_blocks_per_seq=512), kernel=1).kernel == 1
+    assert va.Plan(**base_problem(), kernel=2).kernel == 2
+    assert va.Plan(**base_problem(kv_dtype="bf16")).kernel == 0
+    for kw in (dict(kernel=3), dict(kernel=-1), dict(kernel=1, kv_dtype="bf16"),
+               dict(kernel=2, kv_dtype="bf16")):
+        d = base_problem()
+        d.update(kw)
+        with pytest.raises(va.VaError) as e:
+            va.Plan(**d)
+        assert e.value.status == va.VA_ERR_INVALID_ARG, kw

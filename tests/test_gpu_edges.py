@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import va_inputs
-from gpu_util import as_f64, check_problem, compare
+from gpu_util import FP8_KERNELS, as_f64, check_problem, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -23,11 +23,12 @@ def _lens(n, lo, hi, seed):
     return [int(x) for x in rng.integers(lo, hi + 1, size=n)]
 
 
+@pytest.mark.parametrize("kernel", FP8_KERNELS)
 @pytest.mark.parametrize("grid", [0, 7, 1000])
-def test_many_pairs_fp8(grid):
+def test_many_pairs_fp8(grid, kernel):
     n = 100                                           # 100 pairs: two scan passes
     p = va_inputs.custom(_lens(n, 0, 4, 1), _lens(n, 4, 300, 2), 16, 1, "fp8", seed=3, name="many-pairs-fp8")
-    check_problem(p, force_grid=grid)
+    check_problem(p, force_grid=grid, kernel=kernel)
 
 
 @pytest.mark.parametrize("grid", [0, 300])
@@ -131,13 +132,16 @@ def test_pool_beyond_4gib(dt, hq, hkv):
          f"{int(idx.max()) * page_bytes}")
     k, v = _spread(dev["k"], idx, n_big), _spread(dev["v"], idx, n_big)
     bt = _remap_table(dev["bt"], p.num_blocks, idx)
-    plan = va.Plan.for_problem(_WithBlocks(p, n_big))
-    out = plan.run(dev["q"], k, v, bt, dev["cu"], dev["sk"], p.scale, dev["kd"], dev["vd"])
+    outs = []
+    for kern in (FP8_KERNELS if dt == "fp8" else (0,)):
+        plan = va.Plan.for_problem(_WithBlocks(p, n_big), kernel=kern)
+        outs.append(plan.run(dev["q"], k, v, bt, dev["cu"], dev["sk"], p.scale, dev["kd"], dev["vd"]))
     torch.cuda.synchronize()
     del k, v
     torch.cuda.empty_cache()
     ref, _ = oracle.attn_problem(p)
-    compare(as_f64(out), ref, p.name)
+    for out in outs:
+        compare(as_f64(out), ref, p.name)
 
 
 @pytest.mark.parametrize("dt", ["fp8", "bf16"])

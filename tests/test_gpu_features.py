@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import va_inputs
-from gpu_util import as_f64, check_problem, compare, run
+from gpu_util import FP8_KERNELS, as_f64, check_problem, compare, run, with_kernels
 
 pytestmark = pytest.mark.gpu
 
@@ -38,22 +38,23 @@ def _problem(case):
 
 
 @pytest.mark.parametrize("grid", [0, 7, 300])
-@pytest.mark.parametrize("case", CASES, ids=[f"f{i}" for i in range(len(CASES))])
-def test_features_all_rows(case, grid):
-    check_problem(_problem(case), force_grid=grid)
+@pytest.mark.parametrize("case,kernel", with_kernels(CASES, lambda c: c[4]))
+def test_features_all_rows(case, kernel, grid):
+    check_problem(_problem(case), force_grid=grid, kernel=kernel)
 
 
 def test_sink_dominates_closed_form():
     """A sink far above every logit drives the output to ~0 (and a far-below
     one changes nothing): a check of the denominator that needs no oracle."""
-    p = va_inputs.custom([4, 2], [1024, 769], 16, 1, "fp8", seed=11)
-    base = as_f64(run(p))
-    p.sinks = np.full(16, 60.0, dtype=np.float32)
-    big = as_f64(run(p, force_grid=64))
-    assert np.max(np.abs(big)) < 1e-6
-    p.sinks = np.full(16, -60.0, dtype=np.float32)
-    small = as_f64(run(p, force_grid=64))
-    assert np.max(np.abs(small - base)) <= 2 ** -8 * np.max(np.abs(base))
+    for k in FP8_KERNELS:
+        p = va_inputs.custom([4, 2], [1024, 769], 16, 1, "fp8", seed=11)
+        base = as_f64(run(p, kernel=k))
+        p.sinks = np.full(16, 60.0, dtype=np.float32)
+        big = as_f64(run(p, force_grid=64, kernel=k))
+        assert np.max(np.abs(big)) < 1e-6
+        p.sinks = np.full(16, -60.0, dtype=np.float32)
+        small = as_f64(run(p, force_grid=64, kernel=k))
+        assert np.max(np.abs(small - base)) <= 2 ** -8 * np.max(np.abs(base))
 
 
 def test_long_context_with_every_feature_sampled():
@@ -63,6 +64,26 @@ def test_long_context_with_every_feature_sampled():
     p = va_inputs.custom([4] * 16, [32768] * 16, 16, 1, "fp8", seed=2, window_left=4095,
                          softcap=30.0, sinks=sinks, name="long-context-features")
     rows = va_inputs.sample_rows(p, 96, seed=5)
-    out = as_f64(run(p))
     ref, _ = oracle.attn_problem(p, rows=rows)
-    compare(out[rows], ref, p.name)
+    for k in FP8_KERNELS:
+        compare(as_f64(run(p, kernel=k))[rows], ref, f"{p.name} kernel {k}")
+
+
+@pytest.mark.parametrize("dt", ["fp8", "bf16"])
+def test_window_ignores_released_pages_of_a_separate_page_table(dt):
+    """A sliding-window layer's own page table (swa_page_table) passed as the
+    block table: entries of pages that lie wholly before the window are stale
+    (here out-of-range ids and, for one sequence, ids of live pages of another
+    sequence); the result must equal the oracle's, which never reads them."""
+    wl = 300
+    p = va_inputs.custom([4, 2, 3], [5000, 2100, 64], 16, 1, dt, seed=77, window_left=wl,
+                         name=f"swa-table-{dt}")
+    for b in range(p.num_seqs):
+        lq = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
+        first = max(0, int(p.seqused_k[b]) - lq - wl) // 16     # first page any query sees
+        p.block_table[b, :first] = p.num_blocks + 7 + np.arange(first)
+    first1 = (2100 - 2 - wl) // 16
+    p.block_table[0, :5] = p.block_table[1, first1:first1 + 5]               # live pages of sequence 1
+    for k in (FP8_KERNELS if dt == "fp8" else (0,)):
+        for grid in (0, 7):
+            check_problem(p, force_grid=grid, kernel=k)

@@ -12,9 +12,10 @@ import torch
 import oracle
 import paged_gqa_attention_va_amd as va
 import va_inputs
-from gpu_util import as_f64, check_problem, compare, note, run, to_device
+from gpu_util import FP8_KERNELS, as_f64, check_problem, compare, note, run, to_device, with_kernels
 
 pytestmark = pytest.mark.gpu
+KERNEL = pytest.mark.parametrize("kernel", FP8_KERNELS, ids=["k1", "k2"])
 
 
 def test_fp8_dequant_all_codes_matches_oracle_decoder():
@@ -27,10 +28,11 @@ def test_fp8_dequant_all_codes_matches_oracle_decoder():
     assert np.array_equal(got[~nan], ref[~nan])
 
 
+@KERNEL
 @pytest.mark.parametrize("cfg", [0, 1])
-def test_tiny_configs_all_rows(cfg):
+def test_tiny_configs_all_rows(cfg, kernel):
     p = va_inputs.config(cfg)
-    check_problem(p)
+    check_problem(p, kernel=kernel)
 
 
 @pytest.mark.parametrize("cfg", [0, 1])
@@ -52,25 +54,26 @@ RAGGED = [
 ]
 
 
-@pytest.mark.parametrize("case", RAGGED, ids=[f"r{i}" for i in range(len(RAGGED))])
-def test_ragged_shapes_all_rows(case):
+@pytest.mark.parametrize("case,kernel", with_kernels(RAGGED, lambda c: c[4]))
+def test_ragged_shapes_all_rows(case, kernel):
     ql, kl, hq, hkv, dt, kd, vd = case
     p = va_inputs.custom(ql, kl, hq, hkv, dt, seed=sum(kl) + hq, k_descale=kd, v_descale=vd,
                          name=f"ragged{hq}/{hkv}{dt}")
-    check_problem(p)
+    check_problem(p, kernel=kernel)
 
 
+@KERNEL
 @pytest.mark.parametrize("grid", [1, 2, 7, 64, 1000])
-def test_forced_grid_sizes_agree(grid):
+def test_forced_grid_sizes_agree(grid, kernel):
     p = va_inputs.custom([4, 2, 3, 1], [3000, 769, 100, 40], 16, 1, "fp8", seed=42,
                          name=f"grid{grid}")
-    check_problem(p, force_grid=grid)
+    check_problem(p, force_grid=grid, kernel=kernel)
 
 
 def test_forced_grid_sizes_agree_with_each_other():
     p = va_inputs.custom([4, 2, 3], [4000, 1500, 33], 16, 2, "fp8", seed=43)
     dev = to_device(p)
-    outs = [as_f64(run(p, dev=dev, force_grid=g)) for g in (1, 3, 16, 256)]
+    outs = [as_f64(run(p, dev=dev, force_grid=g, kernel=k)) for k in FP8_KERNELS for g in (1, 3, 16, 256)]
     for o in outs[1:]:
         compare(o, outs[0], "grid vs grid1")
 
@@ -78,10 +81,11 @@ def test_forced_grid_sizes_agree_with_each_other():
 def test_run_to_run_bitwise_deterministic():
     p = va_inputs.custom([4, 3, 2], [9000, 3000, 700], 16, 1, "fp8", seed=44)
     dev = to_device(p)
-    plan = va.Plan.for_problem(p)
-    a = run(p, dev=dev, plan=plan).clone()
-    b = run(p, dev=dev, plan=plan).clone()
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for k in FP8_KERNELS:
+        plan = va.Plan.for_problem(p, kernel=k)
+        a = run(p, dev=dev, plan=plan).clone()
+        b = run(p, dev=dev, plan=plan).clone()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_first_verify_token_with_one_key_is_exact():
@@ -97,10 +101,11 @@ def test_first_verify_token_with_one_key_is_exact():
             assert np.array_equal(out[q0, h], expect)
 
 
-def test_zero_query_gives_mean_of_visible_values():
+@KERNEL
+def test_zero_query_gives_mean_of_visible_values(kernel):
     p = va_inputs.custom([4, 2], [3000, 77], 16, 1, "fp8", seed=46)
     p.q[:] = 0
-    check_problem(p)
+    check_problem(p, kernel=kernel)
 
 
 def test_segment_markers_expose_a_dropped_or_doubled_piece():
@@ -115,12 +120,14 @@ def test_segment_markers_expose_a_dropped_or_doubled_piece():
     for b in range(p.num_seqs):
         for lp in range(-(-int(p.seqused_k[b]) // 16)):
             p.v[p.block_table[b, lp], :, 0, lp % 256] = 0x78      # e4m3fn 256.0
-    check_problem(p)
-    check_problem(p, force_grid=37)
+    for k in FP8_KERNELS:
+        check_problem(p, kernel=k)
+        check_problem(p, force_grid=37, kernel=k)
 
 
+@KERNEL
 @pytest.mark.parametrize("where", ["late", "first", "last"])
-def test_logit_spike_far_above_the_first_keys(where):
+def test_logit_spike_far_above_the_first_keys(where, kernel):
     # One key row is 16 * sign(q) of query row (token 0, head 0): that row's
     # logit there is about 200 (natural units) above the others, far beyond the
     # FP8 kernel's accumulation headroom (64 in log2 units above the first keys
@@ -134,18 +141,20 @@ def test_logit_spike_far_above_the_first_keys(where):
     key = {"late": 5000, "first": 3, "last": 5995}[where]
     p.k[p.block_table[0, key // 16], key % 16, 0] = spike
     for grid in (0, 7):
-        check_problem(p, force_grid=grid)
+        check_problem(p, force_grid=grid, kernel=kernel)
 
 
-def test_q_len_zero_rows_untouched_and_others_correct():
+@KERNEL
+def test_q_len_zero_rows_untouched_and_others_correct(kernel):
     p = va_inputs.custom([0, 4, 0, 2], [100, 3000, 50, 20], 8, 1, "fp8", seed=48)
-    check_problem(p)
+    check_problem(p, kernel=kernel)
 
 
-def test_graph_capture_replay_matches_eager():
+@KERNEL
+def test_graph_capture_replay_matches_eager(kernel):
     p = va_inputs.custom([4, 2, 3], [5000, 800, 64], 16, 1, "fp8", seed=49)
     dev = to_device(p)
-    plan = va.Plan.for_problem(p)
+    plan = va.Plan.for_problem(p, kernel=kernel)
     ws = plan.workspace()
     eager = run(p, dev=dev, plan=plan, workspace=ws).clone()
     out = torch.empty_like(dev["q"])
@@ -179,8 +188,8 @@ def _visible_keys(p, b, t):
     return int(p.seqused_k[b]) - lq + t + 1
 
 
-@pytest.mark.parametrize("case", CLOSED_FORM_SHAPES, ids=[f"s{i}" for i in range(len(CLOSED_FORM_SHAPES))])
-def test_identical_keys_give_mean_of_visible_values(case):
+@pytest.mark.parametrize("case,kernel", with_kernels(CLOSED_FORM_SHAPES, lambda c: c[4]))
+def test_identical_keys_give_mean_of_visible_values(case, kernel):
     # Every key row of a sequence is the same, so every logit of a query row is
     # the same and the output is v_descale times the plain mean of the values
     # the row sees (a closed form, computed here without the oracle).  The
@@ -207,14 +216,14 @@ def test_identical_keys_give_mean_of_visible_values(case):
             expect[q0 + t] = mean[np.arange(hq) // G]
     expect = expect.reshape(-1, 256)
     for grid in (0, 7, 300):
-        got = as_f64(run(p, force_grid=grid))
+        got = as_f64(run(p, force_grid=grid, kernel=kernel))
         err = np.abs(got - expect)
         note(f"  identical keys grid {grid}: max|err|={err.max():.3e}")
         assert np.all(err <= 1e-3 + 2.0 ** -8 * np.abs(expect))
 
 
-@pytest.mark.parametrize("case", CLOSED_FORM_SHAPES, ids=[f"s{i}" for i in range(len(CLOSED_FORM_SHAPES))])
-def test_constant_values_give_exactly_that_value(case):
+@pytest.mark.parametrize("case,kernel", with_kernels(CLOSED_FORM_SHAPES, lambda c: c[4]))
+def test_constant_values_give_exactly_that_value(case, kernel):
     # V == c on every visible key: whatever the weights, the output is
     # v_descale * c.  With c = 3 and v_descale = 0.625 that is 1.875, exact in
     # bf16, and every rounding the kernel makes is far below half a bf16 step,
@@ -227,7 +236,7 @@ def test_constant_values_give_exactly_that_value(case):
         keys = np.arange(int(p.seqused_k[b]))
         p.v[p.block_table[b, keys // 16], keys % 16] = code
     for grid in (0, 7, 300):
-        got = as_f64(run(p, force_grid=grid))
+        got = as_f64(run(p, force_grid=grid, kernel=kernel))
         note(f"  constant values grid {grid}: distinct outputs {np.unique(got)[:4]}")
         assert np.all(got == 1.875)
 
@@ -238,12 +247,20 @@ def test_constant_values_give_exactly_that_value(case):
 # workloads, at the plan's own grid (the launch configuration bench.py times),
 # against the oracle.
 
+def _both_kernels_all_rows(p):
+    """Both FP8 kernels (the plan's own choice among them) against the same
+    oracle rows."""
+    ref, _ = oracle.attn_problem(p)
+    for k in FP8_KERNELS:
+        compare(as_f64(run(p, kernel=k)), ref, f"{p.name} kernel {k}")
+
+
 def test_config2_long_context_all_rows():
-    check_problem(va_inputs.config(2))
+    _both_kernels_all_rows(va_inputs.config(2))
 
 
 def test_config3_high_concurrency_all_rows():
-    check_problem(va_inputs.config(3))
+    _both_kernels_all_rows(va_inputs.config(3))
 
 
 @pytest.mark.parametrize("variant", range(len(va_inputs.SWEEP_VARIANTS)),
