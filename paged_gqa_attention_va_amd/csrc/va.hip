@@ -211,6 +211,35 @@ __device__ __forceinline__ float exp2_fast(float x)
 // Maxima of values that come out of inline assembly: written as instructions
 // so that no canonicalising v_max x, x is put in front of each operand (the
 // inputs are never NaN where these are used).
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one row of a
+// 16-row MFMA tile).  A swizzle swaps the 16-lane halves of each 32-lane half
+// (no address register); the 32-lane step permutes with an address formed on
+// the spot from an opaque lane index, so that it is not formed once and held
+// (or spilled) for the whole kernel.  Bit for bit the two xor shuffles.
+__device__ __forceinline__ float xor16_lane(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+
+__device__ __forceinline__ float xor32_lane(float x)
+{
+    int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(l));
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((l ^ 32) << 2, __builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ float row4_max(float x)
+{
+    x = fmaxf(x, xor16_lane(x));
+    return fmaxf(x, xor32_lane(x));
+}
+
+__device__ __forceinline__ float row4_sum(float x)
+{
+    x += xor16_lane(x);
+    return x + xor32_lane(x);
+}
+
 __device__ __forceinline__ float max3f(float a, float b, float c)
 {
     float r;
@@ -237,6 +266,54 @@ __device__ __forceinline__ int load_uniform(const int32_t *base, int64_t idx)
 {
     typedef const __attribute__((address_space(4))) int32_t cint32;
     return ((cint32 *)base)[idx];
+}
+
+// Three scalar loads under one wait: a[0..2] are uniform addresses.  Written
+// out because the compiler, short of scalar registers, may otherwise give each
+// load a wait of its own, a memory latency apiece.
+__device__ __forceinline__ void load_uniform3(int (&v)[3], const int32_t *a0, const int32_t *a1, const int32_t *a2)
+{
+    asm volatile("s_load_dword %0, %3, 0x0\n\t"
+                 "s_load_dword %1, %4, 0x0\n\t"
+                 "s_load_dword %2, %5, 0x0\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&s"(v[0]), "=&s"(v[1]), "=&s"(v[2])
+                 : "s"(a0), "s"(a1), "s"(a2)
+                 : "memory");
+}
+
+// Ten block-table entries row[min(first + i, last)], i = 0..9, under one wait
+// (the same reason as load_uniform3).  first <= last, both within the row.
+__device__ __forceinline__ void load_entries10(int (&v)[10], const int32_t *row, int first, int last)
+{
+    const int32_t *a[10];
+#pragma unroll
+    for (int i = 0; i < 10; ++i)
+        a[i] = row + min(first + i, last);
+    asm volatile("s_load_dword %0, %10, 0x0\n\t"
+                 "s_load_dword %1, %11, 0x0\n\t"
+                 "s_load_dword %2, %12, 0x0\n\t"
+                 "s_load_dword %3, %13, 0x0\n\t"
+                 "s_load_dword %4, %14, 0x0\n\t"
+                 "s_load_dword %5, %15, 0x0\n\t"
+                 "s_load_dword %6, %16, 0x0\n\t"
+                 "s_load_dword %7, %17, 0x0\n\t"
+                 "s_load_dword %8, %18, 0x0\n\t"
+                 "s_load_dword %9, %19, 0x0\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&s"(v[0]), "=&s"(v[1]), "=&s"(v[2]), "=&s"(v[3]), "=&s"(v[4]),
+                   "=&s"(v[5]), "=&s"(v[6]), "=&s"(v[7]), "=&s"(v[8]), "=&s"(v[9])
+                 : "s"(a[0]), "s"(a[1]), "s"(a[2]), "s"(a[3]), "s"(a[4]),
+                   "s"(a[5]), "s"(a[6]), "s"(a[7]), "s"(a[8]), "s"(a[9])
+                 : "memory");
+}
+
+// A descale factor (one float, or 1 when the pointer is null) through the
+// scalar cache: the value then lives in a scalar register.  A vector-register
+// copy can be spilled, and its reload waits for every copy in flight.
+__device__ __forceinline__ float load_descale(const float *ptr)
+{
+    return ptr ? __builtin_bit_cast(float, load_uniform(reinterpret_cast<const int32_t *>(ptr), 0)) : 1.0f;
 }
 
 // Pages of (sequence, kv head) bg that hold keys for at least one query row.
@@ -1103,8 +1180,8 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
     if (w >= sh.n_eff)
         return;                                        // uniform over the workgroup
 
-    const float kd = p.kdesc ? p.kdesc[0] : 1.0f;
-    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
+    const float kd = load_descale(p.kdesc);
+    const float vd = load_descale(p.vdesc);
     const float c = p.scale_log2 * kd;
     unsigned char *ring = lds + kQBytes + kg * kRingBytes;
     const uint32_t ring_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(ring));
@@ -1570,8 +1647,7 @@ __device__ __forceinline__ void w4_softmax(RowState<RT> &st, bool &retry, bf16x8
                 t = fmaxf(t, x[rt][i]);
             if constexpr (!CAP)
                 t = t == -INFINITY ? -INFINITY : t * c[rt];
-            t = fmaxf(t, __shfl_xor(t, 16));
-            t = fmaxf(t, __shfl_xor(t, 32));                  // row max of this step
+            t = row4_max(t);                                  // row max of this step
             if (t > st.m[rt] + kTauW4) {
                 retry |= st.m[rt] != -INFINITY;                // else nothing is accumulated yet
                 st.m[rt] = t;
@@ -1831,8 +1907,7 @@ __device__ __forceinline__ void w4_convert_q(unsigned char *qst, float *cst, flo
         for (int i = 0; i < 16; ++i)
             amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, raw[kc][i] << 16)),
                                      fabsf(__builtin_bit_cast(float, raw[kc][i] & 0xFFFF0000u))));
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));             // row max (4 lanes)
+    amax = row4_max(amax);                               // row max (4 lanes)
     int k = 0;
     if (amax > 0.f) {
         int e;
@@ -1875,6 +1950,9 @@ __device__ __forceinline__ void w4_epilogue(RowState<RT> &st, unsigned char *lds
     (void)stamp;
     constexpr int NG = 4;
     const int G = 1 << p.log2g;
+    // lane-derived values are formed here, from an opaque copy of the lane:
+    // formed at the piece start they would be held (or spilled) across the loop
+    asm volatile("" : "+v"(lane));
     const int n = lane & 15, j = lane >> 4;
     const int R = min(lq * G, 16 * RT);
     unsigned char *own = lds + kg * kW4RingBytes;
@@ -1882,9 +1960,7 @@ __device__ __forceinline__ void w4_epilogue(RowState<RT> &st, unsigned char *lds
     float *mw = reinterpret_cast<float *>(lds + kW4Mw);                          // [row] (M, W), wave 0
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        float t = st.l[rt];
-        t += __shfl_xor(t, 16);
-        t += __shfl_xor(t, 32);
+        const float t = row4_sum(st.l[rt]);
         st.l[rt] = t;
         if (16 * rt < R && j == 0) {
             ml[(16 * rt + n) * 2] = st.m[rt];
@@ -1945,7 +2021,7 @@ __device__ __forceinline__ void w4_epilogue(RowState<RT> &st, unsigned char *lds
     if (stamp)
         VA_STAMP(p, blockIdx.x, kg, lane, 15, VA_NOW());
 #endif
-    const int tid = opaque_tid();
+    const int tid = kg * 64 + lane;
     const int c = tid & 31;
     // thread: chunk c of rows tid / 32 + 8 it; every row's four terms are read
     // first (rows past R re-read row R - 1 and are not stored)
@@ -2021,9 +2097,8 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
     VA_STAMP(p, w, kg, lane, 11, (unsigned long long)__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)));
 #endif
 
-    const float kd = p.kdesc ? p.kdesc[0] : 1.0f;
-    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
-    const float c = p.scale_log2 * kd;
+    const float kd = load_descale(p.kdesc);
+    const float vd = load_descale(p.vdesc);
     unsigned char *ring = lds + kg * kW4RingBytes;
     const uint32_t ring_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(ring));
     const int64_t page_bytes = (int64_t)kPage * p.hkv * kHeadDim;
@@ -2037,9 +2112,11 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
         dma_lane_offsets(off, p.hkv, pl);
         const int b = uniform(bg / p.hkv);
         const int g = bg - b * p.hkv;
-        const int q0 = load_uniform(p.cu, b);
-        const int lq = checked_q_len(q0, load_uniform(p.cu, b + 1), p.total_q, p.max_q);
-        const int lk = load_uniform(p.seqused, b);
+        int hdr[3];                                            // cu[b], cu[b + 1], seqused[b]
+        load_uniform3(hdr, p.cu + b, p.cu + b + 1, p.seqused + b);
+        const int q0 = hdr[0];
+        const int lq = checked_q_len(q0, hdr[1], p.total_q, p.max_q);
+        const int lk = hdr[2];
         const int pb = first_page(lk, lq, p.window_left);      // the range starts at logical page pb
         const int cnt = (lq <= 0 || lk <= 0) ? 0 : max(0, min((lk + kPage - 1) / kPage, p.mbps) - pb);
         if (cnt == 0) {
@@ -2104,38 +2181,47 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
             dma16(p.q + row0 * kHeadDim, (uint32_t)((pl >> 5) * 512 + ((sl ^ (rr & 15)) * 16)),
                   ring_addr + (uint32_t)(kW4QStage + 2 * i * 512));
         }
+        // The block-table entries of the first five steps' pages, in one batch of
+        // scalar loads while the Q rows are in flight: one latency, none at step 0.
+        int ent[10];
+        load_entries10(ent, btrow, lp0, p1 - 1);
+#pragma unroll
+        for (int i = 0; i < 10; ++i)
+            ent[i] = ent[i] < 0 ? 0 : (ent[i] > maxpage ? maxpage : ent[i]);
         // With the Q rows go K and V of pages 0, 1 and K of pages 2, 3; after the
         // exchange K of pages 4, 5 and V of pages 2, 3 (the exchange's slots).
-        int e2 = 0, e3 = 0, e4 = 0, e5 = 0;                    // block-table entries of pages 2 .. 5
         auto prologue_copies = [&](int part) {
             if (part == 0) {
                 if (nst > 0) {
-                    const int e0 = entry(0), e1 = entry(1);
-                    issue_k(e0, 0);
-                    issue_k(e1, 1);
-                    issue_v(e0, 0);
-                    issue_v(e1, 1);
+                    issue_k(ent[0], 0);
+                    issue_k(ent[1], 1);
+                    issue_v(ent[0], 0);
+                    issue_v(ent[1], 1);
                 }
-                e2 = entry(2);
-                e3 = entry(3);
-                e4 = entry(4);
-                e5 = entry(5);
                 if (nst > 1) {
-                    issue_k(e2, 2);
-                    issue_k(e3, 3);
+                    issue_k(ent[2], 2);
+                    issue_k(ent[3], 3);
                 }
             } else {
                 if (nst > 2) {
-                    issue_k(e4, 4);
-                    issue_k(e5, 5);
+                    issue_k(ent[4], 4);
+                    issue_k(ent[5], 5);
                 }
                 if (nst > 1) {
-                    issue_v(e2, 2);
-                    issue_v(e3, 3);
+                    issue_v(ent[2], 2);
+                    issue_v(ent[3], 3);
                 }
             }
         };
         prologue_copies(0);
+        RowState<RT> st;                                       // O starts at zero
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            st.m[rt] = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        }
         if (nst > 1)
             wait_vmcnt<24>();                                  // this wave's Q copies landed
         else if (nst > 0)
@@ -2147,8 +2233,14 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
         if (first_piece)
             VA_STAMP(p, w, kg, lane, 2, VA_NOW());
 #endif
-        if (kg < RT)
-            w4_convert_q(qst, cst, c, nr, pl);
+        if (kg < RT) {
+            // the logit multiplier, formed here from scalar registers: a vector
+            // copy kept across the pieces is spilled, and its reload would wait
+            // for every copy in flight
+            float kdp = kd;
+            asm volatile("" : "+s"(kdp));
+            w4_convert_q(qst, cst, p.scale_log2 * kdp, nr, pl);
+        }
         __syncthreads();                                       // every row tile converted
         intx8_t qop[RT][2][2];
         float crow[RT];
@@ -2173,22 +2265,19 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
 #endif
         prologue_copies(1);
 
-        RowState<RT> st;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-            st.m[rt] = -INFINITY;
         for (int pass = 0;; ++pass) {                          // a second pass only after `retry`
             if (pass > 0) {
                 prologue_copies(0);
                 prologue_copies(1);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int t = 0; t < 16; ++t)
+                        st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
+            for (int rt = 0; rt < RT; ++rt)
                 st.l[rt] = 0.f;
-#pragma unroll
-                for (int t = 0; t < 16; ++t)
-                    st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-            }
             bool retry = false;
             // Copies: the prologue issues K(0), V(0), K(1), K(2), V(1) (X(s) = the two
             // pages of step s); step t then refills its own slots as soon as it has
@@ -2197,8 +2286,8 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
             // (pages 2t + 6, 2t + 7), eV for V(t + 2) (pages 2t + 4, 2t + 5), eN for
             // the next step's K (pages 2t + 8, 2t + 9), loaded a step ahead (entry()
             // clamps to the piece, so the loads past its end are harmless).
-            int eK0 = entry(6), eK1 = entry(7), eV0 = e4, eV1 = e5;
-            int eN0 = entry(8), eN1 = entry(9);
+            int eK0 = ent[6], eK1 = ent[7], eV0 = ent[4], eV1 = ent[5];
+            int eN0 = ent[8], eN1 = ent[9];
             int ks = 0, vs = 0;                                // K / V slots of local page 2t
             for (int t = 0; t < nst; ++t) {
                 // K(t) must have landed.  Issued after it so far (in issue order, each
@@ -2482,8 +2571,8 @@ void va_split_kv_bf16_w8_kernel(SplitParams p)
     if (w >= sh.n_eff)
         return;                                        // uniform over the workgroup
 
-    const float kd = p.kdesc ? p.kdesc[0] : 1.0f;
-    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
+    const float kd = load_descale(p.kdesc);
+    const float vd = load_descale(p.vdesc);
     const float c = p.scale_log2 * kd;
     unsigned char *ring = lds + kQBytes + kg * kRingBytes;
     const uint32_t ring_addr = uniform((int)(uint32_t)reinterpret_cast<uintptr_t>(ring));
@@ -3028,8 +3117,8 @@ void va_mla_split_kernel(SplitParams p)
     if (w >= sh.n_eff)
         return;                                        // uniform over the workgroup
 
-    const float kd = p.kdesc ? p.kdesc[0] : 1.0f;
-    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
+    const float kd = load_descale(p.kdesc);
+    const float vd = load_descale(p.vdesc);
     const float c = p.scale_log2 * kd;
     unsigned char *qlds = lds;
     constexpr int PP = C::kPages;                      // pages per step of a key group
@@ -3442,7 +3531,7 @@ __global__ __launch_bounds__(kThreads) void va_merge_kernel(MergeParams p)
         acc.z *= f;
         acc.w *= f;
     }
-    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
+    const float vd = load_descale(p.vdesc);
     const float inv = den > 0.f ? vd / den : 0.f;
     uint2 pk;
     pk.x = pack_bf16x2(acc.x * inv, acc.y * inv);
