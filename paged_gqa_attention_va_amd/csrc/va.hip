@@ -3117,8 +3117,10 @@ void va_mla_split_kernel(SplitParams p)
     if (w >= sh.n_eff)
         return;                                        // uniform over the workgroup
 
-    const float kd = load_descale(p.kdesc);
-    const float vd = load_descale(p.vdesc);
+    // (vector loads here: with scalar ones the compiler schedules the PV's
+    // transposed reads one at a time, measured 4-8 % slower)
+    const float kd = p.kdesc ? p.kdesc[0] : 1.0f;
+    const float vd = p.vdesc ? p.vdesc[0] : 1.0f;
     const float c = p.scale_log2 * kd;
     unsigned char *qlds = lds;
     constexpr int PP = C::kPages;                      // pages per step of a key group
