@@ -1950,21 +1950,30 @@ __device__ __forceinline__ void w4_epilogue(RowState<RT> &st, unsigned char *lds
     (void)stamp;
     constexpr int NG = 4;
     const int G = 1 << p.log2g;
-    // lane-derived values are formed here, from an opaque copy of the lane:
-    // formed at the piece start they would be held (or spilled) across the loop
+    // lane-derived values are formed here, from the lane index read again
+    // (opaque): formed at the piece start they would be held (or spilled)
+    // across the page loop
+    lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     asm volatile("" : "+v"(lane));
     const int n = lane & 15, j = lane >> 4;
     const int R = min(lq * G, 16 * RT);
     unsigned char *own = lds + kg * kW4RingBytes;
     float *ml = reinterpret_cast<float *>(own + kW4Ml);                          // [row] (m, l)
     float *mw = reinterpret_cast<float *>(lds + kW4Mw);                          // [row] (M, W), wave 0
+    // the row sums of every row tile first, then their stores (between LDS
+    // stores the swizzles and permutes would run one row tile at a time)
+    const int x32 = (lane ^ 32) << 2;                   // the row sums' permute address, once
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+        st.l[rt] += xor16_lane(st.l[rt]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+        st.l[rt] += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, st.l[rt])));
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const float t = row4_sum(st.l[rt]);
-        st.l[rt] = t;
         if (16 * rt < R && j == 0) {
             ml[(16 * rt + n) * 2] = st.m[rt];
-            ml[(16 * rt + n) * 2 + 1] = t;
+            ml[(16 * rt + n) * 2 + 1] = st.l[rt];
         }
     }
     __syncthreads();                                     // every key group's row states are out
@@ -1972,10 +1981,13 @@ __device__ __forceinline__ void w4_epilogue(RowState<RT> &st, unsigned char *lds
     if (stamp)
         VA_STAMP(p, blockIdx.x, kg, lane, 13, VA_NOW());
 #endif
+    // every row tile's four states are read before any O is written: the
+    // compiler cannot tell the O writes from the state reads apart, and would
+    // otherwise wait out one LDS round trip per row tile (tiles past R read
+    // rows nobody wrote; their factors are not used)
+    float fr[RT], Mr[RT], Wr[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        if (16 * rt >= R)
-            break;                                       // uniform
         const int row = 16 * rt + n;
         float mk[NG], lk[NG];
         float M = -INFINITY;
@@ -1990,10 +2002,19 @@ __device__ __forceinline__ void w4_epilogue(RowState<RT> &st, unsigned char *lds
 #pragma unroll
         for (int k = 0; k < NG; ++k)
             W += lk[k] > 0.f ? lk[k] * exp2_fast(mk[k] - M) : 0.f;
-        const float f = (st.l[rt] > 0.f && W > 0.f) ? exp2_fast(st.m[rt] - M) / W : 0.f;
+        fr[rt] = (st.l[rt] > 0.f && W > 0.f) ? exp2_fast(st.m[rt] - M) / W : 0.f;
+        Mr[rt] = M;
+        Wr[rt] = W;
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        if (16 * rt >= R)
+            break;                                       // uniform
+        const int row = 16 * rt + n;
+        const float f = fr[rt];
         if (kg == 0 && j == 0) {
-            mw[row * 2] = M;
-            mw[row * 2 + 1] = W;
+            mw[row * 2] = Mr[rt];
+            mw[row * 2 + 1] = Wr[rt];
         }
         unsigned char *orow = own + (size_t)row * 512;
 #pragma unroll
