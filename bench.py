@@ -353,7 +353,8 @@ def ceiling(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed calls (default 200; 2000 for a workload under 64 MB, whose call is launch-bound)")
     ap.add_argument("--warmup", type=int, default=200, help="untimed steps before timing")
     ap.add_argument("--warmup-seconds", type=float, default=3.0,
                     help="keep running untimed steps for at least this long (memory and core "
@@ -412,6 +413,8 @@ def main():
         return
 
     if args.ceiling:
+        if args.steps is None:
+            args.steps = 200
         ceiling(args)
         return
 
@@ -523,6 +526,9 @@ def main():
     log(f"bench: plan grid={plan.grid} workspace={plan.workspace_bytes} B, "
         f"{args.copies} pool copies of {2 * k0.numel() * k0.element_size() / 2**20:.0f} MiB")
 
+    if args.steps is None:
+        alg0 = algorithmic_bytes_pe(pe) if pe is not None else algorithmic_bytes(p)
+        args.steps = 2000 if alg0 < (64 << 20) else 200
     stages = {"all": (va.VA_STAGE_SPLIT_KV, va.VA_STAGE_MERGE), "split": (va.VA_STAGE_SPLIT_KV,),
               "merge": (va.VA_STAGE_MERGE,)}[args.stage]
 
