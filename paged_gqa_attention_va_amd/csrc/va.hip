@@ -234,12 +234,6 @@ __device__ __forceinline__ float row4_max(float x)
     return fmaxf(x, xor32_lane(x));
 }
 
-__device__ __forceinline__ float row4_sum(float x)
-{
-    x += xor16_lane(x);
-    return x + xor32_lane(x);
-}
-
 __device__ __forceinline__ float max3f(float a, float b, float c)
 {
     float r;
