@@ -339,15 +339,24 @@ __device__ __forceinline__ int prefix_keys(int s0, int s1, int lq, int64_t num_i
 // last page holding a key below the sequence's key count (clamped to the
 // block-table row).  In the prefix + extend layout a "page" is 16 consecutive
 // keys of the sequence.
-__device__ __forceinline__ int pages_of(const SplitParams &p, int bg)
+// The loaded words are also returned: cu_seqlens_q[b], cu_seqlens_q[b + 1] and
+// seqused_k[b] (paged layout; the key count in the prefix + extend layout).
+__device__ __forceinline__ int pages_of(const SplitParams &p, int bg, int &q0, int &q1, int &lk)
 {
     const int b = bg / p.hkv;
-    const int lq = checked_q_len(p.cu[b], p.cu[b + 1], p.total_q, p.max_q);
-    const int lk = p.kv_indptr ? prefix_keys(p.kv_indptr[b], p.kv_indptr[b + 1], lq, p.num_indices)
-                               : p.seqused[b];
+    q0 = p.cu[b];
+    q1 = p.cu[b + 1];
+    const int lq = checked_q_len(q0, q1, p.total_q, p.max_q);
+    lk = p.kv_indptr ? prefix_keys(p.kv_indptr[b], p.kv_indptr[b + 1], lq, p.num_indices) : p.seqused[b];
     if (lq <= 0 || lk <= 0)
         return 0;
     return max(0, min((lk + kPage - 1) / kPage, p.mbps) - first_page(lk, lq, p.window_left));
+}
+
+__device__ __forceinline__ int pages_of(const SplitParams &p, int bg)
+{
+    int q0, q1, lk;
+    return pages_of(p, bg, q0, q1, lk);
 }
 
 __device__ __forceinline__ uint32_t u4get(const uint4 &u, int i)
@@ -530,6 +539,7 @@ struct Share {
     int s, e;       // flat page range of this workgroup
     int bg, base;   // first (sequence, kv head) touching s and its flat start
     int total;      // pages over all (sequence, kv head) pairs
+    int q0, q1, lk; // pages_of's loaded words for pair bg (valid when bg < pairs)
 };
 
 // Work split (stream-K over pages).  The (sequence, kv head) pairs are laid
@@ -576,13 +586,14 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
     const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;   // lanes < this one
     Share sh;
     sh.s = sh.e = sh.base = 0;
+    sh.q0 = sh.q1 = sh.lk = 0;
     sh.bg = bh;
     // One chunk of up to 64 pairs, lane = pair: page counts, their prefix, the
     // pairs whose start falls inside a share and the prefix of the costs; then
     // the pairs holding the cost positions cs and ce of this workgroup's share.
     // With at most 64 pairs everything comes from one load of the counts.
     auto chunk = [&](int c0, int cnt, int incl, int base, int cbase, int total, int n, int64_t cs, int64_t ce,
-                     bool &found_s, bool &found_e) {
+                     bool &found_s, bool &found_e, int rq0, int rq1, int rlk) {
         const int bg = c0 + lane;
         const int pb = base + incl - cnt;              // this lane's pair: first page
         const bool inside = C > 0 && bg < bh && bg > 0 && cnt > 0 && !starts_a_share(pb, total, n);
@@ -602,6 +613,9 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
                 sh.bg = c0 + ln;
                 sh.base = __builtin_amdgcn_readlane(pb, ln);
                 sh.s = __builtin_amdgcn_readlane(pg, ln);
+                sh.q0 = __builtin_amdgcn_readlane(rq0, ln);
+                sh.q1 = __builtin_amdgcn_readlane(rq1, ln);
+                sh.lk = __builtin_amdgcn_readlane(rlk, ln);
                 found_s = true;
             }
         }
@@ -624,7 +638,8 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
         }
     };
     if (bh <= 64) {
-        const int cnt = lane < bh ? pages_of(p, lane) : 0;
+        int rq0 = 0, rq1 = 0, rlk = 0;
+        const int cnt = lane < bh ? pages_of(p, lane, rq0, rq1, rlk) : 0;
         const int incl = wave_scan_dpp(cnt);
         const int total = __builtin_amdgcn_readlane(incl, 63);
         const int n = min(p.grid_n, max(1, total / max(1, p.min_pages)));
@@ -635,7 +650,7 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
         const int64_t cs = ((int64_t)w * T) / n, ce = ((int64_t)(w + 1) * T) / n;
         sh.s = sh.e = sh.base = total;
         bool found_s = false, found_e = false;
-        chunk(0, cnt, incl, 0, 0, total, n, cs, ce, found_s, found_e);
+        chunk(0, cnt, incl, 0, 0, total, n, cs, ce, found_s, found_e, rq0, rq1, rlk);
         finish(total, n, T);
         return sh;
     }
@@ -665,10 +680,11 @@ __device__ Share locate(const SplitParams &p, int w, int lane, bool write_prefix
     int base = 0, cbase = 0;
     for (int c0 = 0; c0 < bh; c0 += 64) {
         const int bg = c0 + lane;
-        const int cnt = bg < bh ? pages_of(p, bg) : 0;
+        int rq0 = 0, rq1 = 0, rlk = 0;
+        const int cnt = bg < bh ? pages_of(p, bg, rq0, rq1, rlk) : 0;
         const int incl = wave_scan_dpp(cnt);
         const int ctotal = __builtin_amdgcn_readlane(incl, 63);
-        cbase += ctotal + chunk(c0, cnt, incl, base, cbase, total, n, cs, ce, found_s, found_e);
+        cbase += ctotal + chunk(c0, cnt, incl, base, cbase, total, n, cs, ce, found_s, found_e, rq0, rq1, rlk);
         base += ctotal;
         if (found_s && found_e && !write_prefix)
             break;
@@ -1381,17 +1397,19 @@ void va_split_kv_fp8_w8_kernel(SplitParams p)
 // banks; V rows are unswizzled, see w4_pv).  It copies its own pages into them and waits for them with vmcnt
 // alone: no workgroup barrier inside the page loop, so the four waves run
 // their steps independently.  Step t computes the wave's local pages 2t and
-// 2t + 1; at its top the wave copies K of pages 2t + 4, 2t + 5 and V of pages
-// 2t + 2, 2t + 3 into the slots step t - 1 used.  K therefore arrives two
-// steps ahead of its QK and V one step ahead (plus the QK and softmax of its
-// own step) of its PV: one step of lead was less than the memory latency of a
-// loaded GPU.
+// 2t + 1 and refills its own slots as soon as it has read them: K of step
+// t + 3 once its K reads have returned, V of step t + 2 once its V reads have.
+// K therefore arrives about three steps ahead of its QK and V two steps ahead
+// of its PV (one step of lead was less than the memory latency of a loaded GPU).
 //
-// Prologue of a piece: wave kg copies the bf16 rows of row tile kg into V
-// slots 2 and 3, converts them in place into the hi / lo operands, and puts
-// the rows' logit multipliers into K slot 4; after a barrier every wave loads
-// all row tiles' operands into registers; after a second barrier (every wave
-// holds them) those slots are handed back to the rings.
+// Prologue of a piece: wave kg copies the bf16 rows of row tile kg into K
+// slots 4 and 5, converts them in place into the hi / lo operands, and puts
+// the rows' logit multipliers into the last KiB of V slot 3; after a barrier
+// every wave loads all row tiles' operands into registers; after a second
+// barrier (every wave holds them) those slots are handed back to the rings.
+// The copies of steps 0 and 1 (all but that last KiB) go out with the Q rows,
+// so only K of step 2 and one KiB of V wait for the exchange: the memory
+// system has about 40 KiB per wave to fetch while the rows are converted.
 // Epilogue: each wave writes its rows' m, l and scaled O (fp16) into its own
 // 40 KiB (see w4_epilogue); after barriers all 256 threads combine them.
 constexpr int kW4KSlots = 6;
@@ -1399,8 +1417,8 @@ constexpr int kW4VSlots = 4;
 constexpr int kW4PageBytes = 4096;                          // one page of one kv head, K or V
 constexpr int kW4VBase = kW4KSlots * kW4PageBytes;           // V ring offset in a wave's region
 constexpr int kW4RingBytes = (kW4KSlots + kW4VSlots) * kW4PageBytes;   // 40 KiB per wave, 160 KiB in all
-constexpr int kW4QStage = kW4VBase + 2 * kW4PageBytes;       // prologue: row tile (V slots 2, 3)
-constexpr int kW4CStage = 4 * kW4PageBytes;                  // prologue: row multipliers (K slot 4)
+constexpr int kW4QStage = 4 * kW4PageBytes;                  // prologue: row tile (K slots 4, 5)
+constexpr int kW4CStage = kW4VBase + 3 * kW4PageBytes + 3072; // prologue: row multipliers (V slot 3, last KiB)
 constexpr int kW4Ml = 8 * kW4PageBytes;                      // epilogue: (m, l) of the rows (V slot 2)
 constexpr int kW4Mw = kW4Ml + 512;                           // epilogue: (M, W) of the rows (wave 0)
 
@@ -2104,6 +2122,9 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
     sh.e = uniform(sh.e);
     sh.bg = uniform(sh.bg);
     sh.base = uniform(sh.base);
+    sh.q0 = uniform(sh.q0);
+    sh.q1 = uniform(sh.q1);
+    sh.lk = uniform(sh.lk);
     if (w >= sh.n_eff)
         return;                                        // uniform over the workgroup
     VA_STAMP(p, w, kg, lane, 1, VA_NOW());
@@ -2128,7 +2149,13 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
         const int b = uniform(bg / p.hkv);
         const int g = bg - b * p.hkv;
         int hdr[3];                                            // cu[b], cu[b + 1], seqused[b]
-        load_uniform3(hdr, p.cu + b, p.cu + b + 1, p.seqused + b);
+        if (bg == sh.bg) {                                     // loaded by locate() already
+            hdr[0] = sh.q0;
+            hdr[1] = sh.q1;
+            hdr[2] = sh.lk;
+        } else {
+            load_uniform3(hdr, p.cu + b, p.cu + b + 1, p.seqused + b);
+        }
         const int q0 = hdr[0];
         const int lq = checked_q_len(q0, hdr[1], p.total_q, p.max_q);
         const int lk = hdr[2];
@@ -2175,11 +2202,11 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
 #pragma unroll
         for (int x = 0; x < 4; ++x)
             off_v[x] = (uint32_t)((4 * x + (pl >> 4)) * p.hkv * kHeadDim + 16 * (pl & 15));
-        auto issue_v = [&](int y, int slot_i) {                // V of pool page y into V slot slot_i
-            const uint8_t *src_pg = vpool + (int64_t)y * page_bytes;
+        auto issue_v = [&](int y, int slot_i, int x0 = 0, int x1 = 4) {   // V of pool page y (rows 4 x0 ..
+            const uint8_t *src_pg = vpool + (int64_t)y * page_bytes;     // 4 x1 - 1) into V slot slot_i
             const uint32_t dst = ring_addr + (uint32_t)(kW4VBase + slot_i * kW4PageBytes);
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+            for (int x = x0; x < x1; ++x)
                 dma16(src_pg, off_v[x], dst + 1024 * x);
         };
 
@@ -2203,8 +2230,10 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
 #pragma unroll
         for (int i = 0; i < 10; ++i)
             ent[i] = ent[i] < 0 ? 0 : (ent[i] > maxpage ? maxpage : ent[i]);
-        // With the Q rows go K and V of pages 0, 1 and K of pages 2, 3; after the
-        // exchange K of pages 4, 5 and V of pages 2, 3 (the exchange's slots).
+        // With the Q rows go K and V of pages 0 .. 3 (31 copies: the last KiB of
+        // V page 3 is the exchange's multiplier area); after the exchange that
+        // KiB and K of pages 4, 5 (the exchange's row area).  Issue order, which
+        // the waits below count: K(0) V(0) K(1) V(1)' | V(1)'' K(2).
         auto prologue_copies = [&](int part) {
             if (part == 0) {
                 if (nst > 0) {
@@ -2216,15 +2245,15 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
                 if (nst > 1) {
                     issue_k(ent[2], 2);
                     issue_k(ent[3], 3);
+                    issue_v(ent[2], 2);
+                    issue_v(ent[3], 3, 0, 3);
                 }
             } else {
+                if (nst > 1)
+                    issue_v(ent[3], 3, 3, 4);
                 if (nst > 2) {
                     issue_k(ent[4], 4);
                     issue_k(ent[5], 5);
-                }
-                if (nst > 1) {
-                    issue_v(ent[2], 2);
-                    issue_v(ent[3], 3);
                 }
             }
         };
@@ -2238,7 +2267,7 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
                 st.o[t][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
         }
         if (nst > 1)
-            wait_vmcnt<24>();                                  // this wave's Q copies landed
+            wait_vmcnt<31>();                                  // this wave's Q copies landed
         else if (nst > 0)
             wait_vmcnt<16>();
         else
@@ -2294,10 +2323,10 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
             for (int rt = 0; rt < RT; ++rt)
                 st.l[rt] = 0.f;
             bool retry = false;
-            // Copies: the prologue issues K(0), V(0), K(1), K(2), V(1) (X(s) = the two
-            // pages of step s); step t then refills its own slots as soon as it has
-            // read them: K(t + 3) once its K reads have returned, V(t + 2) once its V
-            // reads have.  Block-table entries at the start of step t: eK for K(t + 3)
+            // Copies: the prologue issues K(0), V(0), K(1), V(1), K(2) (X(s) = the two
+            // pages of step s; the last KiB of V(1) just before K(2)); step t then
+            // refills its own slots as soon as it has read them: K(t + 3) once its K
+            // reads have returned, V(t + 2) once its V reads have.  Block-table entries at the start of step t: eK for K(t + 3)
             // (pages 2t + 6, 2t + 7), eV for V(t + 2) (pages 2t + 4, 2t + 5), eN for
             // the next step's K (pages 2t + 8, 2t + 9), loaded a step ahead (entry()
             // clamps to the piece, so the loads past its end are harmless).
@@ -2306,9 +2335,9 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
             int ks = 0, vs = 0;                                // K / V slots of local page 2t
             for (int t = 0; t < nst; ++t) {
                 // K(t) must have landed.  Issued after it so far (in issue order, each
-                // 8 copies): at t = 0, 1: V(t), K(t+1) and V(t+1) if t+1 < nst, K(t+2)
-                // if t+2 < nst; from t = 2 on also V(t-1)
-                wait_vmcnt_x8(8 * ((t >= 2 ? 2 : 1) + 2 * (t + 1 < nst) + (t + 2 < nst)));
+                // 8 copies): V(t), K(t+1) and V(t+1) if t+1 < nst, K(t+2) if t+2 < nst;
+                // from t = 3 on also V(t-1) (V(1) precedes K(2))
+                wait_vmcnt_x8(8 * ((t >= 3 ? 2 : 1) + 2 * (t + 1 < nst) + (t + 2 < nst)));
 #ifdef VA_STAMPS
                 if (first_piece && pass == 0 && t <= 1)
                     VA_STAMP(p, w, kg, lane, 4 + t, VA_NOW());
@@ -2358,8 +2387,8 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
                                       crow, ln, after_k);
                 }
                 // V(t) must have landed.  Issued after it so far: V(t+1), K(t+2) and
-                // K(t+3) where those steps exist, and at t = 0 also K(1)
-                wait_vmcnt_x8(8 * ((t + 1 < nst) * (t == 0 ? 2 : 1) + (t + 2 < nst) + (t + 3 < nst)));
+                // K(t+3) where those steps exist, and at t = 0, 1 also K(t+1)
+                wait_vmcnt_x8(8 * ((t + 1 < nst) * (t <= 1 ? 2 : 1) + (t + 2 < nst) + (t + 3 < nst)));
                 __builtin_amdgcn_sched_barrier(0);
                 w4_pv<RT>(st, va, va + kW4PageBytes, pop, masked, masked ? v_zero_mask(key0, hb, lk, ln) : 0u, ln,
                           after_v);
