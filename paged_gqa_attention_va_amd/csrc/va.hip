@@ -2073,32 +2073,54 @@ __device__ __forceinline__ void w4_epilogue(RowState<RT> &st, unsigned char *lds
             s[it].w = h2add(s[it].w, v.w);
         }
     }
+    // The stores.  Everything an item's address and scale need is copied into
+    // vector registers once (free here): kept in scalar registers, the kernel's
+    // parameters are restored from their spill lanes for every item.
+    const int r0 = tid >> 5;
+    if (whole) {
+        uint64_t ob = reinterpret_cast<uint64_t>(p.out + 8 * c);
+        int rowb = q0 * p.hq + g * G, hq = p.hq, lg = p.log2g;
+        float vdv = vd;
+        uint64_t sk = reinterpret_cast<uint64_t>(p.sinks ? p.sinks + g * G : nullptr);
+        asm volatile("" : "+v"(ob), "+v"(rowb), "+v"(hq), "+v"(lg), "+v"(vdv), "+v"(sk));
+        const bool has_sinks = p.sinks != nullptr;
 #pragma unroll
-    for (int it = 0; it < 2 * RT; ++it) {
-        const int r = (tid >> 5) + 8 * it;
-        if (r >= R)
-            break;
-        const float M = mw[r * 2], W = mw[r * 2 + 1];
-        const int t = r >> p.log2g, h = r & (G - 1);
-        if (whole) {
-            float sc = W > 0.f ? vd : 0.f;
-            if (p.sinks) {                               // the sink joins the denominator only
-                const float sk = p.sinks[g * G + h] * 1.4426950408889634f;
-                const float mm = fmaxf(M, sk);
+        for (int it = 0; it < 2 * RT; ++it) {
+            const int r = r0 + 8 * it;
+            if (r >= R)
+                break;
+            const float M = mw[r * 2], W = mw[r * 2 + 1];
+            const int t = r >> lg, h = r & ((1 << lg) - 1);
+            float sc = W > 0.f ? vdv : 0.f;
+            if (has_sinks) {                             // the sink joins the denominator only
+                const float skl = reinterpret_cast<const float *>(sk)[h] * 1.4426950408889634f;
+                const float mm = fmaxf(M, skl);
                 const float Wf = W > 0.f ? W * exp2_fast(M - mm) : 0.f;
-                sc = vd * Wf / (Wf + exp2_fast(sk - mm));
+                sc = vdv * Wf / (Wf + exp2_fast(skl - mm));
             }
             uint4 o;
             o.x = pack_bf16x2(f16_lo(s[it].x) * sc, f16_hi(s[it].x) * sc);
             o.y = pack_bf16x2(f16_lo(s[it].y) * sc, f16_hi(s[it].y) * sc);
             o.z = pack_bf16x2(f16_lo(s[it].z) * sc, f16_hi(s[it].z) * sc);
             o.w = pack_bf16x2(f16_lo(s[it].w) * sc, f16_hi(s[it].w) * sc);
-            *reinterpret_cast<uint4 *>(p.out + ((int64_t)(q0 + t) * p.hq + g * G + h) * kHeadDim + 8 * c) = o;
-        } else {                                         // fp16 partial O / l as summed
-            const int64_t sr = ((int64_t)slot * p.rows_max + r) * kHeadDim + 8 * c;
-            *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.ws_o) + sr) = s[it];
-            if (c == 0)
-                p.ws_lse[(int64_t)slot * p.rows_max + r] = W > 0.f ? M + __log2f(W) : -INFINITY;
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(ob) +
+                                       (int64_t)(rowb + t * hq + h) * kHeadDim) = o;
+        }
+    } else {                                             // fp16 partial O / l as summed, and the LSE
+        const int64_t row0 = (int64_t)slot * p.rows_max;
+        uint64_t wb = reinterpret_cast<uint64_t>(static_cast<uint16_t *>(p.ws_o) + row0 * kHeadDim + 8 * c);
+        uint64_t lb = reinterpret_cast<uint64_t>(p.ws_lse + row0);
+        asm volatile("" : "+v"(wb), "+v"(lb));
+#pragma unroll
+        for (int it = 0; it < 2 * RT; ++it) {
+            const int r = r0 + 8 * it;
+            if (r >= R)
+                break;
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(wb) + (int64_t)r * kHeadDim) = s[it];
+            if (c == 0) {
+                const float M = mw[r * 2], W = mw[r * 2 + 1];
+                reinterpret_cast<float *>(lb)[r] = W > 0.f ? M + __log2f(W) : -INFINITY;
+            }
         }
     }
 }
@@ -2915,9 +2937,12 @@ __device__ __forceinline__ MlaLane mla_lane(int rt, int lane)
 
 // S^T (16 keys x 16 rows of row tile rt) of the two pages of a step, FP8: 5
 // chunks of 128 dims (the last one half empty: dims 576..639 are zero in Q),
-// Q as the exact hi + lo pair, each Q operand read once for both pages.
+// Q as the exact hi + lo pair, each Q operand used for both pages.  The hi
+// operands come from registers (qhi[c], loaded once per piece), the lo ones
+// from LDS: with both read from LDS in every step the kernel ran 2-5 % slower
+// (LDS bandwidth; register room is left for one of the two).
 __device__ __forceinline__ void mla_qk_f8(floatx4_t (&S)[2], const unsigned char *stage, const unsigned char *qlds,
-                                          const MlaLane &ad, int lane)
+                                          const MlaLane &ad, int lane, const intx8_t (&qhi)[5])
 {
     constexpr int kPageBytes = 16 * kMlaDim;
     const int j = lane >> 4;
@@ -2942,10 +2967,15 @@ __device__ __forceinline__ void mla_qk_f8(floatx4_t (&S)[2], const unsigned char
         }
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
-            const uint4 *qp = reinterpret_cast<const uint4 *>(qlds + ad.q + (2 * c + part) * 2048);
-            const uint4 q0 = qp[0], q1 = qp[64];
-            const intx8_t qop = intx8_t{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w,
-                                        (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+            intx8_t qop;
+            if (part == 0) {
+                qop = qhi[c];
+            } else {
+                const uint4 *qp = reinterpret_cast<const uint4 *>(qlds + ad.q + (2 * c + part) * 2048);
+                const uint4 q0 = qp[0], q1 = qp[64];
+                qop = intx8_t{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w,
+                              (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+            }
             Sp[0][part] = mfma16_f8(kop[0], qop, Sp[0][part]);
             Sp[1][part] = mfma16_f8(kop[1], qop, Sp[1][part]);
         }
@@ -3328,6 +3358,7 @@ void va_mla_split_kernel(SplitParams p)
         }
 
         const MlaLane ad = mla_lane<KVT>(rt, pl);          // the loop's LDS offsets: 9 registers
+        intx8_t qhi[5];                                    // FP8: hi operands of the row tile
         for (int t = 0; t < nsteps; ++t) {
             const int k = kg + 2 * t;                      // block of the piece
             if (KVT == kKvFp8 && t == 0)
@@ -3335,6 +3366,15 @@ void va_mla_split_kernel(SplitParams p)
             else
                 wait_vmcnt<0>();
             __syncthreads();                               // the group's copies too; stage t-1 free
+            if (KVT == kKvFp8 && t == 0) {                 // the Q operands are visible now
+#pragma unroll
+                for (int c = 0; c < 5; ++c) {
+                    const uint4 *qp = reinterpret_cast<const uint4 *>(qlds + ad.q + (2 * c) * 2048);
+                    const uint4 q0 = qp[0], q1 = qp[64];
+                    qhi[c] = intx8_t{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w,
+                                     (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+                }
+            }
             if (t >= 1 && k + 2 < nblk)
                 issue(k + 2, (t + 1) & 1);
             if (k < nblk && rows_live) {
@@ -3352,7 +3392,7 @@ void va_mla_split_kernel(SplitParams p)
                         mla_zero_rows<C::kRowBytes>(ring + (t & 1) * PP * kPageBytes, 2, lk - key0,
                                                     hasb ? lk - key0 - 16 : 0, ln);
                     floatx4_t S[2];
-                    mla_qk_f8(S, stage, qlds, ad, ln);
+                    mla_qk_f8(S, stage, qlds, ad, ln, qhi);
                     const bf16x8_t pop = mla_softmax2(st, S, limit, key0, crow, ln, masked, hasb);
                     mla_pv_f8(st, stage, pop, ad);
                 } else {
