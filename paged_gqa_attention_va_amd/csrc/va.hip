@@ -2986,8 +2986,13 @@ __device__ __forceinline__ void mla_qk_f8(floatx4_t (&S)[2], const unsigned char
 }
 
 // The same for a bf16 cache: 18 slices of 32 dims on v_mfma_f32_16x16x32_bf16.
+// The Q operands of the first kMlaQRegBf16 slices come from registers (qreg,
+// loaded once per piece), the rest from LDS: the registers left beside the
+// accumulators hold 12 slices, and fewer LDS reads per step made the bf16 MLA
+// kernel 4-5 % faster (8 slices: 3 %, 14: 2 %).
+constexpr int kMlaQRegBf16 = 12;
 __device__ __forceinline__ floatx4_t mla_qk_bf16(const unsigned char *stage, const unsigned char *qlds,
-                                                 const MlaLane &ad)
+                                                 const MlaLane &ad, const bf16x8_t (&qreg)[kMlaQRegBf16])
 {
     floatx4_t Sp[3];                                   // 3 independent chains
 #pragma unroll
@@ -2996,7 +3001,8 @@ __device__ __forceinline__ floatx4_t mla_qk_bf16(const unsigned char *stage, con
 #pragma unroll
     for (int s = 0; s < 18; ++s) {
         const bf16x8_t kop = *reinterpret_cast<const bf16x8_t *>(stage + ((s & 1) ? ad.k1 : ad.k0) + 64 * s);
-        const bf16x8_t qop = *reinterpret_cast<const bf16x8_t *>(qlds + ad.q + 1024 * s);
+        const bf16x8_t qop = s < kMlaQRegBf16 ? qreg[s < kMlaQRegBf16 ? s : 0]      // (index kept in range)
+                                              : *reinterpret_cast<const bf16x8_t *>(qlds + ad.q + 1024 * s);
         Sp[s % 3] = mfma16(kop, qop, Sp[s % 3]);
     }
     return (Sp[0] + Sp[1]) + Sp[2];
@@ -3359,6 +3365,7 @@ void va_mla_split_kernel(SplitParams p)
 
         const MlaLane ad = mla_lane<KVT>(rt, pl);          // the loop's LDS offsets: 9 registers
         intx8_t qhi[5];                                    // FP8: hi operands of the row tile
+        bf16x8_t qreg[kMlaQRegBf16];                       // bf16: the first Q slices
         for (int t = 0; t < nsteps; ++t) {
             const int k = kg + 2 * t;                      // block of the piece
             if (KVT == kKvFp8 && t == 0)
@@ -3374,6 +3381,11 @@ void va_mla_split_kernel(SplitParams p)
                     qhi[c] = intx8_t{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w,
                                      (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
                 }
+            }
+            if (KVT == kKvBf16 && t == 0) {
+#pragma unroll
+                for (int sl = 0; sl < kMlaQRegBf16; ++sl)
+                    qreg[sl] = *reinterpret_cast<const bf16x8_t *>(qlds + ad.q + 1024 * sl);
             }
             if (t >= 1 && k + 2 < nblk)
                 issue(k + 2, (t + 1) & 1);
@@ -3399,7 +3411,7 @@ void va_mla_split_kernel(SplitParams p)
                     const bool masked = key0 + 15 > ctx;
                     if (key0 + 15 >= lk)                           // uniform: rows past the end
                         mla_zero_rows<C::kRowBytes>(ring + (t & 1) * kPageBytes, 1, lk - key0, 0, ln);
-                    const floatx4_t S = mla_qk_bf16(stage, qlds, ad);
+                    const floatx4_t S = mla_qk_bf16(stage, qlds, ad, qreg);
                     const shortx4_t pop = mla_softmax(st, S, limit, key0, crow, ln, masked);
                     mla_pv_bf16(st, stage, pop, ad);
                 }
