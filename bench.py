@@ -189,12 +189,17 @@ class HipEvents:
 
 def stamp_report(st: np.ndarray, grid: int) -> dict:
     """Phase times (us, from the earliest kernel entry) of one traced call, from the
-    per-wave timestamps of a VA_STAMPS library (16 words per wave, see va.h)."""
-    w = st.reshape(grid, 4, 16).astype(np.int64)
+    per-wave timestamps of a VA_STAMPS library (32 words per wave, see va.h)."""
+    w = st.reshape(grid, 4, 32).astype(np.int64)
     live = w[:, 0, 1] > 0                                  # workgroups that found work
     if not live.any():                                     # the kernel that ran records no stamps
         return None
-    w = w[live]
+    w = w[live].copy()
+    # slots 4, 5 and 16..19 hold the low 32 bits of the 100 MHz clock (taken
+    # inside the page loop); the full value is the page-loop end (slot 6, full)
+    # minus the 32-bit distance back to it
+    for k in (4, 5, 16, 17, 18, 19):
+        w[:, :, k] = w[:, :, 6] - ((w[:, :, 6] - w[:, :, k]) & 0xFFFFFFFF)
     t0 = w[:, :, 0].min()
     us = lambda x: (x - t0) / 100.0                        # 100 MHz clock -> us
     med = lambda a: round(float(np.median(a)), 2)
@@ -219,6 +224,15 @@ def stamp_report(st: np.ndarray, grid: int) -> dict:
            "us_per_step_median": med(per_step[first & (steps > 1)]),
            "pieces_max": int(w[:, :, 10].max()),
            "second_passes": int((w[:, :, 12] > 1).sum())}
+    # the middle step of the first piece: its phases and the shader clock
+    mid = first & (steps >= 2)
+    if mid.any():
+        ph = lambda a, b: med((w[:, :, b] - w[:, :, a])[mid] / 100.0)
+        span = (w[:, :, 19] - w[:, :, 16])[mid] / 100.0             # us, K landed .. PV done
+        cyc = ((w[:, :, 21] - w[:, :, 20]) & 0xFFFFFFFF)[mid]
+        rep.update({"mid_step_us": med(span), "mid_step_qk_softmax_us": ph(16, 17),
+                    "mid_step_v_wait_us": ph(17, 18), "mid_step_pv_us": ph(18, 19),
+                    "shader_clock_mhz": round(float(np.median(cyc / np.maximum(span, 1e-3))), 0)})
     return rep
 
 
@@ -647,7 +661,7 @@ def main():
     if args.stamps and pe is None:
         # every call of a back-to-back run overwrites the buffer: it ends up holding
         # the last call, in steady state
-        buf = torch.zeros(plan.grid * 4 * 16, dtype=torch.int64, device=dev)
+        buf = torch.zeros(plan.grid * 4 * 32, dtype=torch.int64, device=dev)
         va.set_stamp_buffer(buf)
         torch.cuda.synchronize()
         for i in range(args.steps):

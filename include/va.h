@@ -272,9 +272,11 @@ va_status va_run_noalloc(va_plan_t plan, const void *q, const void *k_pool, cons
  * Diagnostic.  A library compiled with -DVA_STAMPS records, for every wave of
  * the FP8 paged main kernel, the GPU's constant 100 MHz clock at the phase
  * boundaries of its first piece (work located, Q landed, Q operands loaded,
- * first and second steps' pages landed, page loop done, epilogue done) and at
- * exit, plus step, piece and pass counts and the wave's XCD, into `buffer`:
- * 16 uint64 words per wave, wave kg (0..3) of workgroup w at (w * 4 + kg) * 16.
+ * first and second steps' pages landed, page loop done, epilogue phases) and at
+ * exit, the phases of the piece's middle step (K landed, QK and softmax, V
+ * landed, PV) with the shader clock counter around it, plus step, piece and
+ * pass counts and the wave's XCD, into `buffer`: 32 uint64 words per wave, wave
+ * kg (0..3) of workgroup w at (w * 4 + kg) * 32.
  * `buffer` is a device pointer of `bytes` bytes; runs whose grid does not fit
  * record nothing.  NULL turns recording off.  The setting is process-wide.
  * Without VA_STAMPS this returns VA_ERR_UNSUPPORTED and records nothing.

@@ -131,9 +131,14 @@ struct MergeParams {
 // epilogue done (these six for the workgroup's first piece), 8 exit, 9 steps
 // of the first piece, 10 pieces, 11 XCD of the workgroup, 12 page-loop passes
 // of the first piece, 13..15 the epilogue of the first piece: row states
-// exchanged, scaled O published, all published.  Without VA_STAMPS the
-// statements compile to nothing.
-constexpr int kStampSlots = 16;
+// exchanged, scaled O published, all published; 16..19 the middle step
+// (nst / 2) of the first piece's first pass: its K landed, QK and softmax
+// done, its V landed, PV done; 20, 21 the shader clock counter (s_memtime) at
+// that step's K landing and PV end.  Stamps taken inside the page loop (4, 5,
+// 16..21) keep the low 32 bits only, held in registers and written after the
+// loop: a store there would be counted by the vmcnt waits of the copy ring.
+// Without VA_STAMPS the statements compile to nothing.
+constexpr int kStampSlots = 32;
 #ifdef VA_STAMPS
 #define VA_STAMP(p, w, kg, lane, k, value)                                                   \
     do {                                                                                 \
@@ -2348,21 +2353,32 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
             // Copies: the prologue issues K(0), V(0), K(1), V(1), K(2) (X(s) = the two
             // pages of step s; the last KiB of V(1) just before K(2)); step t then
             // refills its own slots as soon as it has read them: K(t + 3) once its K
-            // reads have returned, V(t + 2) once its V reads have.  Block-table entries at the start of step t: eK for K(t + 3)
-            // (pages 2t + 6, 2t + 7), eV for V(t + 2) (pages 2t + 4, 2t + 5), eN for
-            // the next step's K (pages 2t + 8, 2t + 9), loaded a step ahead (entry()
-            // clamps to the piece, so the loads past its end are harmless).
+            // reads have returned, V(t + 2) once its V reads have.  Block-table
+            // entries at the start of step t: eK for K(t + 3) (pages 2t + 6, 2t + 7),
+            // eV for V(t + 2) (pages 2t + 4, 2t + 5), eN for the next step's K (pages
+            // 2t + 8, 2t + 9), loaded a step ahead (entry() clamps to the piece, so
+            // the loads past its end are harmless).
             int eK0 = ent[6], eK1 = ent[7], eV0 = ent[4], eV1 = ent[5];
             int eN0 = ent[8], eN1 = ent[9];
             int ks = 0, vs = 0;                                // K / V slots of local page 2t
+#ifdef VA_STAMPS
+            uint32_t sl[8] = {0, 0, 0, 0, 0, 0, 0, 0};       // the loop's stamps (low 32 bits), held
+#endif
             for (int t = 0; t < nst; ++t) {
+#ifdef VA_STAMPS
+                const bool mid = first_piece && pass == 0 && t == (nst >> 1);
+#endif
                 // K(t) must have landed.  Issued after it so far (in issue order, each
                 // 8 copies): V(t), K(t+1) and V(t+1) if t+1 < nst, K(t+2) if t+2 < nst;
                 // from t = 3 on also V(t-1) (V(1) precedes K(2))
                 wait_vmcnt_x8(8 * ((t >= 3 ? 2 : 1) + 2 * (t + 1 < nst) + (t + 2 < nst)));
 #ifdef VA_STAMPS
                 if (first_piece && pass == 0 && t <= 1)
-                    VA_STAMP(p, w, kg, lane, 4 + t, VA_NOW());
+                    sl[t] = (uint32_t)VA_NOW();
+                if (mid) {
+                    sl[2] = (uint32_t)VA_NOW();
+                    sl[6] = (uint32_t)__builtin_amdgcn_s_memtime();
+                }
 #endif
                 const int kslot = ks, vslot = vs;
                 const unsigned char *ka = ring + ks * kW4PageBytes;
@@ -2408,12 +2424,26 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
                     w4_qk_softmax<RT>(st, retry, pop, S, ka, ka + kW4PageBytes, qop, ctx, lk, p.log2g, wlim, key0,
                                       crow, ln, after_k);
                 }
+#ifdef VA_STAMPS
+                if (mid)
+                    sl[3] = (uint32_t)VA_NOW();
+#endif
                 // V(t) must have landed.  Issued after it so far: V(t+1), K(t+2) and
                 // K(t+3) where those steps exist, and at t = 0, 1 also K(t+1)
                 wait_vmcnt_x8(8 * ((t + 1 < nst) * (t <= 1 ? 2 : 1) + (t + 2 < nst) + (t + 3 < nst)));
+#ifdef VA_STAMPS
+                if (mid)
+                    sl[4] = (uint32_t)VA_NOW();
+#endif
                 __builtin_amdgcn_sched_barrier(0);
                 w4_pv<RT>(st, va, va + kW4PageBytes, pop, masked, masked ? v_zero_mask(key0, hb, lk, ln) : 0u, ln,
                           after_v);
+#ifdef VA_STAMPS
+                if (mid) {
+                    sl[5] = (uint32_t)VA_NOW();
+                    sl[7] = (uint32_t)__builtin_amdgcn_s_memtime();
+                }
+#endif
                 eV0 = eK0;
                 eV1 = eK1;
                 eK0 = eN0;
@@ -2428,6 +2458,13 @@ void va_split_kv_fp8_w4_kernel(SplitParams p)
                     VA_STAMP(p, w, kg, lane, 6, VA_NOW());
                     VA_STAMP(p, w, kg, lane, 9, (unsigned long long)nst);
                     VA_STAMP(p, w, kg, lane, 12, (unsigned long long)(pass + 1));
+                    VA_STAMP(p, w, kg, lane, 4, (unsigned long long)sl[0]);
+                    VA_STAMP(p, w, kg, lane, 5, (unsigned long long)sl[1]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        VA_STAMP(p, w, kg, lane, 16 + i, (unsigned long long)sl[2 + i]);
+                    VA_STAMP(p, w, kg, lane, 20, (unsigned long long)sl[6]);
+                    VA_STAMP(p, w, kg, lane, 21, (unsigned long long)sl[7]);
                 }
 #endif
                 break;

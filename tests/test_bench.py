@@ -96,3 +96,31 @@ def test_bench_prints_one_json_line():
     rf = d["roofline"]
     assert rf["bound"] == "hbm" and rf["peak"] == 8000.0 and 0 < rf["frac"] == pytest.approx(rf["achieved"] / 8000.0,
                                                                                              abs=1e-3)
+
+
+def test_stamp_report_phases_and_low_32_bit_slots():
+    # Two workgroups x four waves of a VA_STAMPS run: clock ticks of 10 ns.
+    # Slots 4, 5 and 16..21 hold only the low 32 bits; the report rebuilds them
+    # from the page-loop end (slot 6) and returns phase medians in us.
+    grid, base = 2, (7 << 32) - 500                  # the low 32 bits wrap inside the call
+    w = np.zeros((grid, 4, 32), dtype=np.int64)
+    full = {0: 0, 1: 150, 2: 560, 3: 760, 4: 940, 5: 1250, 6: 4700, 7: 5200, 8: 5210}
+    for k, v in full.items():
+        w[:, :, k] = base + v
+    w[:, :, 9] = 16                                  # steps of the first piece
+    w[:, :, 10] = 1
+    w[:, :, 12] = 1
+    for k, v in ((16, 2000), (17, 2128), (18, 2136), (19, 2220)):
+        w[:, :, k] = (base + v) & 0xFFFFFFFF
+    w[:, :, 4] = (base + full[4]) & 0xFFFFFFFF
+    w[:, :, 5] = (base + full[5]) & 0xFFFFFFFF
+    w[:, :, 20] = 0xFFFFFF00                         # shader clock: 3960 cycles over 2.2 us
+    w[:, :, 21] = (0xFFFFFF00 + 3960) & 0xFFFFFFFF
+    rep = bench.stamp_report(w.reshape(-1), grid)
+    assert rep["workgroups"] == grid
+    assert rep["step0_landed"] == 9.4 and rep["step1_landed"] == 12.5
+    assert rep["page_loop_done"] == 47.0 and rep["exit_last"] == 52.1
+    assert rep["us_per_step_median"] == round((4700 - 940) / 15 / 100, 2)
+    assert rep["mid_step_qk_softmax_us"] == 1.28 and rep["mid_step_v_wait_us"] == 0.08
+    assert rep["mid_step_pv_us"] == 0.84 and rep["mid_step_us"] == 2.2
+    assert rep["shader_clock_mhz"] == 1800.0
