@@ -2,16 +2,24 @@
 //
 // The kernels and the host side of the C ABI declared in include/va.h.
 //
-//  va_split_kv_fp8_w8_kernel   Split-KV main kernel for an FP8 e4m3 cache.
+//  va_split_kv_fp8_w4_kernel   Split-KV main kernel for an FP8 e4m3 cache,
+//      paged layout, when a workgroup streams enough pages: one wave per SIMD,
+//      each wave a key group holding every packed row (Q operands in registers,
+//      O^T in accumulation registers), its own LDS ring and no barrier inside
+//      the page loop; the four key groups are combined in the epilogue.
+//  va_split_kv_fp8_w8_kernel   The FP8 main kernel with two waves per SIMD (4
+//      key groups x 2 row groups, a shared ring stage per key group): shorter
+//      prologue and epilogue, for workgroups with few pages, and the prefix +
+//      extend layout.
 //  va_split_kv_bf16_w8_kernel  The same for a bf16 cache.
-//      Each workgroup (8 waves) takes a contiguous share of the flattened page
-//      space of all (sequence, kv head) pairs.  For each piece it copies every
-//      K/V page once, straight from HBM into an LDS ring, and reuses it for all
-//      G*q_len packed query rows (GQA packing); MFMA QK^T and PV with an online
+//      Each workgroup takes a contiguous share of the flattened page space of
+//      all (sequence, kv head) pairs.  For each piece it copies every K/V page
+//      once, straight from HBM into an LDS ring, and reuses it for all G*q_len
+//      packed query rows (GQA packing); MFMA QK^T and PV with an online
 //      softmax; then either the final rows or a partial (o, lse) per piece.
-//      A template flag selects the paged layout (block table) or the prefix +
-//      extend layout (keys gathered row by row through kv_indices, draft keys
-//      from separate buffers).
+//      A template flag of the w8 kernels selects the paged layout (block table)
+//      or the prefix + extend layout (keys gathered row by row through
+//      kv_indices, draft keys from separate buffers).
 //  va_mla_split_kernel  The same split for absorbed MLA: 576-wide cache rows
 //                       (latent + RoPE part), values = the 512-wide latent.
 //  va_merge_kernel      Segment reduce: log-sum-exp merge of the partials of
@@ -19,6 +27,8 @@
 //                       workgroups (256- or 512-wide rows).
 //  va_spec_block_table_kernel, va_validate_kernel, va_fp8_to_bf16_kernel
 //                       draft-extend metadata, validate mode, test helper.
+//  va_stream_pages_kernel  Diagnostic: the FP8 kernels' copy path alone (the
+//                       streaming ceiling).
 //
 // The method comes from the sglang PR #36330 summary page ("Implementation
 // breakdown", item 1: pack the G query heads and speculative tokens of a group
@@ -34,11 +44,13 @@
 //   - the S^T accumulator already is the P^T B-operand, so no shuffle is needed;
 //   - row statistics (max, sum) stay inside one lane column.
 //
-// Stream-K partition: WG w of N handles flat pages [floor(w*P/N),
-// floor((w+1)*P/N)) where P is the total page count, computed on the device from
-// seqused_k / cu_seqlens_q.  Any length mix therefore balances over the CUs
-// with no host-side lengths (graph-safe).  Only a WG's first and last piece can
-// be split: they write their partials to workspace slots 2w and 2w + 1.
+// Stream-K partition: WG w of N handles the pages between cost positions
+// floor(w*T/N) and floor((w+1)*T/N), where T is the pages of all pairs plus a
+// fixed cost for each pair that starts inside a share (see locate), computed on
+// the device from seqused_k / cu_seqlens_q.  Any length mix therefore balances
+// over the CUs with no host-side lengths (graph-safe).  Only a WG's first and
+// last piece can be split: they write their partials to workspace slots 2w and
+// 2w + 1.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
